@@ -1,0 +1,293 @@
+// CPU oracle for the fused gated (SwiGLU) MLP with an RMSNorm prologue.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the product path may include, link,
+// load or call this file; only the test suite, the smoke check and the
+// benchmark's CPU-baseline leg use it. It shares no code, header, table or
+// helper with the HIP library: every conversion below is written out here.
+//
+// What it computes (all arithmetic in IEEE double unless stated):
+//   FastTPS review (xllm-io paper-review blog), section 3 "technical
+//   architecture", Eq(1): O = W_down( SiLU(W_gate h) * (W_up h) ), where '*'
+//   is the element-wise product ("elewMul"), and the MLP-block flow on the
+//   same page: RMSNorm -> interleaved gate-up matmul -> SiLU*mul -> down
+//   projection (Figure 4: part1 RMSNorm, part2 interleaved gate/up fusion,
+//   part3 down projection). So h = RMSNorm(x).
+//   Readings where the pages are silent (all listed in the design doc):
+//     RMSNorm(x)_k = gamma_k * x_k / sqrt(mean_k(x^2) + eps)   (no mean
+//       subtraction, no bias, gamma is a plain multiplier);
+//     SiLU(t) = t / (1 + exp(-t))  (Swish with beta = 1; SwiGLU);
+//     interleave: packed row 2i is gate row i, packed row 2i+1 is up row i
+//       (llama.cpp PR digest, blog.cecily.jp: gate/up rows alternate);
+//     weights are nn.Linear-shaped [out, in], row-major;
+//     int4: symmetric, groups of 32 consecutive elements along K, one fp16
+//       scale per group, s = fp16_rne(fp32(max|w| / 7)),
+//       q = clamp(round_half_even(fp32(w / s)), -8, 7), q = 0 when s == 0,
+//       two's-complement nibbles, even k in the low nibble.
+//
+// Summation order is fixed (k ascending), and OpenMP only splits independent
+// outputs, so results do not depend on the thread count.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <cfenv>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+extern "C" {
+
+// ---------------------------------------------------------------- scalars
+
+// bf16 -> double: a bf16 is the top 16 bits of an IEEE binary32.
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+// IEEE binary16 -> double, decoded field by field (exact).
+static double f16_value(uint16_t h) {
+  const int sign = h >> 15;
+  const int e = (h >> 10) & 0x1f;
+  const int m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = std::ldexp((double)m, -24);              // zero / subnormal
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = std::ldexp((double)(m | 0x400), e - 25);  // 1.m * 2^(e-15)
+  return sign ? -v : v;
+}
+
+// binary32 -> binary16 with round-to-nearest-even, written from the format
+// definition: scale the magnitude so the kept bits are the integer part,
+// round that integer half-to-even, rebuild the fields.
+static uint16_t f16_bits_rne(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (std::isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  const double a = std::fabs((double)f);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);  // rounds past 65504
+  const int old_mode = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  uint16_t bits;
+  if (a < std::ldexp(1.0, -14)) {
+    // subnormal range: unit is 2^-24; rounding up may reach 0x400 (min normal)
+    bits = (uint16_t)std::nearbyint(std::ldexp(a, 24));
+  } else {
+    int e2;
+    std::frexp(a, &e2);            // a = f * 2^e2, f in [0.5, 1)
+    const int e = e2 - 1;          // a in [2^e, 2^(e+1))
+    double mant = std::nearbyint(std::ldexp(a, 10 - e));  // in [1024, 2048]
+    int ee = e;
+    if (mant >= 2048.0) { mant = 1024.0; ee += 1; }
+    bits = (uint16_t)(((ee + 15) << 10) | ((int)mant - 1024));
+  }
+  std::fesetround(old_mode);
+  return (uint16_t)(sign | bits);
+}
+
+double oracle_bf16_to_double(uint16_t b) { return bf16_value(b); }
+double oracle_f16_to_double(uint16_t h) { return f16_value(h); }
+uint16_t oracle_f32_to_f16_rne(float f) { return f16_bits_rne(f); }
+
+// SiLU(t) = t * sigmoid(t) = t / (1 + e^-t). For t -> -inf, e^-t overflows to
+// +inf and the quotient is -0, the correct limit.
+double oracle_silu(double t) { return t / (1.0 + std::exp(-t)); }
+
+// ---------------------------------------------------------------- RMSNorm
+
+// r[m] = 1 / sqrt(mean_k x[m,k]^2 + eps)
+void oracle_rms_scale(const uint16_t* x, int64_t M, int64_t d, double eps,
+                      double* r) {
+  for (int64_t m = 0; m < M; ++m) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < d; ++k) {
+      const double v = bf16_value(x[m * d + k]);
+      ss += v * v;
+    }
+    r[m] = 1.0 / std::sqrt(ss / (double)d + eps);
+  }
+}
+
+// n[m,k] = x[m,k] * r[m] * gamma[k]
+void oracle_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps,
+                    int64_t M, int64_t d, double* n) {
+  for (int64_t m = 0; m < M; ++m) {
+    double r;
+    oracle_rms_scale(x + m * d, 1, d, eps, &r);
+    for (int64_t k = 0; k < d; ++k)
+      n[m * d + k] = bf16_value(x[m * d + k]) * r * bf16_value(gamma[k]);
+  }
+}
+
+// ---------------------------------------------------------------- packing
+
+// w_gu[2i, :] = w_gate[i, :], w_gu[2i+1, :] = w_up[i, :]   (bf16 bit copies)
+void oracle_pack_interleaved(const uint16_t* w_gate, const uint16_t* w_up,
+                             uint16_t* w_gu, int64_t ff, int64_t d) {
+  for (int64_t i = 0; i < ff; ++i) {
+    for (int64_t k = 0; k < d; ++k) {
+      w_gu[(2 * i) * d + k] = w_gate[i * d + k];
+      w_gu[(2 * i + 1) * d + k] = w_up[i * d + k];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- int4
+
+// Returns 0, or -5 when a group's scale is not a finite fp16 (a non-finite
+// weight, or max|w|/7 rounding past 65504).
+int oracle_quantize_int4(const uint16_t* w, int64_t rows, int64_t K,
+                         uint8_t* q, uint16_t* scales) {
+  const int old_mode = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  int status = 0;
+  const int64_t groups = K / 32;
+  for (int64_t r = 0; r < rows && status == 0; ++r) {
+    for (int64_t g = 0; g < groups; ++g) {
+      const uint16_t* src = w + r * K + g * 32;
+      float mx = 0.0f;
+      bool finite = true;
+      for (int j = 0; j < 32; ++j) {
+        const float v = (float)bf16_value(src[j]);
+        if (!std::isfinite(v)) finite = false;
+        const float a = std::fabs(v);
+        if (a > mx) mx = a;
+      }
+      const float ratio = mx / 7.0f;          // IEEE binary32 division
+      const uint16_t sh = f16_bits_rne(ratio);
+      if (!finite || (sh & 0x7c00u) == 0x7c00u) { status = -5; break; }
+      scales[r * groups + g] = sh;
+      const float s = (float)f16_value(sh);
+      for (int j = 0; j < 32; j += 2) {
+        int qq[2];
+        for (int t = 0; t < 2; ++t) {
+          int v = 0;
+          if (s != 0.0f) {
+            const float ratio_k = (float)bf16_value(src[j + t]) / s;
+            float rq = std::nearbyint(ratio_k);  // ties to even
+            if (rq > 7.0f) rq = 7.0f;
+            if (rq < -8.0f) rq = -8.0f;
+            v = (int)rq;
+          }
+          qq[t] = v;
+        }
+        q[r * (K / 2) + (g * 32 + j) / 2] =
+            (uint8_t)((qq[0] & 0xF) | ((qq[1] & 0xF) << 4));
+      }
+    }
+  }
+  std::fesetround(old_mode);
+  return status;
+}
+
+// Signed value of nibble k of a packed int4 row.
+static int int4_at(const uint8_t* qrow, int64_t k) {
+  const uint8_t byte = qrow[k / 2];
+  const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+  return nib >= 8 ? nib - 16 : nib;
+}
+
+// out[r,k] = float(s[r, k/32]) * float(q[r,k]); exact in binary32
+// (an 11-bit significand times a 4-bit integer).
+void oracle_dequant_int4(const uint8_t* q, const uint16_t* scales,
+                         int64_t rows, int64_t K, float* out) {
+  const int64_t groups = K / 32;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k)
+      out[r * K + k] = (float)f16_value(scales[r * groups + k / 32]) *
+                       (float)int4_at(q + r * (K / 2), k);
+}
+
+// ---------------------------------------------------------------- forward
+
+// Weight access: one callback-free struct per storage kind keeps the three
+// forward variants on the same arithmetic.
+struct WeightView {
+  int kind;                 // 0 bf16, 1 int4 group-32
+  const uint16_t* bf;       // bf16 [rows, K]
+  const uint8_t* q;         // int4 [rows, K/2]
+  const uint16_t* s;        // fp16 [rows, K/32]
+  int64_t K;
+  double at(int64_t row, int64_t k) const {
+    if (kind == 0) return bf16_value(bf[row * K + k]);
+    return f16_value(s[row * (K / 32) + k / 32]) *
+           (double)int4_at(q + row * (K / 2), k);
+  }
+};
+
+// y[m, :] = Wd (SiLU(Wg n_m) * (Wu n_m)), n_m = RMSNorm(x_m).
+// gate row i is (g_view, g_row0 + g_stride*i), up row i likewise.
+static void forward_core(const uint16_t* x, const uint16_t* gamma, double eps,
+                         const WeightView& gv, int64_t g_row0, int64_t g_stride,
+                         const WeightView& uv, int64_t u_row0, int64_t u_stride,
+                         const WeightView& dv, int64_t M, int64_t d, int64_t ff,
+                         double* y) {
+  double* n = new double[d];
+  double* a = new double[ff];
+  for (int64_t m = 0; m < M; ++m) {
+    oracle_rmsnorm(x + m * d, gamma, eps, 1, d, n);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < ff; ++i) {
+      double g = 0.0, u = 0.0;
+      const int64_t gr = g_row0 + g_stride * i, ur = u_row0 + u_stride * i;
+      for (int64_t k = 0; k < d; ++k) g += gv.at(gr, k) * n[k];
+      for (int64_t k = 0; k < d; ++k) u += uv.at(ur, k) * n[k];
+      a[i] = oracle_silu(g) * u;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < d; ++j) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < ff; ++i) acc += dv.at(j, i) * a[i];
+      y[m * d + j] = acc;
+    }
+  }
+  delete[] n;
+  delete[] a;
+}
+
+// Eq(1) from separate gate and up matrices (the unfused ordering).
+void oracle_forward_unfused(const uint16_t* x, const uint16_t* gamma,
+                            double eps, const uint16_t* w_gate,
+                            const uint16_t* w_up, const uint16_t* w_down,
+                            int64_t M, int64_t d, int64_t ff, double* y) {
+  WeightView g{0, w_gate, nullptr, nullptr, d};
+  WeightView u{0, w_up, nullptr, nullptr, d};
+  WeightView dn{0, w_down, nullptr, nullptr, ff};
+  forward_core(x, gamma, eps, g, 0, 1, u, 0, 1, dn, M, d, ff, y);
+}
+
+// Eq(1) from the interleaved matrix w_gu [2ff, d] (gate at even rows).
+void oracle_forward_bf16(const uint16_t* x, const uint16_t* gamma, double eps,
+                         const uint16_t* w_gu, const uint16_t* w_down,
+                         int64_t M, int64_t d, int64_t ff, double* y) {
+  WeightView gu{0, w_gu, nullptr, nullptr, d};
+  WeightView dn{0, w_down, nullptr, nullptr, ff};
+  forward_core(x, gamma, eps, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
+}
+
+// Eq(1) with int4 weights: w = s * q, widened exactly to double.
+void oracle_forward_int4(const uint16_t* x, const uint16_t* gamma, double eps,
+                         const uint8_t* q_gu, const uint16_t* s_gu,
+                         const uint8_t* q_down, const uint16_t* s_down,
+                         int64_t M, int64_t d, int64_t ff, double* y) {
+  WeightView gu{1, nullptr, q_gu, s_gu, d};
+  WeightView dn{1, nullptr, q_down, s_down, ff};
+  forward_core(x, gamma, eps, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
+}
+
+// Threads the parallel loops above will use.
+int oracle_omp_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+"""Plant plausible mistakes in a scratch copy of the oracle (CPU only) and check
+that the pins in test_oracle_pins.py reject every one of them."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "fmlp_oracle.cpp")
+
+MUTATIONS = {
+    "eps_outside_sqrt": ("std::sqrt(ss / (double)d + eps)", "(std::sqrt(ss / (double)d) + eps)"),
+    "sum_not_mean": ("std::sqrt(ss / (double)d + eps)", "std::sqrt(ss + eps)"),
+    "gamma_dropped": ("* r * bf16_value(gamma[k])", "* r"),
+    "gate_up_rows_swapped": ("gu, 0, 2, gu, 1, 2", "gu, 1, 2, gu, 0, 2"),
+    "silu_on_up_branch": ("oracle_silu(g) * u", "oracle_silu(u) * g"),
+    "w_down_transposed": ("acc += dv.at(j, i) * a[i]", "acc += dv.at(i % dv.K, j % ff) * a[i]"),
+    "round_half_away": ("float rq = std::nearbyint(ratio_k);", "float rq = std::round(ratio_k);"),
+    "nibble_order_swapped": ("(k & 1) ? (byte >> 4) : (byte & 0xF)",
+                             "(k & 1) ? (byte & 0xF) : (byte >> 4)"),
+    "sigmoid_not_silu": ("return t / (1.0 + std::exp(-t));", "return 1.0 / (1.0 + std::exp(-t));"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_reject_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    text = open(SRC).read()
+    assert old in text, f"mutation anchor for {name} no longer in the oracle"
+    src = tmp_path / "mutant.cpp"
+    src.write_text(text.replace(old, new, 1))
+    env = dict(os.environ, FMLP_ORACLE_SRC=str(src), FMLP_ORACLE_LIB=str(tmp_path / "libmutant.so"),
+               OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins accepted mutant {name}:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout

@@ -1,0 +1,342 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties the oracle to a closed form derived by hand, an invariant of
+Eq(1), a library routine that computes a special case, or the definition of a
+storage format (IEEE binary16 via numpy). The operation is Eq(1) of the
+FastTPS review (xllm-io paper-review blog, section 3) with the RMSNorm
+prologue of the MLP-block flow / Figure 4 on the same page; the gate/up row
+interleave follows the llama.cpp PR digest (blog.cecily.jp).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")))
+
+
+def bf16_bits(a) -> np.ndarray:
+    t = torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def rand_bf16(shape, std, seed, mean=0.0):
+    g = torch.Generator().manual_seed(seed)
+    t = (torch.randn(shape, generator=g) * std + mean).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def sigmoid_closed(t):
+    return 1.0 / (1.0 + math.exp(-t))
+
+
+# ------------------------------------------------------------ scalar formats
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 65536, 7, dtype=np.uint16)
+    ref = bf16_values(bits)
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    finite = np.isfinite(ref)
+    assert np.array_equal(got[finite], ref[finite])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_f16_decode_matches_numpy_every_pattern():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.f16_to_double(int(b)) for b in bits])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_f32_to_f16_rne_matches_numpy():
+    # numpy's float32 -> float16 cast rounds to nearest even (IEEE default).
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([
+        rng.standard_normal(4000).astype(np.float32) * np.float32(3.0),
+        (rng.random(2000).astype(np.float32) * np.float32(1e-4)),   # subnormal range
+        np.float32(2.0) ** rng.integers(-30, 17, 500).astype(np.float32),
+        np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24,
+                  2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 1.0 + 2.0 ** -11,
+                  1.0 + 3 * 2.0 ** -11, 2049.0, 2051.0, np.inf, -np.inf],
+                 dtype=np.float32),
+    ])
+    # exact ties between two fp16 neighbours: midpoints m + 0.5 ulp
+    mids = (np.arange(1024, 2048, dtype=np.float32) + np.float32(0.5)) * np.float32(2.0 ** -10)
+    vals = np.concatenate([vals, mids, -mids]).astype(np.float32)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16_rne(float(v)) for v in vals], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------ SiLU
+
+def test_silu_closed_form_values():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(1.0) == pytest.approx(0.7310585786300049, abs=1e-15)
+    assert oracle.silu(-1.0) == pytest.approx(-0.2689414213699951, abs=1e-15)
+    for t in (-7.5, -0.3, 0.25, 2.0, 9.0):
+        assert oracle.silu(t) == pytest.approx(t * sigmoid_closed(t), rel=1e-15)
+    # limits: SiLU(t) -> t for large t, -> 0 (no NaN) for very negative t
+    assert oracle.silu(60.0) == pytest.approx(60.0, rel=1e-15)
+    v = oracle.silu(-800.0)
+    assert v == 0.0 and not math.isnan(v)
+
+
+def test_silu_matches_torch():
+    t = torch.linspace(-30, 30, 1001, dtype=torch.float64)
+    ref = F.silu(t).numpy()
+    got = np.array([oracle.silu(float(v)) for v in t])
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-300)
+
+
+# ------------------------------------------------------------ RMSNorm
+
+def test_rmsnorm_unit_rms_before_gamma():
+    # mean(n^2) with gamma = 1 equals ms/(ms+eps) exactly (closed form)
+    x = bf16_bits([[3.0, 4.0]])
+    g = bf16_bits([1.0, 1.0])
+    n = oracle.rmsnorm(x, g, 1e-5)
+    assert np.mean(n ** 2) == pytest.approx(12.5 / (12.5 + 1e-5), rel=1e-14)
+    assert np.mean(n ** 2) == pytest.approx(0.999999200000640, abs=1e-14)
+    xr = rand_bf16((5, 96), 1.7, 11)
+    n0 = oracle.rmsnorm(xr, bf16_bits(np.ones(96)), 0.0)
+    np.testing.assert_allclose(np.mean(n0 ** 2, axis=1), 1.0, rtol=1e-13)
+
+
+def test_rmsnorm_matches_torch_library():
+    x = rand_bf16((4, 64), 2.0, 3)
+    g = rand_bf16((64,), 0.1, 4, mean=1.0)
+    for eps in (0.0, 1e-5, 0.3):
+        ref = F.rms_norm(torch.from_numpy(bf16_values(x)), (64,),
+                         torch.from_numpy(bf16_values(g)), eps).numpy()
+        np.testing.assert_allclose(oracle.rmsnorm(x, g, eps), ref, rtol=1e-13)
+
+
+# ------------------------------------------------------------ hand cases
+
+def _hand(name):
+    c = GOLDEN[name]
+    return (bf16_bits(c["x"]), bf16_bits(c["gamma"]), bf16_bits(c["w_gate"]),
+            bf16_bits(c["w_up"]), bf16_bits(c["w_down"]))
+
+
+def silu(t):
+    return t * sigmoid_closed(t)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-5])
+def test_h1_closed_form(eps):
+    x, g, wg, wu, wd = _hand("H1")
+    s = math.sqrt(12.5 + eps)
+    a = silu(3.0 / s) * (4.0 / s)
+    expect = np.array([[a, 2 * a]])
+    y = oracle.forward_unfused(x, g, eps, wg, wu, wd)
+    np.testing.assert_allclose(y, expect, rtol=1e-14)
+    wgu = oracle.pack_interleaved(wg, wu)
+    assert np.array_equal(bf16_values(wgu), [[1.0, 0.0], [0.0, 1.0]])
+    np.testing.assert_allclose(oracle.forward_bf16(x, g, eps, wgu, wd), expect, rtol=1e-14)
+    # values quoted for this case to 12 digits
+    if eps == 0.0:
+        assert y[0, 0] == pytest.approx(0.672247962807, abs=1e-12)
+    else:
+        assert y[0, 0] == pytest.approx(0.672247356617, abs=1e-12)
+
+
+def test_h2_closed_form_and_interleave():
+    x, g, wg, wu, wd = _hand("H2")
+    s = math.sqrt(2.5)
+    n = np.array([1.0, -1.0, 4.0, -1.0]) / s
+    a0 = silu(n[0]) * n[1]
+    a1 = silu(n[2]) * (-n[3])
+    expect = np.array([[a0, a1, a0 + a1, 0.5 * a0 - 0.5 * a1]])
+    y = oracle.forward_unfused(x, g, 0.0, wg, wu, wd)
+    np.testing.assert_allclose(y, expect, rtol=1e-14, atol=1e-15)
+    wgu = oracle.pack_interleaved(wg, wu)
+    rows = bf16_values(wgu)
+    np.testing.assert_array_equal(rows[0], bf16_values(wg)[0])
+    np.testing.assert_array_equal(rows[1], bf16_values(wu)[0])
+    np.testing.assert_array_equal(rows[2], bf16_values(wg)[1])
+    np.testing.assert_array_equal(rows[3], bf16_values(wu)[1])
+    np.testing.assert_allclose(oracle.forward_bf16(x, g, 0.0, wgu, wd), expect, rtol=1e-14,
+                               atol=1e-15)
+    assert y[0, 3] == pytest.approx(-0.871574165255, abs=1e-12)
+
+
+# ------------------------------------------------------------ invariants
+
+def _rand_layer(M, d, ff, seed):
+    return (rand_bf16((M, d), 1.0, seed), rand_bf16((d,), 0.1, seed + 1, mean=1.0),
+            rand_bf16((ff, d), 0.05, seed + 2), rand_bf16((ff, d), 0.05, seed + 3),
+            rand_bf16((d, ff), 0.05, seed + 4))
+
+
+def test_zero_weights_give_zero_output():
+    x, g, wg, wu, wd = _rand_layer(3, 32, 24, 100)
+    z_ff = np.zeros_like(wg)
+    z_d = np.zeros_like(wd)
+    for args in ((z_ff, wu, wd), (wg, z_ff, wd), (wg, wu, z_d)):
+        y = oracle.forward_unfused(x, g, 1e-5, *args)
+        assert np.all(y == 0.0)
+    y = oracle.forward_unfused(np.zeros_like(x), g, 1e-5, wg, wu, wd)
+    assert np.all(y == 0.0)
+
+
+def test_interleaved_equals_unfused_bitwise():
+    x, g, wg, wu, wd = _rand_layer(4, 64, 40, 200)
+    wgu = oracle.pack_interleaved(wg, wu)
+    np.testing.assert_array_equal(oracle.forward_bf16(x, g, 1e-5, wgu, wd),
+                                  oracle.forward_unfused(x, g, 1e-5, wg, wu, wd))
+
+
+def test_ff_permutation_invariance():
+    x, g, wg, wu, wd = _rand_layer(2, 32, 48, 300)
+    perm = np.random.default_rng(1).permutation(48)
+    y = oracle.forward_unfused(x, g, 1e-5, wg, wu, wd)
+    yp = oracle.forward_unfused(x, g, 1e-5, wg[perm], wu[perm],
+                                np.ascontiguousarray(wd[:, perm]))
+    np.testing.assert_allclose(yp, y, rtol=1e-12, atol=1e-14)
+
+
+def test_rows_independent_and_linear_in_w_down():
+    x, g, wg, wu, wd = _rand_layer(5, 32, 16, 400)
+    y = oracle.forward_unfused(x, g, 1e-5, wg, wu, wd)
+    for m in range(5):
+        np.testing.assert_array_equal(oracle.forward_unfused(x[m:m + 1], g, 1e-5, wg, wu, wd),
+                                      y[m:m + 1])
+    # 2*W_down is exact in bf16, so y doubles exactly
+    wd2 = bf16_bits(2.0 * bf16_values(wd))
+    np.testing.assert_array_equal(oracle.forward_unfused(x, g, 1e-5, wg, wu, wd2), 2.0 * y)
+
+
+def test_scale_invariance_with_zero_eps():
+    x, g, wg, wu, wd = _rand_layer(3, 32, 16, 500)
+    x4 = bf16_bits(4.0 * bf16_values(x))   # exact in bf16
+    np.testing.assert_allclose(oracle.forward_unfused(x4, g, 0.0, wg, wu, wd),
+                               oracle.forward_unfused(x, g, 0.0, wg, wu, wd), rtol=1e-13,
+                               atol=1e-15)
+
+
+@pytest.mark.parametrize("M,d,ff,seed", [(1, 32, 32, 1), (3, 64, 96, 2), (2, 256, 704, 3)])
+def test_matches_torch_fp64_composition(M, d, ff, seed):
+    # An independent implementation from library routines: rms_norm, matmul, silu.
+    x, g, wg, wu, wd = _rand_layer(M, d, ff, 600 + seed)
+    X, G, WG, WU, WD = (torch.from_numpy(bf16_values(a)) for a in (x, g, wg, wu, wd))
+    n = F.rms_norm(X, (d,), G, 1e-5)
+    ref = (F.silu(n @ WG.T) * (n @ WU.T)) @ WD.T
+    y = oracle.forward_unfused(x, g, 1e-5, wg, wu, wd)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-11, atol=1e-13 * np.abs(ref.numpy()).max())
+
+
+# ------------------------------------------------------------ packing
+
+def test_pack_matches_numpy_slicing():
+    wg = rand_bf16((40, 64), 1.0, 7)
+    wu = rand_bf16((40, 64), 1.0, 8)
+    p = oracle.pack_interleaved(wg, wu)
+    assert np.array_equal(p[0::2], wg) and np.array_equal(p[1::2], wu)
+
+
+# ------------------------------------------------------------ int4
+
+def test_q1_ties_to_even():
+    c = GOLDEN["Q1"]
+    st, q, s = oracle.quantize_int4(bf16_bits([c["w"]]))
+    assert st == 0
+    assert s.view(np.float16)[0, 0] == np.float16(c["scale"])
+    deq = oracle.dequant_int4(q, s)
+    np.testing.assert_array_equal(deq[0], np.array(c["q"], np.float32) * np.float32(0.125))
+    # nibble layout: even k low nibble, two's complement
+    assert q[0, 0] == (7 | ((2 & 0xF) << 4))
+    assert q[0, 1] == ((-2 & 0xF) | (2 << 4))
+
+
+def _nibbles(q):
+    lo = (q & 0xF).astype(np.int32)
+    hi = (q >> 4).astype(np.int32)
+    v = np.empty((q.shape[0], q.shape[1] * 2), np.int32)
+    v[:, 0::2], v[:, 1::2] = lo, hi
+    return np.where(v >= 8, v - 16, v)
+
+
+def test_quantize_is_nearest_with_ties_even():
+    w = rand_bf16((16, 256), 0.02, 9)
+    st, q, s = oracle.quantize_int4(w)
+    assert st == 0
+    wv = bf16_values(w).astype(np.float32).reshape(16, 8, 32)
+    # the scale: fp16(fp32(max|w|) / fp32(7)) computed with numpy
+    mx = np.abs(wv).max(axis=2)
+    np.testing.assert_array_equal(s, (mx / np.float32(7)).astype(np.float16).view(np.uint16))
+    sv = s.view(np.float16).astype(np.float32)[:, :, None]
+    qv = _nibbles(q).reshape(16, 8, 32)
+    ratio = wv / sv                      # fp32 division, as the definition says
+    # brute force: q is the integer in [-8,7] nearest to w/s, ties to even
+    cand = np.arange(-8, 8)
+    dist = np.abs(ratio[..., None] - cand)
+    best = dist.min(axis=-1, keepdims=True)
+    ok = dist == best
+    choice = np.where(ok.sum(-1) == 1, cand[ok.argmax(-1)],
+                      np.where(ok & (cand % 2 == 0), cand, 99).min(-1))
+    np.testing.assert_array_equal(qv, choice)
+    # round-trip error at most half a step
+    assert np.all(np.abs(wv - sv * qv) <= sv / 2 + 1e-12)
+
+
+def test_quantize_zero_group_and_range_error():
+    st, q, s = oracle.quantize_int4(np.zeros((2, 64), np.uint16))
+    assert st == 0 and np.all(q == 0) and np.all(s == 0)
+    big = bf16_bits(np.full((1, 32), 1e6))
+    assert oracle.quantize_int4(big)[0] == oracle.RANGE_ERROR
+    inf = bf16_bits(np.array([[np.inf] + [0.0] * 31]))
+    assert oracle.quantize_int4(inf)[0] == oracle.RANGE_ERROR
+
+
+def test_quantize_commutes_with_interleave():
+    wg = rand_bf16((24, 128), 0.02, 12)
+    wu = rand_bf16((24, 128), 0.02, 13)
+    st1, q1, s1 = oracle.quantize_int4(oracle.pack_interleaved(wg, wu))
+    _, qg, sg = oracle.quantize_int4(wg)
+    _, qu, su = oracle.quantize_int4(wu)
+    assert st1 == 0
+    assert np.array_equal(q1[0::2], qg) and np.array_equal(q1[1::2], qu)
+    assert np.array_equal(s1[0::2], sg) and np.array_equal(s1[1::2], su)
+
+
+def test_dequant_is_exact_product():
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 256, (8, 64), dtype=np.uint8)
+    s = (rng.random((8, 4)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    deq = oracle.dequant_int4(q, s)
+    ref = (np.repeat(s.view(np.float16).astype(np.float64), 32, axis=1)
+           * _nibbles(q).astype(np.float64))
+    np.testing.assert_array_equal(deq.astype(np.float64), ref)
+
+
+def test_int4_forward_matches_torch_composition():
+    rng = np.random.default_rng(6)
+    M, d, ff = 2, 64, 96
+    x = rand_bf16((M, d), 1.0, 20)
+    g = rand_bf16((d,), 0.1, 21, mean=1.0)
+    q_gu = rng.integers(0, 256, (2 * ff, d // 2), dtype=np.uint8)
+    s_gu = (rng.random((2 * ff, d // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    q_d = rng.integers(0, 256, (d, ff // 2), dtype=np.uint8)
+    s_d = (rng.random((d, ff // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    wgu = np.repeat(s_gu.view(np.float16).astype(np.float64), 32, 1) * _nibbles(q_gu)
+    wdn = np.repeat(s_d.view(np.float16).astype(np.float64), 32, 1) * _nibbles(q_d)
+    n = F.rms_norm(torch.from_numpy(bf16_values(x)), (d,), torch.from_numpy(bf16_values(g)), 1e-5)
+    WGU = torch.from_numpy(wgu)
+    ref = (F.silu(n @ WGU[0::2].T) * (n @ WGU[1::2].T)) @ torch.from_numpy(wdn).T
+    y = oracle.forward_int4(x, g, 1e-5, q_gu, s_gu, q_d, s_d)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-11, atol=1e-13 * np.abs(ref.numpy()).max())
