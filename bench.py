@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused gated-MLP forward on one MI355X.
+
+One step = one fmlp_forward call (RMSNorm -> interleaved gate/up matmul ->
+SiLU*mul -> down projection) on one layer, the weight set rotating every
+step through `sets` distinct layers so the 256 MB Infinity Cache cannot serve
+repeats. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line (stdout). Default workload: Phi-3-mini-shaped decode,
+d=3072, ff=8192, M=1, 32 weight sets. `--workload`/`--M` select another
+configuration; `--all` prints one line per (workload, M).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MLP tokens/s + % HBM roofline (decode M=1) / % MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+DEFAULT_WORKLOAD = "phi3mini_decode_d3072_ff8192"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--M", type=int, default=None)
+    ap.add_argument("--all", action="store_true", help="every (workload, M); one line each")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall-clock budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- bytes / flops
+
+def weight_bytes(d, ff, wtype):
+    """(W_gu bytes, W_down bytes), scales included for int4."""
+    if wtype == "int4":
+        return 2 * ff * d // 2 + 2 * ff * (d // 32) * 2, d * ff // 2 + d * (ff // 32) * 2
+    return 2 * ff * d * 2, d * ff * 2
+
+
+def step_bytes(M, d, ff, wtype):
+    """Algorithmic bytes of one step: weights (+ scales) + x + gamma + y."""
+    gu, dn = weight_bytes(d, ff, wtype)
+    return gu + dn + M * d * 2 + d * 2 + M * d * 2
+
+
+def kernel_bytes(kernel, M, d, ff, wtype):
+    """Algorithmic bytes of one launch of a decode kernel: its weights
+    (+ scales), its activation inputs and its outputs; the SiLU*mul
+    intermediate counts as fp32 (4 bytes per element)."""
+    gu, dn = weight_bytes(d, ff, wtype)
+    if "gateup" in kernel:
+        return gu + M * d * 2 + d * 2 + M * ff * 4
+    return dn + M * ff * 4 + M * d * 2
+
+
+def step_flops(M, d, ff):
+    return 6.0 * M * ff * d
+
+
+# ----------------------------------------------------------------------------- traffic
+
+def kernel_source_sha(kernel):
+    """Hash of the HIP source that defines a kernel kind (to expire counter data)."""
+    src = {
+        "decode_gateup_bf16": "decode.hip", "decode_down_bf16": "decode.hip",
+        "decode_gateup_int4": "decode_int4.hip", "decode_down_int4": "decode_int4.hip",
+        "gemm_gateup_silu_f16": "prefill.hip", "gemm_down_f16": "prefill.hip",
+    }.get(kernel)
+    if src is None:
+        return None
+    h = hashlib.sha256()
+    for f in (src, "device_common.hpp"):
+        h.update(open(os.path.join(ROOT, "swiglu_mlp_rmsnorm_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, M):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}_M{M}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        m = re.match(r"^(\w+):\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("source_sha") != kernel_source_sha(kernel):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
+    """Time the fp64 CPU oracle on a bounded sample of the same workload."""
+    from oracle import oracle
+    x, g = host_inputs
+    # rows are independent: for large M, run row subsets until the budget is spent
+    rows_per_call = M if M <= 32 else 1
+    done_rows, calls = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        r0 = (calls * rows_per_call) % M
+        xs = x[r0:r0 + rows_per_call]
+        if w.wtype == "int4":
+            q_gu, s_gu, q_d, s_d = host_layer
+            oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, q_d, s_d)
+        else:
+            wgu, wd = host_layer
+            oracle.forward_bf16(xs, g, w_eps(), wgu, wd)
+        done_rows += xs.shape[0]
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (rows_per_call == M and calls >= 200):
+            break
+    return {
+        "value": done_rows / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+        "sample": (f"{calls} oracle forward call(s) of {rows_per_call} row(s) on weight set 0 of "
+                   f"{w.name} (fp64, {el:.1f} s)"),
+    }
+
+
+def w_eps():
+    from swiglu_mlp_rmsnorm_amd import synth
+    return synth.EPS
+
+
+# ----------------------------------------------------------------------------- run
+
+def run_one(wname, M, steps, warmup, args):
+    import torch
+    from swiglu_mlp_rmsnorm_amd import fmlp as F
+    from swiglu_mlp_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS[wname]
+    dev = torch.device("cuda:0")
+    d, ff = w.d, w.ff
+    path = "decode" if M <= 32 else "prefill"
+    log(f"[bench] {wname} M={M}: building {w.sets} weight set(s)")
+    layers, xs = [], []
+    for l in range(w.sets):
+        if w.wtype == "int4":
+            layers.append(synth.layer_int4(w, l, dev))
+        else:
+            wg, wu, wd = synth.layer_bf16(w, l, dev)
+            layers.append((F.fmlp_pack_interleaved(wg, wu), wd))
+            del wg, wu
+        xs.append(synth.inputs(w, M, dev, layer=l))
+    torch.cuda.synchronize()
+    y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, 1 if w.wtype == "int4" else 0),
+                     dtype=torch.uint8, device=dev)
+
+    def step(i):
+        L = layers[i % w.sets]
+        x, g = xs[i % w.sets]
+        if w.wtype == "int4":
+            F.fmlp_forward(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws)
+        else:
+            F.fmlp_forward(x, g, synth.EPS, L[0], L[1], y=y, workspace=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} done; timing {steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    wall_ms_per_step = (t1 - t0) * 1e3 / steps
+    tokens_per_s = M / (ms_per_step * 1e-3)
+    sb = step_bytes(M, d, ff, w.wtype)
+    log(f"[bench] {ms_per_step*1e3:.2f} us/step (host wall {wall_ms_per_step*1e3:.2f}), "
+        f"{sb / ms_per_step / 1e6:.1f} GB/s step")
+
+    # per-kernel durations from HIP events recorded by the library on its launch stream
+    kernels = {}
+    if not args.no_profile:
+        F.fmlp_profile_enable(True)
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        for name, (n, ms) in F.fmlp_profile_read().items():
+            kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+        F.fmlp_profile_enable(False)
+        log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    if path == "decode":
+        dom = "decode_gateup_int4" if w.wtype == "int4" else "decode_gateup_bf16"
+        dom_units = kernel_bytes(dom, M, d, ff, w.wtype)
+        unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
+    else:
+        dom = "gemm_gateup_silu_f16"
+        dom_units = 2.0 * M * (2 * ff) * d
+        unit, peak, bound = "TFLOP/s", MFMA_PEAK_TFLOPS, "mfma"
+    roofline = None
+    if dom in kernels:
+        avg_s = kernels[dom]["avg_us"] * 1e-6
+        achieved = dom_units / avg_s / (1e9 if unit == "GB/s" else 1e12)
+        roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": unit, "frac": round(achieved / peak, 4),
+                    "units_per_launch": dom_units,
+                    "traffic": measured_traffic(dom, wname, M)}
+    for name, k in kernels.items():
+        if name.startswith("decode"):
+            k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (k["avg_us"] * 1e3), 1)
+        elif name == "gemm_gateup_silu_f16":
+            k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (k["avg_us"] * 1e6), 1)
+        elif name == "gemm_down_f16":
+            k["tflop_per_s"] = round(2.0 * M * ff * d / (k["avg_us"] * 1e6), 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        if w.wtype == "int4":
+            host_layer = tuple(synth.bits(t) for t in layers[0])
+        else:
+            host_layer = (synth.bits(layers[0][0]), synth.bits(layers[0][1]))
+        host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
+        log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
+        cpu = cpu_baseline(w, M, host_layer, host_inputs, args.cpu_seconds)
+
+    step_gbs = sb / (ms_per_step * 1e-3) / 1e9
+    step_tflops = step_flops(M, d, ff) / (ms_per_step * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4-bf16" if w.wtype == "int4" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wname, "M": M, "d": d, "ff": ff, "weight_sets": w.sets,
+                   "wtype": w.wtype, "path": path, "parallelism": "none (1 GPU)"},
+        "step_gb_per_s": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_tflop_per_s": round(step_tflops, 2),
+        "step_mfma_frac": round(step_tflops / MFMA_PEAK_TFLOPS, 4),
+        "host_wall_ms_per_step": round(wall_ms_per_step, 6),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    del layers, xs
+    torch.cuda.empty_cache()
+    return rec
+
+
+def default_steps(w, M):
+    # ~1 s of timed GPU work per line, a whole number of rotations
+    if M > 32:
+        return 200, 20
+    return 100 * w.sets, 4 * w.sets
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: every workload runs on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from swiglu_mlp_rmsnorm_amd import synth
+    jobs = []
+    if args.all:
+        for wname, w in synth.WORKLOADS.items():
+            for M in w.Ms:
+                jobs.append((wname, M))
+    else:
+        w = synth.WORKLOADS[args.workload]
+        jobs.append((args.workload, args.M if args.M is not None else w.Ms[0]))
+    for wname, M in jobs:
+        w = synth.WORKLOADS[wname]
+        s, wu = default_steps(w, M)
+        steps = args.steps if args.steps is not None else s
+        warmup = args.warmup if args.warmup is not None else wu
+        rec = run_one(wname, M, steps, warmup, args)
+        print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

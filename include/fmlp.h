@@ -1,0 +1,180 @@
+/*
+ * fmlp.h -- C ABI of libfmlp.so: the fused gated (SwiGLU) MLP with an RMSNorm
+ * prologue, for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * The operation (FastTPS review, xllm-io paper-review blog, section 3
+ * "technical architecture", Eq(1), and the MLP-block flow / Figure 4 on the
+ * same page):
+ *
+ *     n_m   = gamma * x_m / sqrt(mean_k(x_mk^2) + eps)          (RMSNorm, part1)
+ *     z_m   = W_gu n_m        (gate and up rows interleaved, part2)
+ *     a_mi  = SiLU(z_m[2i]) * z_m[2i+1],  SiLU(t) = t / (1 + e^-t)
+ *     y_m   = W_down a_m                                         (part3)
+ *
+ * i.e. y = W_down(SiLU(W_gate n) * (W_up n)), with the gate/up matrices stored
+ * as one row-interleaved matrix (llama.cpp PR digest on blog.cecily.jp: gate
+ * and up rows alternate so one matmul pass produces both, and the GLU is
+ * applied in that same pass).
+ *
+ * Conventions for every entry point:
+ *   - Every buffer pointer is a caller-owned DEVICE pointer (hipMalloc'd or a
+ *     torch CUDA tensor's data_ptr) on the current HIP device, 16-byte
+ *     aligned. The library never allocates, frees or keeps a pointer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream). Work is enqueued asynchronously on it; only
+ *     fmlp_quantize_int4 synchronises (it must report fp16 scale overflow).
+ *   - Matrices are row-major, nn.Linear-shaped [out_features, in_features].
+ *     bf16 / fp16 values are raw 16-bit IEEE patterns.
+ *   - Return value: FMLP_OK (0) or a negative fmlp_status. Argument checks
+ *     run on the host before any HIP call; a failed launch returns
+ *     FMLP_ERR_HIP and records the hipError_t for fmlp_last_hip_error().
+ *     Faults inside a kernel surface at the caller's next synchronisation,
+ *     as for any HIP kernel. Nothing aborts, throws or prints.
+ *   - Shapes: d and ff are positive multiples of 32 (the int4 group and
+ *     the 16-byte load width), d <= 65536, ff <= 262144, 0 <= M <= 2^24.
+ *   - Thread safety: all entry points may be called from several host
+ *     threads; calls on one stream execute in order.
+ */
+#ifndef FMLP_H_
+#define FMLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fmlp_status {
+  FMLP_OK = 0,
+  FMLP_ERR_INVALID_ARG = -1,       /* null pointer, bad eps, aliasing, bad enum */
+  FMLP_ERR_UNSUPPORTED_SHAPE = -2, /* d/ff/M outside the limits above */
+  FMLP_ERR_ALIGNMENT = -3,         /* a pointer is not 16-byte aligned */
+  FMLP_ERR_WORKSPACE = -4,         /* workspace smaller than fmlp_workspace_size */
+  FMLP_ERR_RANGE = -5,             /* int4 scale not a finite fp16 */
+  FMLP_ERR_HIP = -6,               /* a HIP runtime call or launch failed */
+  FMLP_ERR_DEVICE = -7             /* current device is not gfx950 */
+};
+
+enum fmlp_wtype {
+  FMLP_W_BF16 = 0,     /* bf16 weights */
+  FMLP_W_INT4_G32 = 1  /* int4 codes + fp16 scales, groups of 32 along K */
+};
+
+enum fmlp_path {
+  FMLP_PATH_AUTO = 0,    /* decode kernels for M <= 32, MFMA GEMMs above */
+  FMLP_PATH_DECODE = 1,  /* force the decode (weight-streaming) kernels; M <= 32 */
+  FMLP_PATH_PREFILL = 2  /* force the tiled MFMA GEMM path; any M */
+};
+
+/*
+ * Interleave gate and up weights into one matrix (the "one big matmul" of
+ * FastTPS Fusion MLP, FastTPS review section 3 item 3; row interleave as in
+ * the llama.cpp PR digest).
+ *   w_gate, w_up : bf16 [ff, d], read only.
+ *   w_gu         : bf16 [2ff, d], written: row 2i = w_gate row i,
+ *                  row 2i+1 = w_up row i. Bit copies, no arithmetic.
+ *   w_gu must not overlap either input (FMLP_ERR_INVALID_ARG).
+ */
+int fmlp_pack_interleaved(const void* w_gate, const void* w_up, void* w_gu,
+                          int64_t ff, int64_t d, void* stream);
+
+/*
+ * Quantise a bf16 matrix to symmetric int4 with one fp16 scale per group of
+ * 32 consecutive elements along K (the pages only name Q4_K / Q4_K_M in the
+ * llama.cpp PR digest; this format is the plainest symmetric reading):
+ *   s = fp16_rne( fp32(max_group |w|) / 7 )      (IEEE fp32 division)
+ *   q = clamp( round_half_even( fp32(w) / fp32(s) ), -8, 7 ),  q = 0 if s == 0
+ *   w      : bf16 [rows, K], K a multiple of 32.
+ *   q      : uint8 [rows, K/2]; element k in byte k/2, even k in the low
+ *            nibble, two's complement.
+ *   scales : fp16 [rows, K/32].
+ * Synchronises `stream`. Returns FMLP_ERR_RANGE if some group holds a
+ * non-finite weight or its scale overflows fp16 (outputs then undefined).
+ * Quantising rows of an interleaved matrix equals interleaving quantised
+ * rows, because groups never cross rows.
+ */
+int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
+                       void* scales, void* stream);
+
+/*
+ * Expand int4 codes to fp32: out[r,k] = float(s[r,k/32]) * q[r,k], which is
+ * exact in fp32. A test hook for the in-register dequantisation that the
+ * int4 forward kernels perform; not used by fmlp_forward.
+ *   q [rows, K/2] uint8, scales [rows, K/32] fp16, out [rows, K] fp32.
+ */
+int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows,
+                      int64_t K, float* out, void* stream);
+
+/*
+ * Bytes of scratch fmlp_forward needs for this problem (for either path),
+ * or 0 when the shape is unsupported. Depends only on the arguments.
+ */
+size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
+
+/*
+ * y = W_down( SiLU(W_gate n) * (W_up n) ),  n = RMSNorm(x; gamma, eps),
+ * computed row by row of x (rows are independent).
+ *   x          : bf16 [M, d]          gamma : bf16 [d]
+ *   eps        : finite, >= 0 (added to mean(x^2) inside the square root)
+ *   wtype      : FMLP_W_BF16: w_gu bf16 [2ff, d], w_down bf16 [d, ff],
+ *                             gu_scales and down_scales ignored (may be NULL)
+ *                FMLP_W_INT4_G32: w_gu uint8 [2ff, d/2] + gu_scales fp16
+ *                             [2ff, d/32]; w_down uint8 [d, ff/2] +
+ *                             down_scales fp16 [d, ff/32] (fmlp_quantize_int4
+ *                             layout)
+ *   y          : bf16 [M, d], written (round to nearest even); must not
+ *                overlap any other buffer.
+ *   workspace  : device scratch of at least fmlp_workspace_size(M,d,ff,wtype)
+ *                bytes; contents on entry are ignored, on exit undefined.
+ *   M == 0 is a no-op returning FMLP_OK (x and y may then be NULL).
+ * Accumulation is fp32. The normalised input is kept in fp32-equivalent
+ * precision on the decode path and in fp16 on the MFMA path; the SiLU*mul
+ * intermediate is fp32-equivalent (decode) or fp16 (MFMA path); see the
+ * numerics notes in the repository's design document. Not bitwise identical
+ * across paths; deterministic for a given path and shape.
+ */
+int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
+                 const void* w_gu, const void* gu_scales, const void* w_down,
+                 const void* down_scales, void* y, int64_t M, int64_t d,
+                 int64_t ff, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * fmlp_forward with the kernel path chosen by the caller (enum fmlp_path);
+ * used to test both paths at the same shapes. FMLP_PATH_DECODE with M > 32
+ * returns FMLP_ERR_UNSUPPORTED_SHAPE.
+ */
+int fmlp_forward_path(const void* x, const void* gamma, float eps,
+                      int32_t wtype, const void* w_gu, const void* gu_scales,
+                      const void* w_down, const void* down_scales, void* y,
+                      int64_t M, int64_t d, int64_t ff, void* workspace,
+                      size_t workspace_bytes, void* stream, int32_t path);
+
+/*
+ * Per-kernel timing (measurement support, not needed for computing).
+ * fmlp_profile_enable(1) discards earlier records and starts bracketing every
+ * kernel the library launches with a pair of HIP events recorded on the
+ * launch's own stream; fmlp_profile_enable(0) stops recording (records are
+ * kept until the next enable). fmlp_profile_read synchronises the recorded
+ * events of one kernel kind and returns how many launches were recorded and
+ * their summed GPU time in milliseconds. Kinds are 0 .. n-1 in the order of
+ * fmlp_kernel_name, which returns NULL past the last kind. Events add a
+ * little GPU time per launch, so timing runs should be separate from
+ * throughput runs.
+ */
+int fmlp_profile_enable(int32_t on);
+int fmlp_profile_read(int32_t kind, int64_t* launches, double* total_ms);
+const char* fmlp_kernel_name(int32_t kind);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fmlp_status_string(int status);
+
+/* hipError_t of this thread's most recent FMLP_ERR_HIP (0 if none). */
+int fmlp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FMLP_H_ */

@@ -1,0 +1,221 @@
+// C ABI of libfmlp.so (declared in include/fmlp.h): argument validation,
+// path choice and kernel launch. Validation is host-only and runs before any
+// HIP call, so every argument error is reported without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fmlp.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int t_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  t_last_hip_error = (int)e;
+  return FMLP_ERR_HIP;
+}
+
+constexpr int64_t kMaxD = 65536, kMaxFF = 262144, kMaxM = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, size_t bytes) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return Span{b, b + bytes};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool shape_ok(int64_t d, int64_t ff) {
+  return d > 0 && ff > 0 && d % 32 == 0 && ff % 32 == 0 && d <= kMaxD && ff <= kMaxFF;
+}
+
+// Device check, cached once per device (querying properties on every launch
+// costs host time in a decode loop; the V100 report in the llama.cpp digest
+// measured exactly that).
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return FMLP_ERR_DEVICE;
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      g_dev_ok[dev] = 0;
+      return;
+    }
+    g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  return g_dev_ok[dev] ? FMLP_OK : FMLP_ERR_DEVICE;
+}
+
+std::mutex g_quant_mutex;  // the range flag is one per device
+
+}  // namespace
+
+extern "C" {
+
+const char* fmlp_status_string(int status) {
+  switch (status) {
+    case FMLP_OK: return "ok";
+    case FMLP_ERR_INVALID_ARG: return "invalid argument";
+    case FMLP_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case FMLP_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+    case FMLP_ERR_WORKSPACE: return "workspace too small";
+    case FMLP_ERR_RANGE: return "int4 scale out of fp16 range";
+    case FMLP_ERR_HIP: return "HIP runtime error";
+    case FMLP_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int fmlp_last_hip_error(void) { return t_last_hip_error; }
+
+int fmlp_pack_interleaved(const void* w_gate, const void* w_up, void* w_gu, int64_t ff, int64_t d,
+                          void* stream) {
+  if (!w_gate || !w_up || !w_gu) return FMLP_ERR_INVALID_ARG;
+  if (!shape_ok(d, ff)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_gu)) return FMLP_ERR_ALIGNMENT;
+  const size_t in_b = (size_t)ff * d * 2;
+  const Span out = span(w_gu, 2 * in_b);
+  if (overlap(out, span(w_gate, in_b)) || overlap(out, span(w_up, in_b)))
+    return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  hipError_t e = fmlp::launch_pack(static_cast<const uint16_t*>(w_gate),
+                                   static_cast<const uint16_t*>(w_up), static_cast<uint16_t*>(w_gu),
+                                   ff, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* scales,
+                       void* stream) {
+  if (!w || !q || !scales) return FMLP_ERR_INVALID_ARG;
+  if (rows <= 0 || K <= 0 || K % 32 != 0 || K > kMaxFF || rows > kMaxFF * 2)
+    return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FMLP_ERR_ALIGNMENT;
+  const Span sw = span(w, (size_t)rows * K * 2), sq = span(q, (size_t)rows * K / 2),
+             ss = span(scales, (size_t)rows * (K / 32) * 2);
+  if (overlap(sw, sq) || overlap(sw, ss) || overlap(sq, ss)) return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  std::lock_guard<std::mutex> lock(g_quant_mutex);
+  int range_error = 0;
+  hipError_t e = fmlp::launch_quantize(static_cast<const uint16_t*>(w), rows, K,
+                                       static_cast<uint8_t*>(q), static_cast<uint16_t*>(scales),
+                                       static_cast<hipStream_t>(stream), &range_error);
+  if (e != hipSuccess) return hip_fail(e);
+  return range_error ? FMLP_ERR_RANGE : FMLP_OK;
+}
+
+int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K, float* out,
+                      void* stream) {
+  if (!q || !scales || !out) return FMLP_ERR_INVALID_ARG;
+  if (rows <= 0 || K <= 0 || K % 32 != 0 || K > kMaxFF || rows > kMaxFF * 2)
+    return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(q) || !aligned16(scales) || !aligned16(out)) return FMLP_ERR_ALIGNMENT;
+  const Span so = span(out, (size_t)rows * K * 4);
+  if (overlap(so, span(q, (size_t)rows * K / 2)) ||
+      overlap(so, span(scales, (size_t)rows * (K / 32) * 2)))
+    return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  hipError_t e = fmlp::launch_dequant(static_cast<const uint8_t*>(q),
+                                      static_cast<const uint16_t*>(scales), rows, K, out,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
+  if (M < 0 || M > kMaxM || !shape_ok(d, ff) || (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32))
+    return 0;
+  size_t b = fmlp::prefill_workspace_bytes(M, d, ff);
+  if (M <= fmlp::kDecodeMaxM) {
+    const size_t dec = fmlp::decode_workspace_bytes(M, d, ff);
+    b = dec > b ? dec : b;
+  }
+  return b + 256;  // room to align the base
+}
+
+int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype,
+                      const void* w_gu, const void* gu_scales, const void* w_down,
+                      const void* down_scales, void* y, int64_t M, int64_t d, int64_t ff,
+                      void* workspace, size_t workspace_bytes, void* stream, int32_t path) {
+  if (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32) return FMLP_ERR_INVALID_ARG;
+  if (path != FMLP_PATH_AUTO && path != FMLP_PATH_DECODE && path != FMLP_PATH_PREFILL)
+    return FMLP_ERR_INVALID_ARG;
+  if (M < 0) return FMLP_ERR_INVALID_ARG;
+  if (!shape_ok(d, ff) || M > kMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.0f) return FMLP_ERR_INVALID_ARG;
+  const bool int4 = wtype == FMLP_W_INT4_G32;
+  if (M == 0) return FMLP_OK;
+  if (!x || !gamma || !w_gu || !w_down || !y || !workspace) return FMLP_ERR_INVALID_ARG;
+  if (int4 && (!gu_scales || !down_scales)) return FMLP_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(w_gu) || !aligned16(w_down) ||
+      !aligned16(y) || !aligned16(workspace) || (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))))
+    return FMLP_ERR_ALIGNMENT;
+
+  const bool decode = path == FMLP_PATH_DECODE || (path == FMLP_PATH_AUTO && M <= fmlp::kDecodeMaxM);
+  if (decode && M > fmlp::kDecodeMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!decode && int4) return FMLP_ERR_UNSUPPORTED_SHAPE;  // int4 runs on the decode kernels only
+
+  const size_t need = decode ? fmlp::decode_workspace_bytes(M, d, ff)
+                             : fmlp::prefill_workspace_bytes(M, d, ff);
+  // align the workspace base to 256 bytes inside the caller's buffer
+  const uintptr_t wbase = reinterpret_cast<uintptr_t>(workspace);
+  const uintptr_t abase = (wbase + 255) & ~uintptr_t(255);
+  if (workspace_bytes < need + (abase - wbase)) return FMLP_ERR_WORKSPACE;
+
+  const size_t wgu_b = int4 ? (size_t)2 * ff * d / 2 : (size_t)2 * ff * d * 2;
+  const size_t wd_b = int4 ? (size_t)d * ff / 2 : (size_t)d * ff * 2;
+  const Span sy = span(y, (size_t)M * d * 2);
+  if (overlap(sy, span(x, (size_t)M * d * 2)) || overlap(sy, span(gamma, (size_t)d * 2)) ||
+      overlap(sy, span(w_gu, wgu_b)) || overlap(sy, span(w_down, wd_b)) ||
+      overlap(sy, span(workspace, workspace_bytes)))
+    return FMLP_ERR_INVALID_ARG;
+  if (int4 && (overlap(sy, span(gu_scales, (size_t)2 * ff * (d / 32) * 2)) ||
+               overlap(sy, span(down_scales, (size_t)d * (ff / 32) * 2))))
+    return FMLP_ERR_INVALID_ARG;
+  const Span sw = span(workspace, workspace_bytes);
+  if (overlap(sw, span(x, (size_t)M * d * 2)) || overlap(sw, span(gamma, (size_t)d * 2)) ||
+      overlap(sw, span(w_gu, wgu_b)) || overlap(sw, span(w_down, wd_b)))
+    return FMLP_ERR_INVALID_ARG;
+
+  if (int st = check_device()) return st;
+
+  fmlp::Problem p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.gamma = static_cast<const uint16_t*>(gamma);
+  p.eps = eps;
+  p.wtype = wtype;
+  p.w_gu = w_gu;
+  p.s_gu = static_cast<const uint16_t*>(gu_scales);
+  p.w_down = w_down;
+  p.s_down = static_cast<const uint16_t*>(down_scales);
+  p.y = static_cast<uint16_t*>(y);
+  p.M = (int)M;
+  p.d = (int)d;
+  p.ff = (int)ff;
+  p.ws = reinterpret_cast<char*>(abase);
+  p.ws_bytes = workspace_bytes - (abase - wbase);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = decode ? fmlp::launch_decode(p, s) : fmlp::launch_prefill(p, s);
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype, const void* w_gu,
+                 const void* gu_scales, const void* w_down, const void* down_scales, void* y,
+                 int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  return fmlp_forward_path(x, gamma, eps, wtype, w_gu, gu_scales, w_down, down_scales, y, M, d,
+                           ff, workspace, workspace_bytes, stream, FMLP_PATH_AUTO);
+}
+
+}  // extern "C"

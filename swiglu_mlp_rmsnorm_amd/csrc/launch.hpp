@@ -1,0 +1,43 @@
+// Internal host-side interface between the C ABI (fmlp_api.hip) and the
+// kernel translation units. Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fmlp {
+
+// One forward problem after argument validation.
+struct Problem {
+  const uint16_t* x;       // bf16 [M, d]
+  const uint16_t* gamma;   // bf16 [d]
+  float eps;
+  int wtype;               // 0 bf16, 1 int4 group-32
+  const void* w_gu;        // bf16 [2ff, d] | uint8 [2ff, d/2]
+  const uint16_t* s_gu;    // fp16 [2ff, d/32] (int4)
+  const void* w_down;      // bf16 [d, ff]  | uint8 [d, ff/2]
+  const uint16_t* s_down;  // fp16 [d, ff/32] (int4)
+  uint16_t* y;             // bf16 [M, d]
+  int M, d, ff;
+  char* ws;                // workspace base (256-byte aligned)
+  size_t ws_bytes;
+};
+
+constexpr int kDecodeMaxM = 32;
+
+// Workspace layout, shared by the sizing query and the launchers.
+size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff);
+size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff);
+
+hipError_t launch_pack(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* w_gu, int64_t ff,
+                       int64_t d, hipStream_t stream);
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q,
+                           uint16_t* scales, hipStream_t stream, int* range_error);
+hipError_t launch_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t K,
+                          float* out, hipStream_t stream);
+
+hipError_t launch_decode(const Problem& p, hipStream_t stream);
+hipError_t launch_prefill(const Problem& p, hipStream_t stream);
+
+}  // namespace fmlp

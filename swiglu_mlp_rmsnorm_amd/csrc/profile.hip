@@ -1,0 +1,87 @@
+// Per-kernel timing with HIP events (see profile.hpp). Host code only.
+#include "profile.hpp"
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fmlp.h"
+
+namespace fmlp {
+namespace {
+
+struct Record {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+std::atomic<bool> g_on{false};
+std::mutex g_mu;
+std::vector<Record> g_records;
+thread_local hipEvent_t t_pending = nullptr;
+
+void clear_locked() {
+  for (Record& r : g_records) {
+    hipEventDestroy(r.start);
+    hipEventDestroy(r.stop);
+  }
+  g_records.clear();
+}
+
+}  // namespace
+
+bool profiling_enabled() { return g_on.load(std::memory_order_relaxed); }
+
+void profile_record(int kind, hipStream_t stream, bool start) {
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return;
+  hipEventRecord(ev, stream);
+  if (start) {
+    t_pending = ev;
+    return;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (t_pending) g_records.push_back(Record{kind, t_pending, ev});
+  else hipEventDestroy(ev);
+  t_pending = nullptr;
+}
+
+}  // namespace fmlp
+
+extern "C" {
+
+static const char* const kKernelNames[fmlp::KK_COUNT] = {
+    "pack_interleaved", "quantize_int4",   "dequant_int4",  "decode_gateup_bf16",
+    "decode_down_bf16", "decode_gateup_int4", "decode_down_int4", "rms_prep_f16",
+    "gemm_gateup_silu_f16", "gemm_down_f16"};
+
+int fmlp_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(fmlp::g_mu);
+  fmlp::clear_locked();
+  fmlp::g_on.store(on != 0, std::memory_order_relaxed);
+  return FMLP_OK;
+}
+
+int fmlp_profile_read(int32_t kind, int64_t* launches, double* total_ms) {
+  if (kind < 0 || kind >= fmlp::KK_COUNT || !launches || !total_ms) return FMLP_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(fmlp::g_mu);
+  int64_t n = 0;
+  double ms = 0.0;
+  for (const fmlp::Record& r : fmlp::g_records) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return FMLP_ERR_HIP;
+    float e = 0.f;
+    if (hipEventElapsedTime(&e, r.start, r.stop) != hipSuccess) return FMLP_ERR_HIP;
+    ms += e;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return FMLP_OK;
+}
+
+const char* fmlp_kernel_name(int32_t kind) {
+  return (kind >= 0 && kind < fmlp::KK_COUNT) ? kKernelNames[kind] : nullptr;
+}
+
+}  // extern "C"

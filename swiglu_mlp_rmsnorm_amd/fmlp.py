@@ -1,0 +1,253 @@
+"""Thin Python binding over libfmlp.so (C ABI in include/fmlp.h).
+
+Argument marshalling only: torch tensors in, raw device pointers and the
+current HIP stream handle out, status codes turned into exceptions. Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback of any kind, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmlp.so")
+_lock = threading.Lock()
+_lib = None
+
+FMLP_OK = 0
+FMLP_ERR_INVALID_ARG = -1
+FMLP_ERR_UNSUPPORTED_SHAPE = -2
+FMLP_ERR_ALIGNMENT = -3
+FMLP_ERR_WORKSPACE = -4
+FMLP_ERR_RANGE = -5
+FMLP_ERR_HIP = -6
+FMLP_ERR_DEVICE = -7
+
+FMLP_W_BF16 = 0
+FMLP_W_INT4_G32 = 1
+
+FMLP_PATH_AUTO = 0
+FMLP_PATH_DECODE = 1
+FMLP_PATH_PREFILL = 2
+
+EXPORTS = (
+    "fmlp_pack_interleaved", "fmlp_quantize_int4", "fmlp_dequant_int4",
+    "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path",
+    "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
+    "fmlp_profile_read", "fmlp_kernel_name",
+)
+
+
+class FmlpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().fmlp_status_string(status).decode()
+        if status == FMLP_ERR_HIP:
+            msg += f" (hipError_t {lib().fmlp_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m swiglu_mlp_rmsnorm_amd.build_lib` (hipcc, gfx950)")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.fmlp_pack_interleaved.argtypes = [P, P, P, I64, I64, P]
+        L.fmlp_quantize_int4.argtypes = [P, I64, I64, P, P, P]
+        L.fmlp_dequant_int4.argtypes = [P, P, I64, I64, P, P]
+        L.fmlp_workspace_size.argtypes = [I64, I64, I64, I32]
+        L.fmlp_workspace_size.restype = SZ
+        fwd = [P, P, ctypes.c_float, I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
+        L.fmlp_forward.argtypes = fwd
+        L.fmlp_forward_path.argtypes = fwd + [I32]
+        L.fmlp_status_string.argtypes = [ctypes.c_int]
+        L.fmlp_status_string.restype = ctypes.c_char_p
+        L.fmlp_last_hip_error.argtypes = []
+        L.fmlp_profile_enable.argtypes = [I32]
+        L.fmlp_profile_read.argtypes = [I32, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_double)]
+        L.fmlp_kernel_name.argtypes = [I32]
+        L.fmlp_kernel_name.restype = ctypes.c_char_p
+        for name in ("fmlp_pack_interleaved", "fmlp_quantize_int4", "fmlp_dequant_int4",
+                     "fmlp_forward", "fmlp_forward_path", "fmlp_last_hip_error",
+                     "fmlp_profile_enable", "fmlp_profile_read"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(st: int, where: str):
+    if st != FMLP_OK:
+        raise FmlpError(st, where)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def fmlp_status_string(status: int) -> str:
+    return lib().fmlp_status_string(status).decode()
+
+
+def fmlp_pack_interleaved(w_gate, w_up, w_gu=None, stream=None):
+    """W_gu[2i] = W_gate[i], W_gu[2i+1] = W_up[i]; bf16 [ff,d] x2 -> [2ff,d]."""
+    _need(w_gate, torch.bfloat16, "w_gate")
+    _need(w_up, torch.bfloat16, "w_up")
+    ff, d = w_gate.shape
+    if w_up.shape != (ff, d):
+        raise ValueError("w_up shape differs from w_gate")
+    if w_gu is None:
+        w_gu = torch.empty((2 * ff, d), dtype=torch.bfloat16, device=w_gate.device)
+    _need(w_gu, torch.bfloat16, "w_gu")
+    if w_gu.shape != (2 * ff, d):
+        raise ValueError("w_gu must be [2ff, d]")
+    _check(lib().fmlp_pack_interleaved(_ptr(w_gate), _ptr(w_up), _ptr(w_gu), ff, d,
+                                       _stream(stream)), "fmlp_pack_interleaved")
+    return w_gu
+
+
+def fmlp_quantize_int4(w, q=None, scales=None, stream=None):
+    """bf16 [rows,K] -> (uint8 codes [rows,K/2], fp16 scales [rows,K/32])."""
+    _need(w, torch.bfloat16, "w")
+    rows, K = w.shape
+    if q is None:
+        q = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.float16, device=w.device)
+    _need(q, torch.uint8, "q")
+    _need(scales, torch.float16, "scales")
+    _check(lib().fmlp_quantize_int4(_ptr(w), rows, K, _ptr(q), _ptr(scales), _stream(stream)),
+           "fmlp_quantize_int4")
+    return q, scales
+
+
+def fmlp_dequant_int4(q, scales, out=None, stream=None):
+    """(codes, scales) -> exact fp32 [rows, K]."""
+    _need(q, torch.uint8, "q")
+    _need(scales, torch.float16, "scales")
+    rows, half = q.shape
+    K = 2 * half
+    if out is None:
+        out = torch.empty((rows, K), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    _check(lib().fmlp_dequant_int4(_ptr(q), _ptr(scales), rows, K, _ptr(out), _stream(stream)),
+           "fmlp_dequant_int4")
+    return out
+
+
+def fmlp_workspace_size(M: int, d: int, ff: int, wtype: int = FMLP_W_BF16) -> int:
+    return int(lib().fmlp_workspace_size(M, d, ff, wtype))
+
+
+def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream, path):
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    M, d = x.shape
+    int4 = w_gu.dtype == torch.uint8
+    if int4:
+        _need(w_gu, torch.uint8, "w_gu")
+        _need(w_down, torch.uint8, "w_down")
+        _need(gu_scales, torch.float16, "gu_scales")
+        _need(down_scales, torch.float16, "down_scales")
+        ff = w_down.shape[1] * 2
+        wtype = FMLP_W_INT4_G32
+        if w_gu.shape != (2 * ff, d // 2) or w_down.shape != (d, ff // 2):
+            raise ValueError("int4 weight shapes do not match x")
+    else:
+        _need(w_gu, torch.bfloat16, "w_gu")
+        _need(w_down, torch.bfloat16, "w_down")
+        ff = w_down.shape[1]
+        wtype = FMLP_W_BF16
+        if w_gu.shape != (2 * ff, d) or w_down.shape != (d, ff):
+            raise ValueError("bf16 weight shapes do not match x")
+    if gamma.shape != (d,):
+        raise ValueError("gamma must be [d]")
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if y.shape != (M, d):
+        raise ValueError("y must be [M, d]")
+    need = fmlp_workspace_size(M, d, ff, wtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _need(workspace, torch.uint8, "workspace")
+    args = (_ptr(x), _ptr(gamma), float(eps), wtype, _ptr(w_gu), _ptr(gu_scales), _ptr(w_down),
+            _ptr(down_scales), _ptr(y), M, d, ff, _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    if path is None:
+        _check(lib().fmlp_forward(*args), "fmlp_forward")
+    else:
+        _check(lib().fmlp_forward_path(*args, path), "fmlp_forward_path")
+    return y
+
+
+def fmlp_forward(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
+                 workspace=None, stream=None):
+    """y = W_down(SiLU(W_gate n) * (W_up n)), n = RMSNorm(x); bf16 x [M,d] -> y [M,d].
+
+    bf16 weights: w_gu [2ff,d], w_down [d,ff]. int4 weights: uint8 w_gu
+    [2ff,d/2] + fp16 gu_scales, uint8 w_down [d,ff/2] + fp16 down_scales.
+    Output and workspace are allocated with torch when not given.
+    """
+    return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
+                    None)
+
+
+def fmlp_forward_path(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
+                      workspace=None, stream=None, path=FMLP_PATH_AUTO):
+    """fmlp_forward with the kernel path chosen by the caller (FMLP_PATH_*)."""
+    return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
+                    path)
+
+
+def fmlp_kernel_names() -> list:
+    """Kernel kinds known to the profiler, in kind order."""
+    names, k = [], 0
+    while True:
+        n = lib().fmlp_kernel_name(k)
+        if n is None:
+            return names
+        names.append(n.decode())
+        k += 1
+
+
+def fmlp_profile_enable(on: bool = True) -> None:
+    _check(lib().fmlp_profile_enable(1 if on else 0), "fmlp_profile_enable")
+
+
+def fmlp_profile_read() -> dict:
+    """{kernel name: (launches, total GPU ms)} for every kind with launches."""
+    out = {}
+    for k, name in enumerate(fmlp_kernel_names()):
+        n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+        _check(lib().fmlp_profile_read(k, ctypes.byref(n), ctypes.byref(ms)), "fmlp_profile_read")
+        if n.value:
+            out[name] = (int(n.value), float(ms.value))
+    return out

@@ -1,0 +1,127 @@
+"""The C ABI boundary, without a GPU: the library loads, exports every entry
+point include/fmlp.h declares, and rejects bad arguments on the host before
+any HIP call (so these run on a CPU-only machine)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from swiglu_mlp_rmsnorm_amd import fmlp as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmlp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(F._LIB_PATH),
+                                reason="libfmlp.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fmlp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(F.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", F._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fmlp_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(F.lib(), name)
+
+
+# distinct, 16-byte aligned fake device addresses far apart (never dereferenced)
+A = {k: ctypes.c_void_p((i + 1) << 36) for i, k in enumerate(
+    ["x", "g", "wgu", "sgu", "wd", "sd", "y", "ws"])}
+BIG = 1 << 34
+
+
+def fwd(M=1, d=256, ff=704, eps=1e-5, wtype=0, path=0, ws_bytes=BIG, **over):
+    p = dict(A)
+    p.update(over)
+    return F.lib().fmlp_forward_path(p["x"], p["g"], eps, wtype, p["wgu"], p["sgu"], p["wd"],
+                                     p["sd"], p["y"], M, d, ff, p["ws"], ws_bytes, None, path)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wtype=7), F.FMLP_ERR_INVALID_ARG),
+    (dict(path=9), F.FMLP_ERR_INVALID_ARG),
+    (dict(M=-1), F.FMLP_ERR_INVALID_ARG),
+    (dict(d=48), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(ff=0), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(ff=720), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(d=65536 + 32), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=(1 << 24) + 1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(eps=float("nan")), F.FMLP_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), F.FMLP_ERR_INVALID_ARG),
+    (dict(eps=-1e-5), F.FMLP_ERR_INVALID_ARG),
+    (dict(x=None), F.FMLP_ERR_INVALID_ARG),
+    (dict(ws=None), F.FMLP_ERR_INVALID_ARG),
+    (dict(wtype=1, sgu=None), F.FMLP_ERR_INVALID_ARG),
+    (dict(y=ctypes.c_void_p((7 << 36) + 8)), F.FMLP_ERR_ALIGNMENT),
+    (dict(wgu=ctypes.c_void_p((3 << 36) + 4)), F.FMLP_ERR_ALIGNMENT),
+    (dict(M=33, path=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=64, wtype=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(ws_bytes=100), F.FMLP_ERR_WORKSPACE),
+    (dict(y=A["x"]), F.FMLP_ERR_INVALID_ARG),
+    (dict(y=A["ws"]), F.FMLP_ERR_INVALID_ARG),
+    (dict(ws=A["wd"]), F.FMLP_ERR_INVALID_ARG),
+])
+def test_forward_rejects_before_any_hip_call(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_zero_tokens_is_a_no_op():
+    assert fwd(M=0, x=None, y=None, ws=None) == F.FMLP_OK
+
+
+def test_workspace_size():
+    ws = F.fmlp_workspace_size
+    assert ws(1, 256, 704) > 0
+    assert ws(32, 4096, 14336) >= ws(1, 4096, 14336)
+    assert ws(2048, 4096, 14336) >= 2 * 2048 * (4096 + 14336)
+    assert ws(1, 48, 704) == 0 and ws(-1, 256, 704) == 0 and ws(1, 256, 704, 5) == 0
+    # exactly the reported size is accepted by the host-side checks
+    need = ws(1, 256, 704)
+    assert fwd(ws_bytes=need - 256 - 1) == F.FMLP_ERR_WORKSPACE
+
+
+def test_pack_quant_dequant_validation():
+    L = F.lib()
+    a, b, c = A["x"], A["g"], A["y"]
+    assert L.fmlp_pack_interleaved(None, b, c, 704, 256, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_interleaved(a, b, c, 704, 250, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_pack_interleaved(a, b, ctypes.c_void_p(A["y"].value + 2), 704, 256,
+                                   None) == F.FMLP_ERR_ALIGNMENT
+    assert L.fmlp_pack_interleaved(a, b, a, 704, 256, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_quantize_int4(a, 4, 48, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_quantize_int4(a, 4, 64, None, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_quantize_int4(a, 4, 64, a, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_dequant_int4(a, b, 0, 64, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_dequant_int4(a, b, 4, 64, ctypes.c_void_p(A["y"].value + 4),
+                               None) == F.FMLP_ERR_ALIGNMENT
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        s = F.fmlp_status_string(st)
+        assert s and s != "unknown status"
+    assert F.fmlp_status_string(-99) == "unknown status"
+    assert F.lib().fmlp_last_hip_error() == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        F.fmlp_forward(x, torch.zeros(256, dtype=torch.bfloat16), 1e-5,
+                       torch.zeros(1408, 256, dtype=torch.bfloat16),
+                       torch.zeros(256, 704, dtype=torch.bfloat16))
+    assert math.isfinite(1e-5)
