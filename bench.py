@@ -83,8 +83,9 @@ def kernel_source_sha(kernel):
     """Hash of the HIP source that defines a kernel kind (to expire counter data)."""
     src = {
         "decode_gateup_bf16": "decode.hip", "decode_down_bf16": "decode.hip",
-        "decode_gateup_int4": "decode_int4.hip", "decode_down_int4": "decode_int4.hip",
+        "decode_gateup_int4": "decode.hip", "decode_down_int4": "decode.hip",
         "gemm_gateup_silu_f16": "prefill.hip", "gemm_down_f16": "prefill.hip",
+        "act_prep": "decode.hip",
     }.get(kernel)
     if src is None:
         return None
@@ -117,9 +118,15 @@ def measured_traffic(kernel, workload, M):
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
-    """Time the fp64 CPU oracle on a bounded sample of the same workload."""
+    """Time the fp64 CPU oracle on a bounded sample of the same workload
+    (weight set 0; the seeded row-major weights, or for int4 the seeded tiled
+    buffers expanded by the oracle's own layout code)."""
     from oracle import oracle
     x, g = host_inputs
+    if w.wtype == "int4":
+        q_gu, s_gu, q_d, s_d = host_layer
+        host_layer = (*oracle.untile_int4(q_gu, s_gu, 2 * w.ff, w.d),
+                      *oracle.untile_int4(q_d, s_d, w.d, w.ff))
     # rows are independent: for large M, run row subsets until the budget is spent
     rows_per_call = M if M <= 32 else 1
     done_rows, calls = 0, 0
@@ -131,12 +138,12 @@ def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
             q_gu, s_gu, q_d, s_d = host_layer
             oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, q_d, s_d)
         else:
-            wgu, wd = host_layer
-            oracle.forward_bf16(xs, g, w_eps(), wgu, wd)
+            wg, wu, wd = host_layer
+            oracle.forward_unfused(xs, g, w_eps(), wg, wu, wd)
         done_rows += xs.shape[0]
         calls += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or (rows_per_call == M and calls >= 200):
+        if el >= budget_s:
             break
     return {
         "value": done_rows / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
@@ -163,13 +170,18 @@ def run_one(wname, M, steps, warmup, args):
     path = "decode" if M <= 32 else "prefill"
     log(f"[bench] {wname} M={M}: building {w.sets} weight set(s)")
     layers, xs = [], []
+    host0 = None  # row-major / untiled copies of set 0 for the CPU baseline
     for l in range(w.sets):
         if w.wtype == "int4":
             layers.append(synth.layer_int4(w, l, dev))
+            if l == 0 and not args.no_cpu_baseline:
+                host0 = tuple(synth.bits(t) for t in layers[0])
         else:
             wg, wu, wd = synth.layer_bf16(w, l, dev)
-            layers.append((F.fmlp_pack_interleaved(wg, wu), wd))
-            del wg, wu
+            layers.append((F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd)))
+            if l == 0 and not args.no_cpu_baseline:
+                host0 = (synth.bits(wg), synth.bits(wu), synth.bits(wd))
+            del wg, wu, wd
         xs.append(synth.inputs(w, M, dev, layer=l))
     torch.cuda.synchronize()
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
@@ -180,7 +192,7 @@ def run_one(wname, M, steps, warmup, args):
         L = layers[i % w.sets]
         x, g = xs[i % w.sets]
         if w.wtype == "int4":
-            F.fmlp_forward(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws)
+            F.fmlp_forward(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws, ff=ff)
         else:
             F.fmlp_forward(x, g, synth.EPS, L[0], L[1], y=y, workspace=ws)
 
@@ -242,13 +254,9 @@ def run_one(wname, M, steps, warmup, args):
 
     cpu = None
     if not args.no_cpu_baseline:
-        if w.wtype == "int4":
-            host_layer = tuple(synth.bits(t) for t in layers[0])
-        else:
-            host_layer = (synth.bits(layers[0][0]), synth.bits(layers[0][1]))
         host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
         log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
-        cpu = cpu_baseline(w, M, host_layer, host_inputs, args.cpu_seconds)
+        cpu = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds)
 
     step_gbs = sb / (ms_per_step * 1e-3) / 1e9
     step_tflops = step_flops(M, d, ff) / (ms_per_step * 1e-3) / 1e12

@@ -68,40 +68,67 @@ enum fmlp_path {
 };
 
 /*
+ * Weight storage. The library keeps every weight matrix in a
+ * "fragment-tiled" layout: a storage permutation of the logical row-major
+ * nn.Linear matrix, chosen so each 16-row x 32-column block is one
+ * contiguous 1024-byte tile that a wave64 reads with one 16-byte load per
+ * lane straight into the MFMA 16x16x32 operand layout.
+ *
+ * Tiled bf16, logical W [R, K], R % 16 == 0, K % 32 == 0: element (r, k) is
+ * stored at element index
+ *     ((r/16)*(K/32) + k/32)*512 + (((k%32)/8)*16 + r%16)*8 + k%8.
+ *
+ * Tiled int4, logical codes q [R, K] (two's complement, -8..7) and fp16
+ * scales s [R, K/32] (one per group of 32 consecutive columns), with
+ * nq = ceil(K/128): code (r, k) of group g = k/32 is nibble k%8 (bits
+ * 4*(k%8) .. +3) of 32-bit word ((r/16)*nq + g/4)*256 + (((k%32)/8)*16 +
+ * r%16)*4 + g%4; scale (r, g) is fp16 element ((r/16)*nq + g/4)*64 +
+ * (r%16)*4 + g%4. Groups past K/32 in the last super-tile of 4 groups hold
+ * zero codes and zero scales. Buffer sizes: fmlp_int4_sizes.
+ */
+
+/*
  * Interleave gate and up weights into one matrix (the "one big matmul" of
  * FastTPS Fusion MLP, FastTPS review section 3 item 3; row interleave as in
- * the llama.cpp PR digest).
- *   w_gate, w_up : bf16 [ff, d], read only.
- *   w_gu         : bf16 [2ff, d], written: row 2i = w_gate row i,
- *                  row 2i+1 = w_up row i. Bit copies, no arithmetic.
+ * the llama.cpp PR digest) and store it tiled.
+ *   w_gate, w_up : bf16 [ff, d] row-major, read only.
+ *   w_gu         : tiled bf16 of the logical [2ff, d] matrix whose row 2i is
+ *                  w_gate row i and row 2i+1 is w_up row i. Bit copies.
  *   w_gu must not overlap either input (FMLP_ERR_INVALID_ARG).
  */
 int fmlp_pack_interleaved(const void* w_gate, const void* w_up, void* w_gu,
                           int64_t ff, int64_t d, void* stream);
 
 /*
- * Quantise a bf16 matrix to symmetric int4 with one fp16 scale per group of
- * 32 consecutive elements along K (the pages only name Q4_K / Q4_K_M in the
- * llama.cpp PR digest; this format is the plainest symmetric reading):
+ * Store a bf16 row-major matrix [rows, K] tiled (used for W_down [d, ff]).
+ * rows % 16 == 0, K % 32 == 0; w_tiled (rows*K bf16) must not overlap w.
+ */
+int fmlp_pack_matrix(const void* w, void* w_tiled, int64_t rows, int64_t K,
+                     void* stream);
+
+/* Byte sizes of the tiled int4 code and scale buffers of a [rows, K] matrix. */
+int fmlp_int4_sizes(int64_t rows, int64_t K, size_t* code_bytes,
+                    size_t* scale_bytes);
+
+/*
+ * Quantise a tiled bf16 matrix (logical [rows, K]) to tiled int4 with one
+ * fp16 scale per group of 32 consecutive elements of a row (the pages only
+ * name Q4_K / Q4_K_M in the llama.cpp PR digest; this is the plainest
+ * symmetric group format):
  *   s = fp16_rne( fp32(max_group |w|) / 7 )      (IEEE fp32 division)
  *   q = clamp( round_half_even( fp32(w) / fp32(s) ), -8, 7 ),  q = 0 if s == 0
- *   w      : bf16 [rows, K], K a multiple of 32.
- *   q      : uint8 [rows, K/2]; element k in byte k/2, even k in the low
- *            nibble, two's complement.
- *   scales : fp16 [rows, K/32].
  * Synchronises `stream`. Returns FMLP_ERR_RANGE if some group holds a
  * non-finite weight or its scale overflows fp16 (outputs then undefined).
- * Quantising rows of an interleaved matrix equals interleaving quantised
- * rows, because groups never cross rows.
+ * Groups never cross rows, so quantising the interleaved gate/up matrix
+ * equals interleaving the quantised gate and up matrices.
  */
 int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
                        void* scales, void* stream);
 
 /*
- * Expand int4 codes to fp32: out[r,k] = float(s[r,k/32]) * q[r,k], which is
- * exact in fp32. A test hook for the in-register dequantisation that the
+ * Expand tiled int4 to row-major fp32 [rows, K]: out[r,k] = float(s[r,k/32])
+ * * q[r,k], exact in fp32. A test hook for the in-register expansion the
  * int4 forward kernels perform; not used by fmlp_forward.
- *   q [rows, K/2] uint8, scales [rows, K/32] fp16, out [rows, K] fp32.
  */
 int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows,
                       int64_t K, float* out, void* stream);
@@ -117,22 +144,23 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  * computed row by row of x (rows are independent).
  *   x          : bf16 [M, d]          gamma : bf16 [d]
  *   eps        : finite, >= 0 (added to mean(x^2) inside the square root)
- *   wtype      : FMLP_W_BF16: w_gu bf16 [2ff, d], w_down bf16 [d, ff],
+ *   wtype      : FMLP_W_BF16: w_gu tiled bf16 [2ff, d] (fmlp_pack_interleaved),
+ *                             w_down tiled bf16 [d, ff] (fmlp_pack_matrix);
  *                             gu_scales and down_scales ignored (may be NULL)
- *                FMLP_W_INT4_G32: w_gu uint8 [2ff, d/2] + gu_scales fp16
- *                             [2ff, d/32]; w_down uint8 [d, ff/2] +
- *                             down_scales fp16 [d, ff/32] (fmlp_quantize_int4
- *                             layout)
+ *                FMLP_W_INT4_G32: tiled int4 codes + scales of the same two
+ *                             logical matrices (fmlp_quantize_int4); int4
+ *                             runs on the decode path only (M <= 32)
  *   y          : bf16 [M, d], written (round to nearest even); must not
  *                overlap any other buffer.
  *   workspace  : device scratch of at least fmlp_workspace_size(M,d,ff,wtype)
  *                bytes; contents on entry are ignored, on exit undefined.
  *   M == 0 is a no-op returning FMLP_OK (x and y may then be NULL).
- * Accumulation is fp32. The normalised input is kept in fp32-equivalent
- * precision on the decode path and in fp16 on the MFMA path; the SiLU*mul
- * intermediate is fp32-equivalent (decode) or fp16 (MFMA path); see the
- * numerics notes in the repository's design document. Not bitwise identical
- * across paths; deterministic for a given path and shape.
+ * Accumulation is fp32. The normalised input and the SiLU*mul intermediate
+ * are kept as bf16 hi + lo pairs (about 2^-17 relative) on the bf16 decode
+ * path, and as fp16 on the int4 decode path and the MFMA prefill path
+ * (|values| must stay below 65504 there). Not bitwise identical across
+ * paths; deterministic for a given path and shape. Concurrent calls must
+ * not share a workspace.
  */
 int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
                  const void* w_gu, const void* gu_scales, const void* w_down,

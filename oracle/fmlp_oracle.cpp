@@ -138,6 +138,81 @@ void oracle_pack_interleaved(const uint16_t* w_gate, const uint16_t* w_up,
   }
 }
 
+// ---------------------------------------------------------------- tiled layouts
+// The library stores weights fragment-tiled (a storage permutation only; the
+// logical matrices are unchanged). For a logical bf16 matrix W [R, K]
+// (R % 16 == 0, K % 32 == 0), element (r, k) sits at
+//   ((r/16)*(K/32) + k/32)*512 + (((k%32)/8)*16 + r%16)*8 + k%8.
+static int64_t tiled_bf16_index(int64_t r, int64_t k, int64_t K) {
+  return ((r / 16) * (K / 32) + k / 32) * 512 + (((k % 32) / 8) * 16 + r % 16) * 8 + k % 8;
+}
+
+void oracle_tile_bf16(const uint16_t* w, int64_t R, int64_t K, uint16_t* out) {
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t k = 0; k < K; ++k) out[tiled_bf16_index(r, k, K)] = w[r * K + k];
+}
+
+void oracle_untile_bf16(const uint16_t* t, int64_t R, int64_t K, uint16_t* w) {
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t k = 0; k < K; ++k) w[r * K + k] = t[tiled_bf16_index(r, k, K)];
+}
+
+// Tiled int4: groups of 32 along K are taken four at a time ("super-tiles",
+// nq = ceil(K/128) per 16-row block, 1024 bytes each). Code (r, k) with group
+// g = k/32 lives in super-tile ((r/16)*nq + g/4), 16-byte lane slot
+// L = ((k%32)/8)*16 + r%16, 32-bit word g%4 of that slot, nibble k%8 (bits
+// 4*(k%8)). Scale (r, g) is fp16 element ((r/16)*nq + g/4)*64 + (r%16)*4 + g%4.
+// Groups past K/32 in the last super-tile hold zero codes and zero scales.
+int64_t oracle_int4_tiled_code_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 127) / 128) * 1024; }
+int64_t oracle_int4_tiled_scale_count(int64_t R, int64_t K) { return (R / 16) * ((K + 127) / 128) * 64; }
+
+static void int4_tiled_pos(int64_t r, int64_t k, int64_t K, int64_t* byte, int* shift) {
+  const int64_t nq = (K + 127) / 128, g = k / 32;
+  const int64_t lane = ((k % 32) / 8) * 16 + r % 16;
+  const int64_t word = ((r / 16) * nq + g / 4) * 256 + lane * 4 + g % 4;
+  const int nib = (int)(k % 8);
+  *byte = word * 4 + nib / 2;
+  *shift = (nib % 2) * 4;
+}
+static int64_t int4_tiled_scale_index(int64_t r, int64_t g, int64_t K) {
+  const int64_t nq = (K + 127) / 128;
+  return ((r / 16) * nq + g / 4) * 64 + (r % 16) * 4 + g % 4;
+}
+
+// row-major (q [R, K/2] even k low nibble, s [R, K/32]) -> tiled
+void oracle_tile_int4(const uint8_t* q, const uint16_t* s, int64_t R, int64_t K, uint8_t* qt,
+                      uint16_t* st) {
+  std::memset(qt, 0, (size_t)oracle_int4_tiled_code_bytes(R, K));
+  std::memset(st, 0, (size_t)oracle_int4_tiled_scale_count(R, K) * 2);
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = q[r * (K / 2) + k / 2];
+      const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+      int64_t b;
+      int sh;
+      int4_tiled_pos(r, k, K, &b, &sh);
+      qt[b] = (uint8_t)(qt[b] | (nib << sh));
+    }
+    for (int64_t g = 0; g < K / 32; ++g) st[int4_tiled_scale_index(r, g, K)] = s[r * (K / 32) + g];
+  }
+}
+
+// tiled -> row-major
+void oracle_untile_int4(const uint8_t* qt, const uint16_t* st, int64_t R, int64_t K, uint8_t* q,
+                        uint16_t* s) {
+  std::memset(q, 0, (size_t)(R * (K / 2)));
+  for (int64_t r = 0; r < R; ++r) {
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t b;
+      int sh;
+      int4_tiled_pos(r, k, K, &b, &sh);
+      const int nib = (qt[b] >> sh) & 0xF;
+      q[r * (K / 2) + k / 2] = (uint8_t)(q[r * (K / 2) + k / 2] | ((k & 1) ? nib << 4 : nib));
+    }
+    for (int64_t g = 0; g < K / 32; ++g) s[r * (K / 32) + g] = st[int4_tiled_scale_index(r, g, K)];
+  }
+}
+
 // ---------------------------------------------------------------- int4
 
 // Returns 0, or -5 when a group's scale is not a finite fp16 (a non-finite

@@ -64,6 +64,12 @@ def _load():
             "oracle_forward_bf16": (None, [P, P, D, P, P, I64, I64, I64, P]),
             "oracle_forward_int4": (None, [P, P, D, P, P, P, P, I64, I64, I64, P]),
             "oracle_omp_threads": (ctypes.c_int, []),
+            "oracle_tile_bf16": (None, [P, I64, I64, P]),
+            "oracle_untile_bf16": (None, [P, I64, I64, P]),
+            "oracle_int4_tiled_code_bytes": (I64, [I64, I64]),
+            "oracle_int4_tiled_scale_count": (I64, [I64, I64]),
+            "oracle_tile_int4": (None, [P, P, I64, I64, P, P]),
+            "oracle_untile_int4": (None, [P, P, I64, I64, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -187,3 +193,49 @@ def forward_int4(x, gamma, eps, q_gu, s_gu, q_down, s_down) -> np.ndarray:
     _load().oracle_forward_int4(_p(x), _p(gamma), eps, _p(q_gu), _p(s_gu),
                                 _p(q_down), _p(s_down), M, d, ff, _p(y))
     return y
+
+
+# ---------------------------------------------------------------- tiled layouts
+# The library's physical weight layout (see the C++ source for the index maps).
+
+def tile_bf16(w: np.ndarray) -> np.ndarray:
+    """Row-major bf16 [R, K] -> fragment-tiled (flat, same element count)."""
+    w = _c(w, np.uint16)
+    R, K = w.shape
+    out = np.empty(R * K, np.uint16)
+    _load().oracle_tile_bf16(_p(w), R, K, _p(out))
+    return out
+
+
+def untile_bf16(t: np.ndarray, R: int, K: int) -> np.ndarray:
+    """Fragment-tiled bf16 (any shape, R*K elements) -> row-major [R, K]."""
+    t = _c(t, np.uint16).reshape(-1)
+    assert t.size == R * K
+    out = np.empty((R, K), np.uint16)
+    _load().oracle_untile_bf16(_p(t), R, K, _p(out))
+    return out
+
+
+def int4_tiled_sizes(R: int, K: int):
+    """(code bytes, scale count) of the tiled int4 format."""
+    L = _load()
+    return int(L.oracle_int4_tiled_code_bytes(R, K)), int(L.oracle_int4_tiled_scale_count(R, K))
+
+
+def tile_int4(q: np.ndarray, s: np.ndarray):
+    """Row-major (q [R, K/2], s [R, K/32]) -> tiled (codes, scales), flat."""
+    q, s = _c(q, np.uint8), _c(s, np.uint16)
+    R, K = q.shape[0], q.shape[1] * 2
+    nb, ns = int4_tiled_sizes(R, K)
+    qt, st = np.empty(nb, np.uint8), np.empty(ns, np.uint16)
+    _load().oracle_tile_int4(_p(q), _p(s), R, K, _p(qt), _p(st))
+    return qt, st
+
+
+def untile_int4(qt: np.ndarray, st: np.ndarray, R: int, K: int):
+    """Tiled int4 (flat codes, flat scales) -> row-major (q [R, K/2], s [R, K/32])."""
+    qt, st = _c(qt, np.uint8).reshape(-1), _c(st, np.uint16).reshape(-1)
+    q = np.empty((R, K // 2), np.uint8)
+    s = np.empty((R, K // 32), np.uint16)
+    _load().oracle_untile_int4(_p(qt), _p(st), R, K, _p(q), _p(s))
+    return q, s

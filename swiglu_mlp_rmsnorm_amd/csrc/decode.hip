@@ -1,271 +1,457 @@
-// Decode path (M <= 32 tokens): two weight-streaming kernels.
+// Decode path (M <= 32 tokens): two kernels per forward (three for int4).
 //
-//   1. gate/up: z = W_gu v (v = gamma * x, unnormalised), the RMS scale r of
-//      each token folded in afterwards (z * r = W_gu (gamma * x * r)), then
-//      a = SiLU(z_gate) * z_up on the interleaved row pairs, in registers
-//      (FastTPS review section 3: RMSNorm -> interleaved gate-up matmul ->
-//      SiLU*mul; llama.cpp PR digest: GLU applied in the same matmul pass).
-//   2. down: y = W_down a.
+//   0. (int4 only) act prep: r = 1/sqrt(mean(x^2) + eps) per token and the
+//      normalised input n = gamma * x * r as fp16 in the int4 operand order
+//      (FastTPS review, section 3, Figure 4 part1). On the bf16 path the
+//      RMSNorm is folded into step 1 instead.
+//   1. gate/up: z = W_gu n over the interleaved rows, then a = SiLU(z_gate) *
+//      z_up on each (2i, 2i+1) pair in registers (Figure 4 part2; llama.cpp
+//      PR digest: the GLU is applied in the same pass as the gate/up matmul).
+//      Only a (M x ff) leaves the kernel.
+//   2. down: y = W_down a (Figure 4 part3).
 //
-// Both are bound by HBM reads of the weights (decode arithmetic intensity is
-// ~M flop/byte, far under the bf16 ridge of ~315 flop/byte), so the design
-// goal is to keep enough 16-byte loads in flight and spend little VALU time.
-// The dot products run on MFMA 16x16x32 bf16: weights are the A operand
-// (16 rows per block, loaded straight from HBM into registers in the MFMA
-// lane layout), tokens are the B operand (16 columns, zero-padded above M).
-// The B operand carries the activation as an exact bf16 hi + lo split, so the
-// contraction has fp32-equivalent precision in the activation (the product
-// of two bf16 values has 16 significant bits, which hi + lo hold exactly).
-// K is split across the waves of a workgroup and reduced through LDS in a
-// fixed order: results are deterministic.
+// Steps 1 and 2 are bound by HBM reads of the weights (decode arithmetic
+// intensity is about M flop/byte against a bf16 ridge of ~315 flop/byte), so
+// they are built to stream: weights arrive in the fragment-tiled layout, one
+// contiguous 1 KB tile per 16-row x 32-column block, read by one 16-byte load
+// per lane straight into the MFMA operand layout; each wave keeps a P-deep
+// register ring of upcoming tiles in flight; the S waves of a workgroup split
+// K and reduce through LDS in a fixed order (deterministic results).
+//
+// Dot products run on MFMA 16x16x32 with A = activations (16 token rows, zero
+// above M) and B = weights (16 weight rows), so lane l accumulates weight row
+// l%16 for tokens 4*(l/16) .. +3.
+//
+// bf16 weights: the activation is an exact-to-2^-17 bf16 hi + lo pair (two
+// bf16 MFMAs per tile), so the normalised input and the SiLU*mul
+// intermediate keep fp32-like precision (rounding either to bf16 alone
+// breaks the accuracy bar at the larger shapes).
+//
+// int4 weights: one fp16 MFMA per group. A word holds the 8 codes a lane
+// needs; with u = word ^ 0x88888888 each nibble is q+8, and
+//   (u & 0x000F000F) | 0x64006400 -> fp16 (1032 + q0, 1032 + q4)
+//   (u & 0x00F000F0) | 0x64006400 -> fp16 (1152 + 16 q1, 1152 + 16 q5)
+// (and the same on u >> 8 for codes 2,6 / 3,7): six VALU operations per 8
+// weights, all exact. The activation slots facing the x16 codes carry n/16,
+// and a second MFMA of the activations against the constant offsets
+// (-1032 / -1152) seeds the accumulator, so the pair of MFMAs returns
+// sum_k q_k n_k for the group exactly up to fp32 rounding; the lane then
+// scales it by its row's fp16 group scale. Activation and intermediate are
+// fp16 on this path (inside the accuracy bar).
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "profile.hpp"
 
+// Tuning (compile-time; defaults chosen by measurement on MI355X).
+#ifndef FMLP_GU_RB
+#define FMLP_GU_RB 2  // 16-row blocks per gate/up workgroup
+#endif
+#ifndef FMLP_GU_S
+#define FMLP_GU_S 8   // waves per gate/up workgroup (split K)
+#endif
+#ifndef FMLP_GU_P
+#define FMLP_GU_P 2   // ring depth (tiles in flight per wave and row block)
+#endif
+#ifndef FMLP_DN_S
+#define FMLP_DN_S 16
+#endif
+#ifndef FMLP_DN_P
+#define FMLP_DN_P 1
+#endif
+#ifndef FMLP_Q4_P
+#define FMLP_Q4_P 1   // int4 ring depth (super-tiles of 4 groups)
+#endif
+
 namespace fmlp {
+
+enum { WK_BF16 = 0, WK_INT4 = 1 };
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
-  (void)d;
-  // a_hi, a_lo: bf16 [M, ff] each
-  return 2 * align256((size_t)M * (size_t)ff * 2);
+  // n fp16 [M, d] (int4 only); a: bf16 hi + lo [M, ff] (int4: fp16 in the first half)
+  return align256((size_t)M * d * 2) + 2 * align256((size_t)M * ff * 2);
 }
 
-// ---------------------------------------------------------------------------
-// gate/up + RMSNorm + SiLU*mul.
-// Workgroup: S waves, RB row blocks of 16 W_gu rows (RB*8 gate/up pairs).
-// Wave w handles K32 blocks w, w+S, w+2S, ... of all RB row blocks, so the S
-// waves of a workgroup together read contiguous spans of each row.
-// Output: a = a_hi + a_lo (bf16 pair, fp32-equivalent), [M, ff].
-template <int NCB, int RB, int S>
-__global__ __launch_bounds__(64 * S) void k_decode_gateup_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
-    const uint16_t* __restrict__ wgu, uint16_t* __restrict__ a_hi, uint16_t* __restrict__ a_lo,
-    int M, int d, int ff) {
-  __shared__ f32x4 red[S * RB * NCB * 64];
-  __shared__ float ssred[S * NCB * 16];
+struct DecodeWs {
+  uint16_t *n0, *a0, *a1;
+};
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * (RB * 16);
-  const int nkb = d >> 5;
+static DecodeWs decode_ws(const Problem& p) {
+  const size_t nb = align256((size_t)p.M * p.d * 2), ab = align256((size_t)p.M * p.ff * 2);
+  char* b = p.ws;
+  return DecodeWs{reinterpret_cast<uint16_t*>(b), reinterpret_cast<uint16_t*>(b + nb),
+                  reinterpret_cast<uint16_t*>(b + nb + ab)};
+}
 
-  const uint16_t* wrow[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) wrow[rb] = wgu + (row0 + rb * 16 + col) * (int64_t)d + grp * 8;
-  const uint16_t* xrow[NCB];
-  bool tok[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int t = cb * 16 + col;
-    tok[cb] = t < M;
-    xrow[cb] = x + (int64_t)(tok[cb] ? t : 0) * d + grp * 8;
-  }
-  const uint16_t* grow = gamma + grp * 8;
+// ------------------------------------------------------------ int4 helpers
 
-  f32x4 acc[RB][NCB];
-  float ss[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    ss[cb] = 0.0f;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+// 8 codes -> fp16 operand words (see the file comment for the slot order).
+__device__ __forceinline__ u32x4 int4_to_f16_magic(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u, u8 = u >> 8;
+  u32x4 r;
+  r[0] = (u & 0x000F000Fu) | 0x64006400u;
+  r[1] = (u & 0x00F000F0u) | 0x64006400u;
+  r[2] = (u8 & 0x000F000Fu) | 0x64006400u;
+  r[3] = (u8 & 0x00F000F0u) | 0x64006400u;
+  return r;
+}
 
-  int kb = wave;
-  u32x4 wn[RB];
-  if (kb < nkb) {
+// Negated magic offsets per slot: -1032 for slots of codes 0,4,2,6 and -1152
+// for slots of codes 1,5,3,7 (fp16 0xE408 / 0xE480).
+constexpr uint32_t kNegOffA = 0xE408E408u, kNegOffB = 0xE480E480u;
+
+// Position of logical element m (0..7) of an 8-block in the int4 operand
+// order, and whether that slot carries the value divided by 16.
+__device__ __forceinline__ int q4_slot(int m) { return (m & 1) ? 2 + ((m >> 1) & 1) * 4 + (m >> 2) : (m >> 1 & 1) * 4 + (m >> 2); }
+
+// ------------------------------------------------------------ act prep (int4)
+// One 256-thread workgroup per token: r = 1/sqrt(mean(x^2) + eps), then
+// n = x * gamma * r stored as fp16 [M, d] in the int4 slot order, the slots
+// of odd elements carrying n/16.
+__global__ __launch_bounds__(256) void k_act_prep_q4(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ gamma,
+                                                     float eps, uint16_t* __restrict__ n0, int d) {
+  __shared__ float part[4];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * d;
+  const int chunks = d >> 3;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const u32x4 v = ld16(xr + c * 8);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) wn[rb] = ld16_stream(wrow[rb] + kb * 32);
-  }
-  for (; kb < nkb; kb += S) {
-    u32x4 w[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) w[rb] = wn[rb];
-    if (kb + S < nkb) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) wn[rb] = ld16_stream(wrow[rb] + (kb + S) * 32);
-    }
-    const int k = kb * 32;
-    const u32x4 gv = ld16(grow + k);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      u32x4 xv = {0u, 0u, 0u, 0u};
-      if (tok[cb]) xv = ld16(xrow[cb] + k);
-      u32x4 hi, lo;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = bf16_lo(xv[j]), x1 = bf16_hi(xv[j]);
-        ss[cb] = fmaf(x0, x0, ss[cb]);
-        ss[cb] = fmaf(x1, x1, ss[cb]);
-        uint32_t h, l;
-        split_bf16_pair(x0 * bf16_lo(gv[j]), x1 * bf16_hi(gv[j]), h, l);
-        hi[j] = h;
-        lo[j] = l;
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][cb] = mfma_bf16(w[rb], hi, acc[rb][cb]);
-        acc[rb][cb] = mfma_bf16(w[rb], lo, acc[rb][cb]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_lo(v[j]), b = bf16_hi(v[j]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
     }
   }
-
-  // sum of squares: lanes col, col+16, col+32, col+48 hold the same token
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    ss[cb] += __shfl_xor(ss[cb], 16);
-    ss[cb] += __shfl_xor(ss[cb], 32);
-    if (grp == 0) ssred[(wave * NCB + cb) * 16 + col] = ss[cb];
-  }
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) red[((wave * RB + rb) * NCB + cb) * 64 + lane] = acc[rb][cb];
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
-
-  // epilogue: one thread per (pair, token); pairs fastest for coalesced stores
-  constexpr int kPairs = RB * 8;
-  const float inv_d = 1.0f / (float)d;
-  for (int o = threadIdx.x; o < kPairs * NCB * 16; o += 64 * S) {
-    const int p = o % kPairs, t = o / kPairs;
-    if (t >= M) continue;
-    const int cb = t >> 4, c = t & 15;
-    const int rb = p >> 3, lr = (p & 7) * 2;  // gate row within the block
-    const int L = (lr >> 2) * 16 + c, e = lr & 3;
-    float g = 0.f, u = 0.f, sst = 0.f;
+  const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+  for (int c = threadIdx.x; c < chunks; c += 256) {
+    const u32x4 v = ld16(xr + c * 8), g = ld16(gamma + c * 8);
+    float n[8];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const f32x4 v = red[((s * RB + rb) * NCB + cb) * 64 + L];
-      g += v[e];
-      u += v[e + 1];
-      sst += ssred[(s * NCB + cb) * 16 + c];
+    for (int j = 0; j < 4; ++j) {
+      n[2 * j] = bf16_lo(v[j]) * bf16_lo(g[j]) * r;
+      n[2 * j + 1] = bf16_hi(v[j]) * bf16_hi(g[j]) * r;
     }
-    const float r = 1.0f / sqrtf(sst * inv_d + eps);
-    const float av = silu_mul(g * r, u * r);
-    const uint16_t h = bf16_rne(av);
-    const int64_t idx = (int64_t)t * ff + row0 / 2 + p;
-    a_hi[idx] = h;
-    a_lo[idx] = bf16_rne(av - __uint_as_float((uint32_t)h << 16));
+    _Float16 h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[q4_slot(e)] = (_Float16)((e & 1) ? n[e] * 0.0625f : n[e]);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * j]) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * j + 1]) << 16);
+    st16(n0 + m * d + c * 8, o);
   }
 }
 
-// ---------------------------------------------------------------------------
-// down projection: y[t, j] = sum_i W_down[j, i] a[t, i], a = a_hi + a_lo.
-template <int NCB, int RB, int S>
-__global__ __launch_bounds__(64 * S) void k_decode_down_bf16(
-    const uint16_t* __restrict__ a_hi, const uint16_t* __restrict__ a_lo,
-    const uint16_t* __restrict__ wd, uint16_t* __restrict__ y, int M, int d, int ff) {
-  __shared__ f32x4 red[S * RB * NCB * 64];
+// ------------------------------------------------------------ GEMV core
+// acc[rb][cb] += W[row block rb0+rb] . act for the K range owned by this wave.
+// Activation operand modes:
+//   ACT_X   : bf16 weights; act = gamma * x (unnormalised, exact in fp32),
+//             split hi/lo here from act0 = x [M, K] and act1 = gamma [K];
+//             also accumulates sum x^2 per token into ss (RMS folded later)
+//   ACT_HL  : bf16 weights; act0 / act1 = hi / lo bf16 [M, K], natural order
+//   ACT_Q4  : int4 weights; act0 = fp16 [M, K] in the int4 slot order
+// Weights: bf16 tiles (1 KB per 16 x 32 block) or int4 super-tiles (1 KB per
+// 16 rows x 4 groups) + scales. Each wave walks K units wave, wave+S, ...
+// with a P-deep ring of weight tiles and activation chunks in flight.
+enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2 };
 
+template <int MODE, int NCB, int RB, int S, int P>
+__device__ __forceinline__ void gemv_core(const void* __restrict__ w,
+                                          const uint16_t* __restrict__ sc,
+                                          const uint16_t* __restrict__ act0,
+                                          const uint16_t* __restrict__ act1, int64_t rb0, int K,
+                                          int M, f32x4 (&acc)[RB][NCB], float (&ss)[NCB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * (RB * 16);
-  const int nkb = ff >> 5;
-
-  const uint16_t* wrow[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) wrow[rb] = wd + (row0 + rb * 16 + col) * (int64_t)ff + grp * 8;
-  const uint16_t* ahr[NCB];
-  const uint16_t* alr[NCB];
+  const int jmax = M >= 4 ? 4 : M;
+  const int nkb = K >> 5;
+  int64_t aoff[NCB];
   bool tok[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int t = cb * 16 + col;
     tok[cb] = t < M;
-    const int64_t off = (int64_t)(tok[cb] ? t : 0) * ff + grp * 8;
-    ahr[cb] = a_hi + off;
-    alr[cb] = a_lo + off;
+    aoff[cb] = (int64_t)(tok[cb] ? t : 0) * K + grp * 8;
+    ss[cb] = 0.f;
   }
-
-  f32x4 acc[RB][NCB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int kb = wave;
-  u32x4 wn[RB];
-  if (kb < nkb) {
+  if constexpr (MODE != ACT_Q4) {
+    // unit = one 32-column group
+    const uint16_t* wt = static_cast<const uint16_t*>(w) + lane * 8;
+    const int nit = wave < nkb ? (nkb - wave + S - 1) / S : 0;
+    u32x4 wb[P][RB], hb[P][NCB], lb[P][NCB];
+    u32x4 gb[P];
+    auto issue = [&](int slot, int it) {
+      const int kb = wave + it * S;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) wn[rb] = ld16_stream(wrow[rb] + kb * 32);
-  }
-  for (; kb < nkb; kb += S) {
-    u32x4 w[RB];
+      for (int rb = 0; rb < RB; ++rb) wb[slot][rb] = ld16_stream(wt + ((rb0 + rb) * nkb + kb) * 512);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) w[rb] = wn[rb];
-    if (kb + S < nkb) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) wn[rb] = ld16_stream(wrow[rb] + (kb + S) * 32);
-    }
-    const int k = kb * 32;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (tok[cb]) {
-        hi = ld16(ahr[cb] + k);
-        lo = ld16(alr[cb] + k);
+      for (int cb = 0; cb < NCB; ++cb) {
+        hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
+        if (MODE == ACT_HL) lb[slot][cb] = ld16(act1 + aoff[cb] + kb * 32);
       }
+      if (MODE == ACT_X) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < nit) issue(p, p);
+    for (int i0 = 0; i0 < nit; i0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int it = i0 + p;
+        if (it < nit) {
+          u32x4 wv[RB], h[NCB], l[NCB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) wv[rb] = wb[p][rb];
+          const u32x4 gv = gb[p];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            h[cb] = tok[cb] ? hb[p][cb] : u32x4{0u, 0u, 0u, 0u};
+            l[cb] = tok[cb] ? lb[p][cb] : u32x4{0u, 0u, 0u, 0u};
+          }
+          if (it + P < nit) issue(p, it + P);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            if (MODE == ACT_X) {
+              // h holds x; build the hi/lo pair of gamma * x in place
+              const u32x4 xv = h[cb];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float x0 = bf16_lo(xv[j]), x1 = bf16_hi(xv[j]);
+                ss[cb] = fmaf(x0, x0, ss[cb]);
+                ss[cb] = fmaf(x1, x1, ss[cb]);
+                uint32_t hh, ll;
+                split_bf16_pair(x0 * bf16_lo(gv[j]), x1 * bf16_hi(gv[j]), hh, ll);
+                h[cb][j] = hh;
+                l[cb][j] = ll;
+              }
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+              acc[rb][cb] = mfma_bf16(h[cb], wv[rb], acc[rb][cb]);
+              acc[rb][cb] = mfma_bf16(l[cb], wv[rb], acc[rb][cb]);
+            }
+          }
+        }
+      }
+    }
+  } else {
+    // unit = one super-tile of 4 groups
+    const int nq = (K + 127) >> 7;
+    const uint8_t* qt = static_cast<const uint8_t*>(w) + lane * 16;
+    const uint16_t* stl = sc + col * 4;
+    const int nit = wave < nq ? (nq - wave + S - 1) / S : 0;
+    const u32x4 negoff = {kNegOffA, kNegOffB, kNegOffA, kNegOffB};
+    u32x4 qb[P][RB], ab[P][4][NCB];
+    uint64_t sb[P][RB];
+    auto issue = [&](int slot, int it) {
+      const int q = wave + it * S;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        acc[rb][cb] = mfma_bf16(w[rb], hi, acc[rb][cb]);
-        acc[rb][cb] = mfma_bf16(w[rb], lo, acc[rb][cb]);
+        const int64_t st = (rb0 + rb) * nq + q;
+        qb[slot][rb] = ld16_stream(qt + st * 1024);
+        sb[slot][rb] = *reinterpret_cast<const uint64_t*>(stl + st * 64);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = q * 4 + j < nkb ? q * 4 + j : nkb - 1;  // padding groups are skipped
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) ab[slot][j][cb] = ld16(act0 + aoff[cb] + kb * 32);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      if (p < nit) issue(p, p);
+    for (int i0 = 0; i0 < nit; i0 += P) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int it = i0 + p;
+        if (it < nit) {
+          const int q = wave + it * S;
+          u32x4 qv[RB], av[4][NCB];
+          uint64_t sv[RB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            qv[rb] = qb[p][rb];
+            sv[rb] = sb[p][rb];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+              av[j][cb] = tok[cb] ? ab[p][j][cb] : u32x4{0u, 0u, 0u, 0u};
+          if (it + P < nit) issue(p, it + P);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (q * 4 + j >= nkb) break;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              const f32x4 c = mfma_f16(av[j][cb], negoff, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) {
+                const f32x4 dq = mfma_f16(av[j][cb], int4_to_f16_magic(qv[rb][j]), c);
+                const float s = (float)__builtin_bit_cast(
+                    _Float16, (uint16_t)(sv[rb] >> (16 * j)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (e < jmax) acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
+              }
+            }
+          }
+        }
       }
     }
   }
+}
 
+// Cross-wave reduction of the accumulators through LDS (fixed wave order).
+// Afterwards red[((w*RB + rb)*NCB + cb)*64 + lane] holds wave w's values.
+template <int RB, int NCB>
+__device__ __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RB][NCB]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) red[((wave * RB + rb) * NCB + cb) * 64 + lane] = acc[rb][cb];
-  __syncthreads();
+}
 
-  constexpr int kRows = RB * 16;
-  for (int o = threadIdx.x; o < kRows * NCB * 16; o += 64 * S) {
-    const int rl = o % kRows, t = o / kRows;
-    if (t >= M) continue;
-    const int cb = t >> 4, c = t & 15;
-    const int rb = rl >> 4, lr = rl & 15;
-    const int L = (lr >> 2) * 16 + c, e = lr & 3;
-    float sum = 0.f;
+// ------------------------------------------------------------ gate/up kernel
+// Workgroup: RB blocks of 16 W_gu rows (RB*8 gate/up pairs), S waves split K.
+// bf16: activations come straight from x and gamma (ACT_X); each wave also
+// sums x^2 over its K units, the sums are reduced with the dot products and
+// r = 1/sqrt(mean(x^2) + eps) scales z before SiLU*mul (z * r = W (gamma x r)).
+// Writes a = a0 + a1 (bf16 hi/lo, natural order, [M, ff]).
+// int4: activations are the prepared fp16 n (ACT_Q4); writes a0 = fp16 a in
+// the int4 slot order, [M, ff].
+template <int WK, int NCB, int RB, int S, int P>
+__global__ __launch_bounds__(64 * S) void k_decode_gateup(
+    const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ act0,
+    const uint16_t* __restrict__ act1, float eps, uint16_t* __restrict__ a0,
+    uint16_t* __restrict__ a1, int M, int d, int ff) {
+  __shared__ f32x4 red[S * RB * NCB * 64];
+  __shared__ float ssred[S * NCB * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rb0 = (int64_t)blockIdx.x * RB;
+  f32x4 acc[RB][NCB];
+  float ss[NCB];
+  gemv_core<WK == WK_BF16 ? ACT_X : ACT_Q4, NCB, RB, S, P>(w, sc, act0, act1, rb0, d, M, acc, ss);
+  stash<RB, NCB>(red, acc);
+  if (WK == WK_BF16) {
+    // lanes col, col+16, col+32, col+48 hold the same token
 #pragma unroll
-    for (int s = 0; s < S; ++s) sum += red[((s * RB + rb) * NCB + cb) * 64 + L][e];
-    y[(int64_t)t * d + row0 + rl] = bf16_rne(sum);
+    for (int cb = 0; cb < NCB; ++cb) {
+      float v = ss[cb];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) ssred[(wave * NCB + cb) * 16 + lane] = v;
+    }
+  }
+  __syncthreads();
+  // one thread per (pair, token), pairs fastest
+  constexpr int kPairs = RB * 8;
+  const float inv_d = 1.0f / (float)d;
+  for (int o = threadIdx.x; o < kPairs * M; o += 64 * S) {
+    const int p = o % kPairs, t = o / kPairs;
+    const int cb = t >> 4, c = t & 15;
+    const int rb = p >> 3, lr = (p & 7) * 2;
+    const int L = (c >> 2) * 16 + lr, e = c & 3;
+    float g = 0.f, u = 0.f, sst = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int base = ((s * RB + rb) * NCB + cb) * 64 + L;
+      g += red[base][e];
+      u += red[base + 1][e];
+      if (WK == WK_BF16) sst += ssred[(s * NCB + cb) * 16 + c];
+    }
+    const int i = (int)(rb0 * 8) + p;  // index along ff
+    if (WK == WK_BF16) {
+      const float r = 1.0f / sqrtf(sst * inv_d + eps);
+      const float av = silu_mul(g * r, u * r);
+      const uint16_t h = bf16_rne(av);
+      a0[(int64_t)t * ff + i] = h;
+      a1[(int64_t)t * ff + i] = bf16_rne(av - __uint_as_float((uint32_t)h << 16));
+    } else {
+      const float av = silu_mul(g, u);
+      const int mm = i & 7;
+      const _Float16 hv = (_Float16)((mm & 1) ? av * 0.0625f : av);
+      a0[(int64_t)t * ff + (i & ~7) + q4_slot(mm)] = __builtin_bit_cast(uint16_t, hv);
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-
-template <int NCB>
-static hipError_t launch_decode_bf16_t(const Problem& p, hipStream_t stream) {
-  uint16_t* a_hi = reinterpret_cast<uint16_t*>(p.ws);
-  uint16_t* a_lo = reinterpret_cast<uint16_t*>(p.ws + align256((size_t)p.M * p.ff * 2));
-  constexpr int RB_GU = (NCB == 1) ? 4 : 2, S_GU = 8;
-  constexpr int RB_D = 1, S_D = 16;
-  const int gu_blocks = (2 * p.ff) / (16 * RB_GU);
-  {
-    ProfileScope prof(KK_DECODE_GATEUP_BF16, stream);
-    hipLaunchKernelGGL((k_decode_gateup_bf16<NCB, RB_GU, S_GU>), dim3(gu_blocks), dim3(64 * S_GU),
-                       0, stream, p.x, p.gamma, p.eps, reinterpret_cast<const uint16_t*>(p.w_gu),
-                       a_hi, a_lo, p.M, p.d, p.ff);
+// ------------------------------------------------------------ down kernel
+// Workgroup: one block of 16 W_down rows, S waves split K = ff.
+template <int WK, int NCB, int S, int P>
+__global__ __launch_bounds__(64 * S) void k_decode_down(
+    const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ a0,
+    const uint16_t* __restrict__ a1, uint16_t* __restrict__ y, int M, int d, int ff) {
+  __shared__ f32x4 red[S * NCB * 64];
+  const int64_t rb0 = blockIdx.x;
+  f32x4 acc[1][NCB];
+  float ss[NCB];
+  gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, 1, S, P>(w, sc, a0, a1, rb0, ff, M, acc, ss);
+  stash<1, NCB>(red, acc);
+  __syncthreads();
+  for (int o = threadIdx.x; o < 16 * M; o += 64 * S) {
+    const int rl = o & 15, t = o >> 4;
+    const int cb = t >> 4, c = t & 15;
+    const int L = (c >> 2) * 16 + rl, e = c & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) sum += red[(s * NCB + cb) * 64 + L][e];
+    y[(int64_t)t * d + rb0 * 16 + rl] = bf16_rne(sum);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int d_blocks = p.d / (16 * RB_D);
-  ProfileScope prof(KK_DECODE_DOWN_BF16, stream);
-  hipLaunchKernelGGL((k_decode_down_bf16<NCB, RB_D, S_D>), dim3(d_blocks), dim3(64 * S_D), 0,
-                     stream, a_hi, a_lo, reinterpret_cast<const uint16_t*>(p.w_down), p.y, p.M,
-                     p.d, p.ff);
+}
+
+// ------------------------------------------------------------ launch
+
+template <int WK, int NCB>
+static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
+  const DecodeWs ws = decode_ws(p);
+  constexpr int RB = (NCB == 1) ? FMLP_GU_RB : (FMLP_GU_RB > 2 ? 2 : FMLP_GU_RB);
+  constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
+  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
+  hipError_t e;
+  if constexpr (WK == WK_INT4) {
+    ProfileScope prof(KK_ACT_PREP, stream);
+    hipLaunchKernelGGL(k_act_prep_q4, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps, ws.n0,
+                       p.d);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
+  const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
+  const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
+  {
+    ProfileScope prof(WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16, stream);
+    hipLaunchKernelGGL((k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP>),
+                       dim3((2 * p.ff) / (16 * RB)), dim3(64 * FMLP_GU_S), 0, stream, p.w_gu,
+                       p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M, p.d, p.ff);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  ProfileScope prof(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16, stream);
+  hipLaunchKernelGGL((k_decode_down<WK, NCB, FMLP_DN_S, DP>), dim3(p.d / 16), dim3(64 * FMLP_DN_S),
+                     0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_int4(const Problem& p, hipStream_t stream);
-
 hipError_t launch_decode(const Problem& p, hipStream_t stream) {
-  if (p.wtype == 1) return launch_decode_int4(p, stream);
-  if (p.M <= 16) return launch_decode_bf16_t<1>(p, stream);
-  return launch_decode_bf16_t<2>(p, stream);
+  if (p.wtype == 1)
+    return p.M <= 16 ? launch_decode_t<WK_INT4, 1>(p, stream)
+                     : launch_decode_t<WK_INT4, 2>(p, stream);
+  return p.M <= 16 ? launch_decode_t<WK_BF16, 1>(p, stream) : launch_decode_t<WK_BF16, 2>(p, stream);
 }
 
 }  // namespace fmlp

@@ -36,6 +36,11 @@ bool shape_ok(int64_t d, int64_t ff) {
   return d > 0 && ff > 0 && d % 32 == 0 && ff % 32 == 0 && d <= kMaxD && ff <= kMaxFF;
 }
 
+// a logical [rows, K] weight matrix in the tiled formats
+bool matrix_ok(int64_t rows, int64_t K) {
+  return rows > 0 && K > 0 && rows % 16 == 0 && K % 32 == 0 && rows <= 2 * kMaxFF && K <= kMaxFF;
+}
+
 // Device check, cached once per device (querying properties on every launch
 // costs host time in a decode loop; the V100 report in the llama.cpp digest
 // measured exactly that).
@@ -97,14 +102,35 @@ int fmlp_pack_interleaved(const void* w_gate, const void* w_up, void* w_gu, int6
   return e == hipSuccess ? FMLP_OK : hip_fail(e);
 }
 
+int fmlp_pack_matrix(const void* w, void* w_tiled, int64_t rows, int64_t K, void* stream) {
+  if (!w || !w_tiled) return FMLP_ERR_INVALID_ARG;
+  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(w) || !aligned16(w_tiled)) return FMLP_ERR_ALIGNMENT;
+  if (overlap(span(w, (size_t)rows * K * 2), span(w_tiled, (size_t)rows * K * 2)))
+    return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  hipError_t e = fmlp::launch_tile_matrix(static_cast<const uint16_t*>(w),
+                                          static_cast<uint16_t*>(w_tiled), rows, K,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+int fmlp_int4_sizes(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_bytes) {
+  if (!code_bytes || !scale_bytes) return FMLP_ERR_INVALID_ARG;
+  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  *code_bytes = (size_t)fmlp::int4_code_bytes(rows, K);
+  *scale_bytes = (size_t)fmlp::int4_scale_bytes(rows, K);
+  return FMLP_OK;
+}
+
 int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* scales,
                        void* stream) {
   if (!w || !q || !scales) return FMLP_ERR_INVALID_ARG;
-  if (rows <= 0 || K <= 0 || K % 32 != 0 || K > kMaxFF || rows > kMaxFF * 2)
-    return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FMLP_ERR_ALIGNMENT;
-  const Span sw = span(w, (size_t)rows * K * 2), sq = span(q, (size_t)rows * K / 2),
-             ss = span(scales, (size_t)rows * (K / 32) * 2);
+  const Span sw = span(w, (size_t)rows * K * 2),
+             sq = span(q, (size_t)fmlp::int4_code_bytes(rows, K)),
+             ss = span(scales, (size_t)fmlp::int4_scale_bytes(rows, K));
   if (overlap(sw, sq) || overlap(sw, ss) || overlap(sq, ss)) return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;
   std::lock_guard<std::mutex> lock(g_quant_mutex);
@@ -119,12 +145,11 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* sc
 int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K, float* out,
                       void* stream) {
   if (!q || !scales || !out) return FMLP_ERR_INVALID_ARG;
-  if (rows <= 0 || K <= 0 || K % 32 != 0 || K > kMaxFF || rows > kMaxFF * 2)
-    return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(q) || !aligned16(scales) || !aligned16(out)) return FMLP_ERR_ALIGNMENT;
   const Span so = span(out, (size_t)rows * K * 4);
-  if (overlap(so, span(q, (size_t)rows * K / 2)) ||
-      overlap(so, span(scales, (size_t)rows * (K / 32) * 2)))
+  if (overlap(so, span(q, (size_t)fmlp::int4_code_bytes(rows, K))) ||
+      overlap(so, span(scales, (size_t)fmlp::int4_scale_bytes(rows, K))))
     return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;
   hipError_t e = fmlp::launch_dequant(static_cast<const uint8_t*>(q),
@@ -173,15 +198,15 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
   const uintptr_t abase = (wbase + 255) & ~uintptr_t(255);
   if (workspace_bytes < need + (abase - wbase)) return FMLP_ERR_WORKSPACE;
 
-  const size_t wgu_b = int4 ? (size_t)2 * ff * d / 2 : (size_t)2 * ff * d * 2;
-  const size_t wd_b = int4 ? (size_t)d * ff / 2 : (size_t)d * ff * 2;
+  const size_t wgu_b = int4 ? (size_t)fmlp::int4_code_bytes(2 * ff, d) : (size_t)2 * ff * d * 2;
+  const size_t wd_b = int4 ? (size_t)fmlp::int4_code_bytes(d, ff) : (size_t)d * ff * 2;
   const Span sy = span(y, (size_t)M * d * 2);
   if (overlap(sy, span(x, (size_t)M * d * 2)) || overlap(sy, span(gamma, (size_t)d * 2)) ||
       overlap(sy, span(w_gu, wgu_b)) || overlap(sy, span(w_down, wd_b)) ||
       overlap(sy, span(workspace, workspace_bytes)))
     return FMLP_ERR_INVALID_ARG;
-  if (int4 && (overlap(sy, span(gu_scales, (size_t)2 * ff * (d / 32) * 2)) ||
-               overlap(sy, span(down_scales, (size_t)d * (ff / 32) * 2))))
+  if (int4 && (overlap(sy, span(gu_scales, (size_t)fmlp::int4_scale_bytes(2 * ff, d))) ||
+               overlap(sy, span(down_scales, (size_t)fmlp::int4_scale_bytes(d, ff)))))
     return FMLP_ERR_INVALID_ARG;
   const Span sw = span(workspace, workspace_bytes);
   if (overlap(sw, span(x, (size_t)M * d * 2)) || overlap(sw, span(gamma, (size_t)d * 2)) ||

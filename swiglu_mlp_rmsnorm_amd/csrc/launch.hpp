@@ -14,10 +14,10 @@ struct Problem {
   const uint16_t* gamma;   // bf16 [d]
   float eps;
   int wtype;               // 0 bf16, 1 int4 group-32
-  const void* w_gu;        // bf16 [2ff, d] | uint8 [2ff, d/2]
-  const uint16_t* s_gu;    // fp16 [2ff, d/32] (int4)
-  const void* w_down;      // bf16 [d, ff]  | uint8 [d, ff/2]
-  const uint16_t* s_down;  // fp16 [d, ff/32] (int4)
+  const void* w_gu;        // tiled bf16 [2ff, d] | tiled int4 codes
+  const uint16_t* s_gu;    // tiled fp16 scales (int4)
+  const void* w_down;      // tiled bf16 [d, ff] | tiled int4 codes
+  const uint16_t* s_down;  // tiled fp16 scales (int4)
   uint16_t* y;             // bf16 [M, d]
   int M, d, ff;
   char* ws;                // workspace base (256-byte aligned)
@@ -26,12 +26,18 @@ struct Problem {
 
 constexpr int kDecodeMaxM = 32;
 
+// Sizes of the tiled int4 format for a logical [R, K] matrix.
+inline int64_t int4_code_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 127) / 128) * 1024; }
+inline int64_t int4_scale_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 127) / 128) * 128; }
+
 // Workspace layout, shared by the sizing query and the launchers.
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff);
 size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff);
 
 hipError_t launch_pack(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* w_gu, int64_t ff,
                        int64_t d, hipStream_t stream);
+hipError_t launch_tile_matrix(const uint16_t* w, uint16_t* out, int64_t R, int64_t K,
+                              hipStream_t stream);
 hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q,
                            uint16_t* scales, hipStream_t stream, int* range_error);
 hipError_t launch_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t K,

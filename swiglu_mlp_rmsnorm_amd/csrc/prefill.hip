@@ -68,33 +68,33 @@ __global__ __launch_bounds__(256) void k_rms_prep_f16(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- GEMM
-// C[f, t] = sum_k W[f, k] * Act[t, k], W bf16 [N, K] (converted to fp16 on
-// the way into LDS), Act fp16 [M, K].
+// C[f, t] = sum_k W[f, k] * Act[t, k]; W in the fragment-tiled bf16 layout
+// (converted to fp16 on its way into LDS), Act fp16 [M, K] row-major.
 // Tile: BN = 128 features x BM = 128 tokens x BK = 64, 256 threads = 4 waves
 // in a 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA 16x16x32 blocks.
-// Global loads for tile k+1 are issued before the MFMAs of tile k
-// (register double buffering); LDS rows are padded to 144 bytes so the
-// 16 rows read by one ds_read_b128 quarter-wave fall in distinct banks.
-// Tiles are assigned XCD-major: the 8 XCDs each take a contiguous range of
-// tile indices, token tiles fastest, so the workgroups sharing a weight tile
-// run on the same XCD and share its L2.
-constexpr int kBN = 128, kBM = 128, kBK = 64, kLdsStride = kBK + 8;  // fp16 elements
+// LDS holds both operands in fragment order (1 KB per 16 x 32 block, slot L
+// at byte 16 L), so every MFMA operand read is one contiguous ds_read_b128
+// per wave; weight tiles are copied as they are, activation chunks are
+// scattered to their slots on the way in.
+// Global loads of step k+1 are issued before the MFMAs of step k (register
+// double buffering). Tiles are assigned XCD-major: each of the 8 XCDs takes a
+// contiguous range of tile indices with token tiles fastest, so workgroups
+// sharing a weight tile run on the same XCD and share its L2.
+constexpr int kBN = 128, kBM = 128, kBK = 64;
 
 enum { EPI_SILU_MUL_F16 = 0, EPI_STORE_BF16 = 1 };
 
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ W,
+__global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ Wt,
                                                    const uint16_t* __restrict__ Act,
                                                    uint16_t* __restrict__ out, int M, int N,
                                                    int K) {
-  __shared__ uint16_t sA[kBN * kLdsStride];
-  __shared__ uint16_t sB[kBM * kLdsStride];
+  __shared__ uint16_t sA[(kBN / 16) * (kBK / 32) * 512];
+  __shared__ uint16_t sB[(kBM / 16) * (kBK / 32) * 512];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
 
-  // XCD-major tile index
   const int nN = (N + kBN - 1) / kBN, nM = (M + kBM - 1) / kBM;
   const int T = nN * nM;
   const int pid = blockIdx.x;
@@ -103,19 +103,29 @@ __global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ 
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int tn = tile / nM, tm = tile % nM;
   const int n0 = tn * kBN, m0 = tm * kBM;
+  const int nkb = K >> 5, nrb = N >> 4;
 
-  // loader mapping: 4 chunks of 16 bytes per thread per operand
-  const int lrow = tid >> 3, lch = tid & 7;
+  // weight loader: chunk c = tid + 256 i -> block (rbl, kbl) = ((c>>6)>>1, (c>>6)&1), slot c&63
   const uint16_t* wsrc[4];
-  const uint16_t* asrc[4];
+  int wdst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int f = n0 + lrow + 32 * i;
-    f = f < N ? f : N - 1;
-    int t = m0 + lrow + 32 * i;
+    const int c = tid + 256 * i, blk = c >> 6;
+    int rb = (n0 >> 4) + (blk >> 1);
+    rb = rb < nrb ? rb : nrb - 1;
+    wsrc[i] = Wt + ((int64_t)rb * nkb + (blk & 1)) * 512 + (c & 63) * 8;
+    wdst[i] = c * 8;
+  }
+  // activation loader: chunk c -> token row c>>3, 16-byte column chunk c&7
+  const uint16_t* asrc[4];
+  int adst[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i, tl = c >> 3, kc = c & 7;
+    int t = m0 + tl;
     t = t < M ? t : M - 1;
-    wsrc[i] = W + (int64_t)f * K + lch * 8;
-    asrc[i] = Act + (int64_t)t * K + lch * 8;
+    asrc[i] = Act + (int64_t)t * K + kc * 8;
+    adst[i] = (((tl >> 4) * 2 + (kc >> 2)) * 64 + (kc & 3) * 16 + (tl & 15)) * 8;
   }
 
   f32x4 acc[4][4];
@@ -124,15 +134,17 @@ __global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nkt = (K + kBK - 1) / kBK;
+  const int nkt = (nkb + 1) >> 1;
   u32x4 rw[4], ra[4];
   auto gload = [&](int kt) {
-    const int k = kt * kBK;
-    const bool kin = k + lch * 8 < K;
+    const int kb = kt * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rw[i] = kin ? ld16(wsrc[i] + k) : u32x4{0u, 0u, 0u, 0u};
-      ra[i] = kin ? ld16(asrc[i] + k) : u32x4{0u, 0u, 0u, 0u};
+      const int c = tid + 256 * i;
+      const bool win = kb + ((c >> 6) & 1) < nkb;
+      rw[i] = win ? ld16(wsrc[i] + (int64_t)kb * 512) : u32x4{0u, 0u, 0u, 0u};
+      const bool ain = kb * 32 + (c & 7) * 8 < K;
+      ra[i] = ain ? ld16(asrc[i] + kb * 32) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto lstore = [&]() {
@@ -141,8 +153,8 @@ __global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ 
       u32x4 h;
 #pragma unroll
       for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(rw[i][j]);
-      *reinterpret_cast<u32x4*>(&sA[(lrow + 32 * i) * kLdsStride + lch * 8]) = h;
-      *reinterpret_cast<u32x4*>(&sB[(lrow + 32 * i) * kLdsStride + lch * 8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sA[wdst[i]]) = h;
+      *reinterpret_cast<u32x4*>(&sB[adst[i]]) = ra[i];
     }
   };
 
@@ -152,14 +164,12 @@ __global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ 
   for (int kt = 0; kt < nkt; ++kt) {
     if (kt + 1 < nkt) gload(kt + 1);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       u32x4 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const u32x4*>(
-            &sA[(wn * 64 + i * 16 + col) * kLdsStride + ks * 32 + grp * 8]);
-        bf[i] = *reinterpret_cast<const u32x4*>(
-            &sB[(wm * 64 + i * 16 + col) * kLdsStride + ks * 32 + grp * 8]);
+        af[i] = *reinterpret_cast<const u32x4*>(&sA[(((wn * 4 + i) * 2 + ks) * 64 + lane) * 8]);
+        bf[i] = *reinterpret_cast<const u32x4*>(&sB[(((wm * 4 + i) * 2 + ks) * 64 + lane) * 8]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -174,6 +184,7 @@ __global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ 
   }
 
   // epilogue: lane holds features f0..f0+3 of token t for block (i, j)
+  const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int f0 = n0 + wn * 64 + i * 16 + grp * 4;

@@ -51,7 +51,7 @@ void profile_record(int kind, hipStream_t stream, bool start) {
 extern "C" {
 
 static const char* const kKernelNames[fmlp::KK_COUNT] = {
-    "pack_interleaved", "quantize_int4",   "dequant_int4",  "decode_gateup_bf16",
+    "pack_tile", "quantize_int4", "dequant_int4", "act_prep", "decode_gateup_bf16",
     "decode_down_bf16", "decode_gateup_int4", "decode_down_int4", "rms_prep_f16",
     "gemm_gateup_silu_f16", "gemm_down_f16"};
 

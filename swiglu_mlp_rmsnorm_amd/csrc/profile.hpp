@@ -10,6 +10,7 @@ enum KernelKind {
   KK_PACK = 0,
   KK_QUANTIZE,
   KK_DEQUANT,
+  KK_ACT_PREP,
   KK_DECODE_GATEUP_BF16,
   KK_DECODE_DOWN_BF16,
   KK_DECODE_GATEUP_INT4,

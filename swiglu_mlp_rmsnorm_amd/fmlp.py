@@ -13,7 +13,9 @@ import threading
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmlp.so")
+# FMLP_LIB selects another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("FMLP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       "libfmlp.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -34,7 +36,7 @@ FMLP_PATH_DECODE = 1
 FMLP_PATH_PREFILL = 2
 
 EXPORTS = (
-    "fmlp_pack_interleaved", "fmlp_quantize_int4", "fmlp_dequant_int4",
+    "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",
     "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
     "fmlp_profile_read", "fmlp_kernel_name",
@@ -63,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_LIB_PATH)
         P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
         L.fmlp_pack_interleaved.argtypes = [P, P, P, I64, I64, P]
+        L.fmlp_pack_matrix.argtypes = [P, P, I64, I64, P]
+        L.fmlp_int4_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.fmlp_quantize_int4.argtypes = [P, I64, I64, P, P, P]
         L.fmlp_dequant_int4.argtypes = [P, P, I64, I64, P, P]
         L.fmlp_workspace_size.argtypes = [I64, I64, I64, I32]
@@ -78,7 +82,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_double)]
         L.fmlp_kernel_name.argtypes = [I32]
         L.fmlp_kernel_name.restype = ctypes.c_char_p
-        for name in ("fmlp_pack_interleaved", "fmlp_quantize_int4", "fmlp_dequant_int4",
+        for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
+                     "fmlp_quantize_int4", "fmlp_dequant_int4",
                      "fmlp_forward", "fmlp_forward_path", "fmlp_last_hip_error",
                      "fmlp_profile_enable", "fmlp_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -133,14 +138,38 @@ def fmlp_pack_interleaved(w_gate, w_up, w_gu=None, stream=None):
     return w_gu
 
 
-def fmlp_quantize_int4(w, q=None, scales=None, stream=None):
-    """bf16 [rows,K] -> (uint8 codes [rows,K/2], fp16 scales [rows,K/32])."""
+def fmlp_pack_matrix(w, w_tiled=None, stream=None):
+    """Row-major bf16 [rows, K] -> the same matrix in the tiled layout (shape kept)."""
     _need(w, torch.bfloat16, "w")
     rows, K = w.shape
+    if w_tiled is None:
+        w_tiled = torch.empty((rows, K), dtype=torch.bfloat16, device=w.device)
+    _need(w_tiled, torch.bfloat16, "w_tiled")
+    if w_tiled.numel() != rows * K:
+        raise ValueError("w_tiled must hold rows*K elements")
+    _check(lib().fmlp_pack_matrix(_ptr(w), _ptr(w_tiled), rows, K, _stream(stream)),
+           "fmlp_pack_matrix")
+    return w_tiled
+
+
+def fmlp_int4_sizes(rows: int, K: int):
+    """(code bytes, scale bytes) of a tiled int4 [rows, K] matrix."""
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().fmlp_int4_sizes(rows, K, ctypes.byref(cb), ctypes.byref(sb)), "fmlp_int4_sizes")
+    return int(cb.value), int(sb.value)
+
+
+def fmlp_quantize_int4(w, q=None, scales=None, stream=None):
+    """Tiled bf16 [rows,K] -> (tiled int4 codes uint8, tiled fp16 scales), flat."""
+    _need(w, torch.bfloat16, "w")
+    rows, K = w.shape
+    cb, sb = fmlp_int4_sizes(rows, K)
     if q is None:
-        q = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
+        q = torch.empty(cb, dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty((rows, K // 32), dtype=torch.float16, device=w.device)
+        scales = torch.empty(sb // 2, dtype=torch.float16, device=w.device)
+    if q.numel() < cb or scales.numel() * 2 < sb:
+        raise ValueError("int4 buffers too small")
     _need(q, torch.uint8, "q")
     _need(scales, torch.float16, "scales")
     _check(lib().fmlp_quantize_int4(_ptr(w), rows, K, _ptr(q), _ptr(scales), _stream(stream)),
@@ -148,12 +177,13 @@ def fmlp_quantize_int4(w, q=None, scales=None, stream=None):
     return q, scales
 
 
-def fmlp_dequant_int4(q, scales, out=None, stream=None):
-    """(codes, scales) -> exact fp32 [rows, K]."""
+def fmlp_dequant_int4(q, scales, rows, K, out=None, stream=None):
+    """Tiled int4 (codes, scales) of a [rows, K] matrix -> exact row-major fp32."""
     _need(q, torch.uint8, "q")
     _need(scales, torch.float16, "scales")
-    rows, half = q.shape
-    K = 2 * half
+    cb, sb = fmlp_int4_sizes(rows, K)
+    if q.numel() < cb or scales.numel() * 2 < sb:
+        raise ValueError("int4 buffers too small")
     if out is None:
         out = torch.empty((rows, K), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
@@ -166,7 +196,8 @@ def fmlp_workspace_size(M: int, d: int, ff: int, wtype: int = FMLP_W_BF16) -> in
     return int(lib().fmlp_workspace_size(M, d, ff, wtype))
 
 
-def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream, path):
+def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream, path,
+             ff=None):
     _need(x, torch.bfloat16, "x")
     _need(gamma, torch.bfloat16, "gamma")
     M, d = x.shape
@@ -176,10 +207,13 @@ def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, 
         _need(w_down, torch.uint8, "w_down")
         _need(gu_scales, torch.float16, "gu_scales")
         _need(down_scales, torch.float16, "down_scales")
-        ff = w_down.shape[1] * 2
+        if ff is None:
+            raise ValueError("int4 weights are flat buffers: pass ff")
         wtype = FMLP_W_INT4_G32
-        if w_gu.shape != (2 * ff, d // 2) or w_down.shape != (d, ff // 2):
-            raise ValueError("int4 weight shapes do not match x")
+        for (t, s_, R, K) in ((w_gu, gu_scales, 2 * ff, d), (w_down, down_scales, d, ff)):
+            cb, sb = fmlp_int4_sizes(R, K)
+            if t.numel() < cb or s_.numel() * 2 < sb:
+                raise ValueError("int4 weight buffers too small for the shapes")
     else:
         _need(w_gu, torch.bfloat16, "w_gu")
         _need(w_down, torch.bfloat16, "w_down")
@@ -209,22 +243,23 @@ def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, 
 
 
 def fmlp_forward(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, ff=None):
     """y = W_down(SiLU(W_gate n) * (W_up n)), n = RMSNorm(x); bf16 x [M,d] -> y [M,d].
 
-    bf16 weights: w_gu [2ff,d], w_down [d,ff]. int4 weights: uint8 w_gu
-    [2ff,d/2] + fp16 gu_scales, uint8 w_down [d,ff/2] + fp16 down_scales.
+    bf16 weights: tiled w_gu [2ff,d] (fmlp_pack_interleaved) and tiled w_down
+    [d,ff] (fmlp_pack_matrix). int4 weights: the flat tiled code/scale
+    buffers of fmlp_quantize_int4, with ff given explicitly.
     Output and workspace are allocated with torch when not given.
     """
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
-                    None)
+                    None, ff)
 
 
 def fmlp_forward_path(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
-                      workspace=None, stream=None, path=FMLP_PATH_AUTO):
+                      workspace=None, stream=None, path=FMLP_PATH_AUTO, ff=None):
     """fmlp_forward with the kernel path chosen by the caller (FMLP_PATH_*)."""
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
-                    path)
+                    path, ff)
 
 
 def fmlp_kernel_names() -> list:

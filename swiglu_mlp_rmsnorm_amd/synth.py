@@ -88,10 +88,22 @@ def bf16_weight(rows: int, cols: int, seed: int, device="cpu", std: float = 0.02
     return normal_bf16((rows, cols), 0.0, std, seed, device)
 
 
+def int4_tiled_sizes(rows: int, K: int):
+    """(code bytes, scale count) of the library's tiled int4 storage of a
+    [rows, K] matrix: 1024-byte super-tiles of 16 rows x 4 groups of 32."""
+    nq = (K + 127) // 128
+    return (rows // 16) * nq * 1024, (rows // 16) * nq * 64
+
+
 def int4_weight(rows: int, K: int, seed_q: int, seed_s: int, device="cpu"):
-    """Raw packed int4 bytes [rows, K/2] and fp16 scales [rows, K/32]."""
-    return (uniform_bytes((rows, K // 2), seed_q, device),
-            uniform_f16((rows, K // 32), 0.005, 0.02, seed_s, device))
+    """Flat tiled int4 codes (uniform bytes) and flat fp16 scales ~U(0.005, 0.02).
+
+    Every byte is uniform, so every code is uniform over [-8, 7] whatever the
+    storage order; slots of padding groups (K not a multiple of 128) hold
+    random values that no consumer reads.
+    """
+    nb, ns = int4_tiled_sizes(rows, K)
+    return uniform_bytes((nb,), seed_q, device), uniform_f16((ns,), 0.005, 0.02, seed_s, device)
 
 
 def layer_bf16(w: Workload, layer: int, device="cpu"):
@@ -103,10 +115,8 @@ def layer_bf16(w: Workload, layer: int, device="cpu"):
 
 
 def layer_int4(w: Workload, layer: int, device="cpu"):
-    """(q_gu [2ff, d/2], s_gu [2ff, d/32], q_down [d, ff/2], s_down [d, ff/32]).
-
-    The gate/up matrix is drawn directly in its interleaved row order.
-    """
+    """Tiled int4 (q_gu, s_gu) of the logical [2ff, d] gate/up matrix (drawn
+    directly in interleaved row order) and (q_down, s_down) of [d, ff]."""
     s = lambda t: seed_of(w.index, layer, t)
     q_gu, s_gu = int4_weight(2 * w.ff, w.d, s(T_QGU), s(T_SGU), device)
     q_d, s_d = int4_weight(w.d, w.ff, s(T_QD), s(T_SD), device)

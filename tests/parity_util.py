@@ -3,11 +3,14 @@ oracle on the same seeded inputs and compare with the accuracy bar
 
     max |y - y_ref| <= 2e-2 * rms(y_ref)   and   sum|y - y_ref| / sum|y_ref| <= 3e-3
 
-(y_ref is the oracle's fp64 result, y the library's bf16 output)."""
+(y_ref is the oracle's fp64 result, y the library's bf16 output). The oracle
+always receives the seeded inputs themselves (host copies), never a buffer
+the HIP library produced."""
 import numpy as np
 import torch
 
 from oracle import oracle
+from swiglu_mlp_rmsnorm_amd import fmlp as F
 from swiglu_mlp_rmsnorm_amd import synth
 
 MAX_REL_TOL = 2e-2
@@ -30,21 +33,46 @@ def assert_parity(y_gpu, y_ref, what=""):
     return mx, l1
 
 
-def bf16_layer(d, ff, seed, device="cuda"):
-    """(w_gate, w_up, w_down) bf16 on the device, N(0, 0.02)."""
-    return (synth.bf16_weight(ff, d, seed + 2, device), synth.bf16_weight(ff, d, seed + 3, device),
-            synth.bf16_weight(d, ff, seed + 4, device))
+class Bf16Layer:
+    """Row-major synthetic weights (oracle side) and their packed, tiled
+    device copies (HIP side)."""
+
+    def __init__(self, d, ff, seed, device="cuda"):
+        self.d, self.ff = d, ff
+        self.wg = synth.bf16_weight(ff, d, seed + 2, device)
+        self.wu = synth.bf16_weight(ff, d, seed + 3, device)
+        self.wd = synth.bf16_weight(d, ff, seed + 4, device)
+        self.wgu_t = F.fmlp_pack_interleaved(self.wg, self.wu)
+        self.wd_t = F.fmlp_pack_matrix(self.wd)
+        self.host = tuple(synth.bits(t) for t in (self.wg, self.wu, self.wd))
+
+    def oracle(self, x, g, eps):
+        wg, wu, wd = self.host
+        return oracle.forward_unfused(synth.bits(x), synth.bits(g), eps, wg, wu, wd)
+
+    def forward(self, x, g, eps, **kw):
+        return F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **kw)
+
+
+class Int4Layer:
+    """Synthetic tiled int4 weights; the oracle untiles the same seeded bytes."""
+
+    def __init__(self, d, ff, seed, device="cuda"):
+        self.d, self.ff = d, ff
+        self.q_gu, self.s_gu = synth.int4_weight(2 * ff, d, seed, seed + 1, device)
+        self.q_d, self.s_d = synth.int4_weight(d, ff, seed + 2, seed + 3, device)
+        b = synth.bits
+        q_gu, s_gu = oracle.untile_int4(b(self.q_gu), b(self.s_gu), 2 * ff, d)
+        q_d, s_d = oracle.untile_int4(b(self.q_d), b(self.s_d), d, ff)
+        self.host = (q_gu, s_gu, q_d, s_d)
+
+    def oracle(self, x, g, eps):
+        return oracle.forward_int4(synth.bits(x), synth.bits(g), eps, *self.host)
+
+    def forward(self, x, g, eps, **kw):
+        return F.fmlp_forward_path(x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d,
+                                   ff=self.ff, **kw)
 
 
 def bf16_inputs(M, d, seed, device="cuda"):
     return synth.activations(M, d, seed, device), synth.gamma(d, seed + 1, device)
-
-
-def oracle_bf16(x, g, eps, w_gu, w_down):
-    b = synth.bits
-    return oracle.forward_bf16(b(x), b(g), eps, b(w_gu), b(w_down))
-
-
-def oracle_int4(x, g, eps, q_gu, s_gu, q_d, s_d):
-    b = synth.bits
-    return oracle.forward_int4(b(x), b(g), eps, b(q_gu), b(s_gu), b(q_d), b(s_d))

@@ -101,12 +101,25 @@ def test_pack_quant_dequant_validation():
     assert L.fmlp_pack_interleaved(a, b, ctypes.c_void_p(A["y"].value + 2), 704, 256,
                                    None) == F.FMLP_ERR_ALIGNMENT
     assert L.fmlp_pack_interleaved(a, b, a, 704, 256, None) == F.FMLP_ERR_INVALID_ARG
-    assert L.fmlp_quantize_int4(a, 4, 48, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
-    assert L.fmlp_quantize_int4(a, 4, 64, None, c, None) == F.FMLP_ERR_INVALID_ARG
-    assert L.fmlp_quantize_int4(a, 4, 64, a, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_quantize_int4(a, 16, 48, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_quantize_int4(a, 8, 64, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_quantize_int4(a, 16, 64, None, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_quantize_int4(a, 16, 64, a, c, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_dequant_int4(a, b, 0, 64, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
-    assert L.fmlp_dequant_int4(a, b, 4, 64, ctypes.c_void_p(A["y"].value + 4),
+    assert L.fmlp_dequant_int4(a, b, 16, 64, ctypes.c_void_p(A["y"].value + 4),
                                None) == F.FMLP_ERR_ALIGNMENT
+    assert L.fmlp_pack_matrix(a, None, 16, 64, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_matrix(a, c, 24, 64, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_pack_matrix(a, a, 16, 64, None) == F.FMLP_ERR_INVALID_ARG
+
+
+def test_int4_sizes_match_the_format():
+    from oracle import oracle
+    for R, K in ((16, 32), (64, 704), (57344, 8192), (8192, 28672)):
+        assert F.fmlp_int4_sizes(R, K) == (oracle.int4_tiled_sizes(R, K)[0],
+                                           oracle.int4_tiled_sizes(R, K)[1] * 2)
+    with pytest.raises(F.FmlpError):
+        F.fmlp_int4_sizes(8, 64)
 
 
 def test_status_strings():

@@ -1,0 +1,52 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (fmlp_forward, automatic path choice, weight set 0 of each workload).
+Rows are independent, so the oracle runs on a sample of rows and the error
+bar is evaluated over those rows."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from swiglu_mlp_rmsnorm_amd import fmlp as F
+from swiglu_mlp_rmsnorm_amd import synth
+
+from parity_util import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("phi3mini_decode_d3072_ff8192", 1), ("phi3mini_decode_d3072_ff8192", 8),
+    ("llama8b_decode_d4096_ff14336", 1), ("llama8b_decode_d4096_ff14336", 4),
+    ("llama8b_decode_d4096_ff14336", 16), ("llama8b_decode_d4096_ff14336", 32),
+    ("llama8b_prefill_d4096_ff14336", 512), ("llama8b_prefill_d4096_ff14336", 2048),
+    ("llama70b_int4_decode_d8192_ff28672", 1), ("llama70b_int4_decode_d8192_ff28672", 16),
+]
+
+
+def sample_rows(M, n):
+    if M <= n:
+        return list(range(M))
+    return sorted(set(int(r) for r in np.linspace(0, M - 1, n)))
+
+
+@pytest.mark.parametrize("wname,M", CASES)
+def test_full_size_parity(wname, M):
+    w = synth.WORKLOADS[wname]
+    x, g = synth.inputs(w, M, "cuda")
+    b = synth.bits
+    if w.wtype == "int4":
+        q_gu, s_gu, q_d, s_d = synth.layer_int4(w, 0, "cuda")
+        y = F.fmlp_forward(x, g, synth.EPS, q_gu, q_d, s_gu, s_d, ff=w.ff)
+        rows = sample_rows(M, 2)
+        host = (*oracle.untile_int4(b(q_gu), b(s_gu), 2 * w.ff, w.d),
+                *oracle.untile_int4(b(q_d), b(s_d), w.d, w.ff))
+        ref = oracle.forward_int4(b(x)[rows], b(g), synth.EPS, *host)
+    else:
+        wg, wu, wd = synth.layer_bf16(w, 0, "cuda")
+        y = F.fmlp_forward(x, g, synth.EPS, F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
+        rows = sample_rows(M, 8 if M <= 32 else 4)
+        ref = oracle.forward_unfused(b(x)[rows], b(g), synth.EPS, b(wg), b(wu), b(wd))
+    torch.cuda.synchronize()
+    assert torch.all(torch.isfinite(y.float()))
+    mx, l1 = assert_parity(y[rows], ref, f"{wname} M={M}")
+    print(f"{wname} M={M} rows={rows}: max/rms={mx:.3e} L1={l1:.3e}")

@@ -17,8 +17,11 @@ MUTATIONS = {
     "silu_on_up_branch": ("oracle_silu(g) * u", "oracle_silu(u) * g"),
     "w_down_transposed": ("acc += dv.at(j, i) * a[i]", "acc += dv.at(i % dv.K, j % ff) * a[i]"),
     "round_half_away": ("float rq = std::nearbyint(ratio_k);", "float rq = std::round(ratio_k);"),
-    "nibble_order_swapped": ("(k & 1) ? (byte >> 4) : (byte & 0xF)",
-                             "(k & 1) ? (byte & 0xF) : (byte >> 4)"),
+    "nibble_order_swapped": ("const uint8_t byte = qrow[k / 2];\n  const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);",
+                             "const uint8_t byte = qrow[k / 2];\n  const int nib = (k & 1) ? (byte & 0xF) : (byte >> 4);"),
+    "tile_slot_transposed": ("(((k % 32) / 8) * 16 + r % 16) * 8 + k % 8",
+                             "((r % 16) * 4 + (k % 32) / 8) * 8 + k % 8"),
+    "int4_tile_word_order": ("lane * 4 + g % 4", "(g % 4) * 64 + lane"),
     "sigmoid_not_silu": ("return t / (1.0 + std::exp(-t));", "return 1.0 / (1.0 + std::exp(-t));"),
 }
 

@@ -340,3 +340,48 @@ def test_int4_forward_matches_torch_composition():
     ref = (F.silu(n @ WGU[0::2].T) * (n @ WGU[1::2].T)) @ torch.from_numpy(wdn).T
     y = oracle.forward_int4(x, g, 1e-5, q_gu, s_gu, q_d, s_d)
     np.testing.assert_allclose(y, ref.numpy(), rtol=1e-11, atol=1e-13 * np.abs(ref.numpy()).max())
+
+
+# ------------------------------------------------------------ tiled layouts
+# Positions worked out by hand from the layout definition (16-row x 32-column
+# tiles; slot L = 16*((k%32)/8) + r%16 of 8 consecutive columns).
+
+def test_tile_bf16_positions_by_hand():
+    R, K = 32, 96
+    w = np.arange(R * K, dtype=np.uint16).reshape(R, K)
+    t = oracle.tile_bf16(w)
+    # (r=17, k=45): tile (1, 1) -> index 1*3+1 = 4; slot 16*1 + 1 = 17; offset 5
+    assert t[4 * 512 + 17 * 8 + 5] == w[17, 45]
+    # (r=0, k=8): tile 0, slot 16, offset 0
+    assert t[16 * 8] == w[0, 8]
+    # (r=15, k=95): tile (0, 2) -> 2; slot 16*3 + 15 = 63; offset 7
+    assert t[2 * 512 + 63 * 8 + 7] == w[15, 95]
+    assert np.array_equal(oracle.untile_bf16(t, R, K), w)
+    assert sorted(t.tolist()) == list(range(R * K))  # a permutation
+
+
+def test_tile_int4_positions_by_hand():
+    R, K = 32, 256          # nq = 2 super-tiles per 16-row block
+    q = np.zeros((R, K // 2), np.uint8)
+    s = np.zeros((R, K // 32), np.uint16)
+    q[5, 70 // 2] = 0x0B    # code (5, 70) = 0xB (-5), even k -> low nibble
+    s[21, 6] = 0x1234       # scale (21, group 6)
+    qt, st = oracle.tile_int4(q, s)
+    # (5, 70): g = 2 -> super-tile 0; slot 16*((70%32)//8) + 5 = 5; word 5*4 + 2 = 22;
+    # nibble 70%8 = 6 -> byte 22*4 + 3 = 91, low nibble
+    assert qt[91] == 0x0B and np.count_nonzero(qt) == 1
+    # scale (21, 6): super-tile (1, 1) -> 1*2 + 1 = 3; element 3*64 + 5*4 + 2 = 214
+    assert st[214] == 0x1234 and np.count_nonzero(st) == 1
+    q2, s2 = oracle.untile_int4(qt, st, R, K)
+    assert np.array_equal(q2, q) and np.array_equal(s2, s)
+
+
+def test_tile_int4_padding_is_zero():
+    R, K = 16, 96           # 3 groups -> one super-tile with one padding group
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    s = rng.integers(1, 30000, (R, K // 32), dtype=np.uint16)
+    qt, st = oracle.tile_int4(q, s)
+    words = qt.view(np.uint32).reshape(64, 4)
+    assert np.all(words[:, 3] == 0)
+    assert np.all(st.reshape(16, 4)[:, 3] == 0)
