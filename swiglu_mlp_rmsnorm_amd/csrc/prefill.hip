@@ -17,6 +17,8 @@
 #include "launch.hpp"
 #include "profile.hpp"
 
+#include <mutex>
+
 namespace fmlp {
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -70,144 +72,263 @@ __global__ __launch_bounds__(256) void k_rms_prep_f16(const uint16_t* __restrict
 // ---------------------------------------------------------------- GEMM
 // C[f, t] = sum_k W[f, k] * Act[t, k]; W in the fragment-tiled bf16 layout
 // (converted to fp16 on its way into LDS), Act fp16 [M, K] row-major.
-// Tile: BN = 128 features x BM = 128 tokens x BK = 64, 256 threads = 4 waves
-// in a 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA 16x16x32 blocks.
-// LDS holds both operands in fragment order (1 KB per 16 x 32 block, slot L
-// at byte 16 L), so every MFMA operand read is one contiguous ds_read_b128
-// per wave; weight tiles are copied as they are, activation chunks are
-// scattered to their slots on the way in.
-// Global loads of step k+1 are issued before the MFMAs of step k (register
-// double buffering). Tiles are assigned XCD-major: each of the 8 XCDs takes a
-// contiguous range of tile indices with token tiles fastest, so workgroups
-// sharing a weight tile run on the same XCD and share its L2.
-constexpr int kBN = 128, kBM = 128, kBK = 64;
-
+//
+// MFMA 32x32x16 f16: measured on MI355X it sustains ~2.0 PFLOP/s from a
+// single wave per SIMD with two independent accumulators, where 16x16x32
+// needs several waves and many chains to pass ~1.3 PFLOP/s.
+// Operands: A = weights (32 rows x 16 K per fragment), B = activations
+// (32 tokens x 16 K); lane l supplies row/token l % 32, K slots
+// 8*(l/32) .. +7; the accumulator lane l holds column (token) l % 32 and
+// rows 8i + 4*(l/32) + j in register 4i + j, so each lane owns whole
+// gate/up pairs (rows 2p, 2p+1) for the SiLU*mul epilogue.
+//
+// Block tile BN features x BM tokens x 64 K, WGN x WGM waves each owning a
+// (BN/WGN) x (BM/WGM) sub-tile. LDS holds both operands in fragment order
+// (1 KB per 32 x 16 fragment, slot L at byte 16 L) in two stages; every MFMA
+// operand read is one contiguous ds_read_b128 per wave. Weights pass through
+// registers (bf16 -> fp16, and the 16 x 32 storage tile is re-cut into two
+// 32 x 16 fragments); activations are loaded straight into LDS in fragment
+// order (global_load_lds). Stage k+1 is filled while step k computes.
+// Tiles are assigned XCD-major: each of the 8 XCDs takes a contiguous range
+// of tile indices, token tiles fastest, so workgroups sharing a weight band
+// run on the same XCD and share its L2.
 enum { EPI_SILU_MUL_F16 = 0, EPI_STORE_BF16 = 1 };
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_wf16(const uint16_t* __restrict__ Wt,
-                                                   const uint16_t* __restrict__ Act,
-                                                   uint16_t* __restrict__ out, int M, int N,
-                                                   int K) {
-  __shared__ uint16_t sA[(kBN / 16) * (kBK / 32) * 512];
-  __shared__ uint16_t sB[(kBM / 16) * (kBK / 32) * 512];
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int NB, int MB, int WGN, int WGM>  // 32-row blocks per tile; wave grid
+struct GemmCfg {
+  static constexpr int W = WGN * WGM, THREADS = 64 * W;
+  static constexpr int BN = NB * 32, BM = MB * 32;
+  static constexpr int WNB = NB / WGN, WMB = MB / WGM;     // 32-row blocks per wave
+  // per stage: NB*2 storage tiles of weights, MB*4 fragments of activations
+  static constexpr int A_PER_T = NB * 2 * 2 / W, B_PER_T = MB * 4 / W;  // 16-byte chunks
+  static constexpr int A_ELEMS = NB * 4 * 512, B_ELEMS = MB * 4 * 512;  // fp16 per stage
+  static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
+  static constexpr size_t LDS_BYTES = 2 * STAGE_ELEMS * 2;
+  static_assert(A_PER_T >= 2 && A_PER_T % 2 == 0 && B_PER_T >= 4 && B_PER_T % 4 == 0, "tile");
+};
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// LDS fragment index of (32-row block, 16-column chunk q of the 64-column step).
+__device__ __forceinline__ int frag_at(int blk32, int q) { return blk32 * 4 + q; }
+
+template <int NB, int MB, int WGN, int WGM, int EPI>
+__global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_wf16(const uint16_t* __restrict__ Wt,
+                                                              const uint16_t* __restrict__ Act,
+                                                              uint16_t* __restrict__ out, int M,
+                                                              int N, int K) {
+  using C = GemmCfg<NB, MB, WGN, WGM>;
+  extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WGN, wm = wave / WGN;
 
-  const int nN = (N + kBN - 1) / kBN, nM = (M + kBM - 1) / kBM;
+  const int nN = (N + C::BN - 1) / C::BN, nM = (M + C::BM - 1) / C::BM;
   const int T = nN * nM;
   const int pid = blockIdx.x;
   const int xcd = pid & 7, idx = pid >> 3;
   const int per = T >> 3, rem = T & 7;
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int tn = tile / nM, tm = tile % nM;
-  const int n0 = tn * kBN, m0 = tm * kBM;
+  const int n0 = tn * C::BN, m0 = tm * C::BM;
   const int nkb = K >> 5, nrb = N >> 4;
 
-  // weight loader: chunk c = tid + 256 i -> block (rbl, kbl) = ((c>>6)>>1, (c>>6)&1), slot c&63
-  const uint16_t* wsrc[4];
-  int wdst[4];
+  // Weight chunk i of a thread: storage tile (16-row block rbl, K block kbl),
+  // slot = lane; rbl = W*(i >> 1) + wave, kbl = i & 1. Its 8 values (row r'
+  // = lane % 16, columns 8*(lane/16) ..) land in fragment (rbl/2, 2 kbl +
+  // lane/32), slot 32*((lane/16) % 2) + 16*(rbl % 2) + lane % 16.
+  const uint16_t* wbase = Wt + (int64_t)(n0 >> 4) * nkb * 512;
+  uint32_t woff[C::A_PER_T];
+  int wdst[C::A_PER_T];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, blk = c >> 6;
-    int rb = (n0 >> 4) + (blk >> 1);
-    rb = rb < nrb ? rb : nrb - 1;
-    wsrc[i] = Wt + ((int64_t)rb * nkb + (blk & 1)) * 512 + (c & 63) * 8;
-    wdst[i] = c * 8;
+  for (int i = 0; i < C::A_PER_T; ++i) {
+    const int rbl = C::W * (i >> 1) + wave, kbl = i & 1;
+    const int rbc = (n0 >> 4) + rbl < nrb ? rbl : nrb - 1 - (n0 >> 4);  // rows past N clamped
+    woff[i] = (uint32_t)((rbc * nkb + kbl) * 512 + lane * 8);
+    const int g = lane >> 4;
+    wdst[i] = (frag_at(rbl >> 1, 2 * kbl + (g >> 1)) * 64 + 32 * (g & 1) + 16 * (rbl & 1) +
+               (lane & 15)) * 8;
   }
-  // activation loader: chunk c -> token row c>>3, 16-byte column chunk c&7
-  const uint16_t* asrc[4];
-  int adst[4];
+  // Activation chunk i: fragment (token block tb = W*(i >> 2) + wave... ) see below;
+  // fragment (tb, q) slot = lane covers token 32 tb + lane % 32, columns 16 q + 8 (lane/32).
+  const uint16_t* abase = Act + (int64_t)m0 * K;
+  uint32_t aoff[C::B_PER_T];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i, tl = c >> 3, kc = c & 7;
-    int t = m0 + tl;
-    t = t < M ? t : M - 1;
-    asrc[i] = Act + (int64_t)t * K + kc * 8;
-    adst[i] = (((tl >> 4) * 2 + (kc >> 2)) * 64 + (kc & 3) * 16 + (tl & 15)) * 8;
+  for (int i = 0; i < C::B_PER_T; ++i) {
+    const int f = C::W * i + wave;  // fragment index within the stage: tb = f / 4, q = f % 4
+    int tl = (f >> 2) * 32 + (lane & 31);
+    tl = m0 + tl < M ? tl : M - 1 - m0;  // tokens past M clamped
+    aoff[i] = (uint32_t)(tl * K + (f & 3) * 16 + (lane >> 5) * 8);
   }
 
-  f32x4 acc[4][4];
+  f32x16 acc[C::WNB][C::WMB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::WNB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::WMB; ++j) acc[i][j] = f32x16{};
 
   const int nkt = (nkb + 1) >> 1;
-  u32x4 rw[4], ra[4];
-  auto gload = [&](int kt) {
+  u32x4 rw[C::A_PER_T];
+  // weights of step kt -> registers (K block kb + 1 may not exist on the last step)
+  auto a_load = [&](int kt) {
     const int kb = kt * 2;
+    const bool full = kb + 1 < nkb;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const bool win = kb + ((c >> 6) & 1) < nkb;
-      rw[i] = win ? ld16(wsrc[i] + (int64_t)kb * 512) : u32x4{0u, 0u, 0u, 0u};
-      const bool ain = kb * 32 + (c & 7) * 8 < K;
-      ra[i] = ain ? ld16(asrc[i] + kb * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < C::A_PER_T; ++i)
+      rw[i] = ((i & 1) == 0 || full) ? ld16(wbase + woff[i] + kb * 512) : u32x4{0u, 0u, 0u, 0u};
   };
-  auto lstore = [&]() {
+  // registers -> LDS stage, bf16 -> fp16, re-cut into 32 x 16 fragments
+  auto a_store = [&](int stage) {
+    uint16_t* sA = lds + stage * C::STAGE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < C::A_PER_T; ++i) {
       u32x4 h;
 #pragma unroll
       for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(rw[i][j]);
       *reinterpret_cast<u32x4*>(&sA[wdst[i]]) = h;
-      *reinterpret_cast<u32x4*>(&sB[adst[i]]) = ra[i];
+    }
+  };
+  // activations of step kt -> LDS stage directly; a missing last K block
+  // (fragments q = 2, 3) is zero-filled from registers instead
+  auto b_load = [&](int kt, int stage) {
+    const int kb = kt * 2;
+    const bool full = kb + 1 < nkb;
+    uint16_t* sB = lds + stage * C::STAGE_ELEMS + C::A_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i) {
+      const int f = C::W * i + wave;
+      uint16_t* dst = &sB[f * 512];
+      if ((f & 3) < 2 || full)
+        __builtin_amdgcn_global_load_lds((gptr_t)(abase + aoff[i] + kb * 32), (lptr_t)dst, 16, 0, 0);
+      else
+        *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  gload(0);
-  lstore();
-  __syncthreads();
+  // prologue: stage 0 <- step 0; registers <- weights of step 1
+  a_load(0);
+  b_load(0, 0);
+  a_store(0);
+  if (nkt > 1) a_load(1);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+
   for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const u32x4*>(&sA[(((wn * 4 + i) * 2 + ks) * 64 + lane) * 8]);
-        bf[i] = *reinterpret_cast<const u32x4*>(&sB[(((wm * 4 + i) * 2 + ks) * 64 + lane) * 8]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f16(af[i], bf[j], acc[i][j]);
-    }
-    __syncthreads();
+    const int cur = kt & 1, nxt = cur ^ 1;
+    // stage nxt was released by the last barrier: fill it for step kt+1 while
+    // this step computes; the weights of step kt+2 start loading right away
     if (kt + 1 < nkt) {
-      lstore();
-      __syncthreads();
+      a_store(nxt);
+      if (kt + 2 < nkt) a_load(kt + 2);
+      b_load(kt + 1, nxt);
     }
+    const uint16_t* sA = lds + cur * C::STAGE_ELEMS;
+    const uint16_t* sB = sA + C::A_ELEMS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      u32x4 af[C::WNB], bf[C::WMB];
+#pragma unroll
+      for (int i = 0; i < C::WNB; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(&sA[frag_at(wn * C::WNB + i, q) * 512 + lane * 8]);
+#pragma unroll
+      for (int j = 0; j < C::WMB; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(&sB[frag_at(wm * C::WMB + j, q) * 512 + lane * 8]);
+#pragma unroll
+      for (int i = 0; i < C::WNB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::WMB; ++j) acc[i][j] = mfma32_f16(af[i], bf[j], acc[i][j]);
+    }
+    // stage nxt complete (direct loads and this wave's writes) before the barrier
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
   }
 
-  // epilogue: lane holds features f0..f0+3 of token t for block (i, j)
-  const int col = lane & 15, grp = lane >> 4;
+  // epilogue: lane holds token t = col of block (i, j) and rows 8r + 4 grp + e
+  const int col = lane & 31, grp = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f0 = n0 + wn * 64 + i * 16 + grp * 4;
-    if (f0 >= N) continue;
+  for (int i = 0; i < C::WNB; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = m0 + wm * 64 + j * 16 + col;
+    for (int j = 0; j < C::WMB; ++j) {
+      const int t = m0 + (wm * C::WMB + j) * 32 + col;
       if (t >= M) continue;
-      const f32x4 v = acc[i][j];
-      if (EPI == EPI_SILU_MUL_F16) {
-        const _Float16 a0 = (_Float16)silu_mul(v[0], v[1]);
-        const _Float16 a1 = (_Float16)silu_mul(v[2], v[3]);
-        const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-        *reinterpret_cast<uint32_t*>(out + (int64_t)t * (N / 2) + f0 / 2) = packed;
-      } else {
-        const uint32_t lo = pack_bf16_rne(v[0], v[1]), hi = pack_bf16_rne(v[2], v[3]);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(out + (int64_t)t * N + f0);
-        dst[0] = lo;
-        dst[1] = hi;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int f0 = n0 + (wn * C::WNB + i) * 32 + 8 * r + 4 * grp;
+        if (f0 >= N) continue;
+        const float v0 = acc[i][j][4 * r], v1 = acc[i][j][4 * r + 1];
+        const float v2 = acc[i][j][4 * r + 2], v3 = acc[i][j][4 * r + 3];
+        if (EPI == EPI_SILU_MUL_F16) {
+          const _Float16 a0 = (_Float16)silu_mul(v0, v1);
+          const _Float16 a1 = (_Float16)silu_mul(v2, v3);
+          const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+          *reinterpret_cast<uint32_t*>(out + (int64_t)t * (N / 2) + f0 / 2) = packed;
+        } else {
+          uint32_t* dst = reinterpret_cast<uint32_t*>(out + (int64_t)t * N + f0);
+          dst[0] = pack_bf16_rne(v0, v1);
+          dst[1] = pack_bf16_rne(v2, v3);
+        }
       }
     }
   }
+}
+
+// Launch one GEMM with a given block tile and wave grid.
+template <int NB, int MB, int WGN, int WGM, int EPI>
+static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, uint16_t* out, int M,
+                                int N, int K, hipStream_t stream) {
+  using C = GemmCfg<NB, MB, WGN, WGM>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [] {
+    attr_err =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_wf16<NB, MB, WGN, WGM, EPI>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((k_gemm_wf16<NB, MB, WGN, WGM, EPI>), dim3(tiles), dim3(C::THREADS),
+                     C::LDS_BYTES, stream, W, Act, out, M, N, K);
+  return hipGetLastError();
+}
+
+// Estimated cost of a tile choice: waves of workgroups (one workgroup per CU
+// for the large tiles, two for 128 x 128) times the time of one tile, which
+// grows with its area and with the workgroups sharing a CU, discounted by how
+// well the tile size feeds the matrix cores.
+static double gemm_cost(int M, int N, int bn, int bm, double eff, int per_cu) {
+  const int tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+  const int slots = 256 * per_cu;
+  const int waves = (tiles + slots - 1) / slots;
+  return (double)waves * bn * bm * per_cu / eff;
+}
+
+#ifndef FMLP_GEMM_TILE
+#define FMLP_GEMM_TILE 0  // 0: by cost; 1: 256x256 4 waves; 2: 128x256; 3: 128x128; 4: 256x256 8 waves
+#endif
+
+template <int EPI>
+static hipError_t launch_gemm(const uint16_t* W, const uint16_t* Act, uint16_t* out, int M, int N,
+                              int K, hipStream_t stream) {
+  if (FMLP_GEMM_TILE == 1) return launch_gemm_t<8, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
+  if (FMLP_GEMM_TILE == 2) return launch_gemm_t<4, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
+  if (FMLP_GEMM_TILE == 3) return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, stream);
+  if (FMLP_GEMM_TILE == 4) return launch_gemm_t<8, 8, 2, 4, EPI>(W, Act, out, M, N, K, stream);
+  const double c256 = gemm_cost(M, N, 256, 256, 1.0, 1);
+  const double c128n = gemm_cost(M, N, 128, 256, 0.85, 1);
+  const double c128 = gemm_cost(M, N, 128, 128, 0.7, 2);
+  if (c256 <= c128n && c256 <= c128)
+    return launch_gemm_t<8, 8, 2, 4, EPI>(W, Act, out, M, N, K, stream);
+  if (c128n <= c128) return launch_gemm_t<4, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
+  return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, stream);
 }
 
 hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
@@ -221,21 +342,15 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nM = (p.M + kBM - 1) / kBM;
-  const int N1 = 2 * p.ff;
-  const int T1 = ((N1 + kBN - 1) / kBN) * nM;
   {
     ProfileScope prof(KK_GEMM_GATEUP, stream);
-    hipLaunchKernelGGL((k_gemm_wf16<EPI_SILU_MUL_F16>), dim3(T1), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(p.w_gu), n, a, p.M, N1, p.d);
+    e = launch_gemm<EPI_SILU_MUL_F16>(reinterpret_cast<const uint16_t*>(p.w_gu), n, a, p.M,
+                                      2 * p.ff, p.d, stream);
   }
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int T2 = ((p.d + kBN - 1) / kBN) * nM;
   ProfileScope prof(KK_GEMM_DOWN, stream);
-  hipLaunchKernelGGL((k_gemm_wf16<EPI_STORE_BF16>), dim3(T2), dim3(256), 0, stream,
-                     reinterpret_cast<const uint16_t*>(p.w_down), a, p.y, p.M, p.d, p.ff);
-  return hipGetLastError();
+  return launch_gemm<EPI_STORE_BF16>(reinterpret_cast<const uint16_t*>(p.w_down), a, p.y, p.M,
+                                     p.d, p.ff, stream);
 }
 
 }  // namespace fmlp
