@@ -45,6 +45,9 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (the "
+                         "known-size reference for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -71,6 +74,20 @@ def kernel_bytes(kernel, M, d, ff, wtype):
     if "gateup" in kernel:
         return gu + M * d * 2 + d * 2 + M * ff * 4
     return dn + M * ff * 4 + M * d * 2
+
+
+def gemm_bytes(kernel, M, d, ff):
+    """Algorithmic bytes of one prefill GEMM launch: bf16 weights, fp16
+    activations in, its output (fp16 SiLU*mul product, or bf16 y)."""
+    if kernel == "gemm_gateup_silu_f16":
+        return 2 * ff * d * 2 + M * d * 2 + M * ff * 2
+    return d * ff * 2 + M * ff * 2 + M * d * 2
+
+
+def algorithmic_bytes(kernel, M, d, ff, wtype):
+    if kernel.startswith("gemm"):
+        return gemm_bytes(kernel, M, d, ff)
+    return kernel_bytes(kernel, M, d, ff, wtype)
 
 
 def step_flops(M, d, ff):
@@ -296,8 +313,25 @@ def default_steps(w, M):
     return 100 * w.sets, 4 * w.sets
 
 
+def copy_calibration(mib):
+    """Five plain copies of `mib` MiB between two fresh device buffers: each
+    reads and writes exactly mib * 2^20 bytes, which makes it the yardstick
+    for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path: every workload runs on a single MI355X.", file=sys.stderr)

@@ -1,0 +1,130 @@
+#!/usr/bin/env python3
+"""Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
+
+  ktrace: --kernel-trace --stats output -> per-kernel call count and
+          average / min / max duration.
+  pmc:    four --pmc runs (FETCH_SIZE and WRITE_SIZE of one kernel, the same
+          two counters of a plain copy of known size) -> HBM bytes per launch
+          of that kernel, each counter scaled by what it reads for the copy.
+
+Reads CSV files only; runs nothing on the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def _one(pattern):
+    hits = sorted(glob.glob(pattern, recursive=True))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def ktrace(args):
+    path = _one(os.path.join(args.dir, "**", "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    out = [f"# rocprofv3 kernel trace: {args.title}",
+           f"command: {args.cmd}", "",
+           f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = re.sub(r"\(.*", "", r["Name"])[:90]
+        out.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+                   f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                   f"{float(r['Percentage']):>6.2f}  {name}")
+    text = "\n".join(out) + "\n"
+    open(args.out, "w").write(text)
+    print(text)
+
+
+def _counter(dirname, counter, match):
+    """Per-dispatch values of one counter for kernels whose name matches."""
+    path = _one(os.path.join(dirname, "**", "*counter_collection.csv"))
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or not re.search(match, r["Kernel_Name"]):
+            continue
+        key = r["Dispatch_Id"]
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"{counter}: no dispatch of /{match}/ in {path}")
+    return list(vals.values())
+
+
+def pmc(args):
+    from bench import algorithmic_bytes, kernel_source_sha
+    from swiglu_mlp_rmsnorm_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    alg = algorithmic_bytes(args.kernel, args.M, w.d, w.ff, w.wtype)
+    copy_f = statistics.median(_counter(args.copy_fetch, "FETCH_SIZE", args.copy_match))
+    copy_w = statistics.median(_counter(args.copy_write, "WRITE_SIZE", args.copy_match))
+    k_f = _counter(args.fetch, "FETCH_SIZE", args.match)
+    k_w = _counter(args.write, "WRITE_SIZE", args.match)
+    # counters are KiB per dispatch; the copy moves copy_bytes each way
+    fetch_scale = args.copy_bytes / (copy_f * 1024.0)
+    write_scale = args.copy_bytes / (copy_w * 1024.0)
+    fetch_b = statistics.median(k_f) * 1024.0 * fetch_scale
+    write_b = statistics.median(k_w) * 1024.0 * write_scale
+    traffic = fetch_b + write_b
+    sha = kernel_source_sha(args.kernel)
+    lines = [
+        f"# HBM traffic of {args.kernel} on {args.workload}, M={args.M}",
+        f"kernel: {args.kernel}",
+        f"kernel_match: {args.match}",
+        f"source_sha: {sha}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {traffic / alg:.4f}",
+        f"dispatches_fetch: {len(k_f)}",
+        f"dispatches_write: {len(k_w)}",
+        f"fetch_kib_median: {statistics.median(k_f):.1f}",
+        f"write_kib_median: {statistics.median(k_w):.1f}",
+        f"copy_bytes: {args.copy_bytes}",
+        f"copy_fetch_kib: {copy_f:.1f}",
+        f"copy_write_kib: {copy_w:.1f}",
+        f"fetch_scale: {fetch_scale:.4f}",
+        f"write_scale: {write_scale:.4f}",
+        "",
+        "commands:",
+        f"  kernel FETCH_SIZE: {args.cmd_fetch}",
+        f"  kernel WRITE_SIZE: {args.cmd_write}",
+        f"  copy FETCH_SIZE:   {args.cmd_copy_fetch}",
+        f"  copy WRITE_SIZE:   {args.cmd_copy_write}",
+    ]
+    text = "\n".join(l for l in lines if l is not None) + "\n"
+    open(args.out, "w").write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    k = sub.add_parser("ktrace")
+    k.add_argument("--dir", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--out", required=True)
+    p = sub.add_parser("pmc")
+    for a in ("fetch", "write", "copy_fetch", "copy_write", "match", "kernel", "workload",
+              "out", "cmd_fetch", "cmd_write", "cmd_copy_fetch", "cmd_copy_write"):
+        p.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
+    p.add_argument("--copy-match", default=".")
+    p.add_argument("--copy-bytes", type=int, required=True)
+    p.add_argument("--M", type=int, required=True)
+    args = ap.parse_args()
+    {"ktrace": ktrace, "pmc": pmc}[args.mode](args)
+
+
+if __name__ == "__main__":
+    main()

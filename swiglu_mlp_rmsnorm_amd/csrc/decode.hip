@@ -426,24 +426,21 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
   hipError_t e;
   if constexpr (WK == WK_INT4) {
-    ProfileScope prof(KK_ACT_PREP, stream);
-    hipLaunchKernelGGL(k_act_prep_q4, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps, ws.n0,
-                       p.d);
+    launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps,
+                  ws.n0, p.d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
   const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
-  {
-    ProfileScope prof(WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16, stream);
-    hipLaunchKernelGGL((k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP>),
-                       dim3((2 * p.ff) / (16 * RB)), dim3(64 * FMLP_GU_S), 0, stream, p.w_gu,
-                       p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M, p.d, p.ff);
-  }
+  launch_kernel(WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16,
+                k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP>, dim3((2 * p.ff) / (16 * RB)),
+                dim3(64 * FMLP_GU_S), 0, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1,
+                p.M, p.d, p.ff);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  ProfileScope prof(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16, stream);
-  hipLaunchKernelGGL((k_decode_down<WK, NCB, FMLP_DN_S, DP>), dim3(p.d / 16), dim3(64 * FMLP_DN_S),
-                     0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
+  launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
+                k_decode_down<WK, NCB, FMLP_DN_S, DP>, dim3(p.d / 16), dim3(64 * FMLP_DN_S), 0,
+                stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
   return hipGetLastError();
 }
 

@@ -45,9 +45,8 @@ __global__ __launch_bounds__(256) void k_tile_bf16(const uint16_t* __restrict__ 
 static hipError_t launch_tile(const uint16_t* a, const uint16_t* b, uint16_t* out, int64_t R,
                               int64_t K, hipStream_t stream) {
   const int64_t blocks = (R * K / 8 + 255) / 256;
-  ProfileScope prof(KK_PACK, stream);
-  hipLaunchKernelGGL(k_tile_bf16, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0,
-                     stream, a, b, out, R, K);
+  launch_kernel(KK_PACK, k_tile_bf16, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                dim3(256), 0, stream, a, b, out, R, K);
   return hipGetLastError();
 }
 
@@ -131,11 +130,8 @@ hipError_t launch_quantize(const uint16_t* wt, int64_t R, int64_t K, uint8_t* qt
                            hipStream_t stream, int* range_error) {
   hipLaunchKernelGGL(k_quant_flag_reset, dim3(1), dim3(1), 0, stream);
   const int64_t threads = (R / 16) * ((K + 127) / 128) * 4 * 16;
-  {
-    ProfileScope prof(KK_QUANTIZE, stream);
-    hipLaunchKernelGGL(k_quantize_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, wt, R, K, reinterpret_cast<uint32_t*>(qt), st);
-  }
+  launch_kernel(KK_QUANTIZE, k_quantize_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                0, stream, wt, R, K, reinterpret_cast<uint32_t*>(qt), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int flag = 0;
@@ -178,9 +174,8 @@ __global__ __launch_bounds__(256) void k_dequant_int4(const uint32_t* __restrict
 hipError_t launch_dequant(const uint8_t* qt, const uint16_t* st, int64_t R, int64_t K, float* out,
                           hipStream_t stream) {
   const int64_t threads = R * (K / 32);
-  ProfileScope prof(KK_DEQUANT, stream);
-  hipLaunchKernelGGL(k_dequant_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const uint32_t*>(qt), st, R, K, out);
+  launch_kernel(KK_DEQUANT, k_dequant_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                stream, reinterpret_cast<const uint32_t*>(qt), st, R, K, out);
   return hipGetLastError();
 }
 

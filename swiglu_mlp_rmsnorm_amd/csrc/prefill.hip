@@ -295,8 +295,9 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, uint16_t
   });
   if (attr_err != hipSuccess) return attr_err;
   const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL((k_gemm_wf16<NB, MB, WGN, WGM, EPI>), dim3(tiles), dim3(C::THREADS),
-                     C::LDS_BYTES, stream, W, Act, out, M, N, K);
+  launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
+                k_gemm_wf16<NB, MB, WGN, WGM, EPI>, dim3(tiles), dim3(C::THREADS),
+                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K);
   return hipGetLastError();
 }
 
@@ -335,20 +336,13 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   if (p.wtype != 0) return hipErrorNotSupported;
   uint16_t* n = reinterpret_cast<uint16_t*>(p.ws);
   uint16_t* a = reinterpret_cast<uint16_t*>(p.ws + align256((size_t)p.M * p.d * 2));
-  {
-    ProfileScope prof(KK_RMS_PREP, stream);
-    hipLaunchKernelGGL(k_rms_prep_f16, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps, n,
-                       p.d);
-  }
+  launch_kernel(KK_RMS_PREP, k_rms_prep_f16, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps,
+                n, p.d);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  {
-    ProfileScope prof(KK_GEMM_GATEUP, stream);
-    e = launch_gemm<EPI_SILU_MUL_F16>(reinterpret_cast<const uint16_t*>(p.w_gu), n, a, p.M,
-                                      2 * p.ff, p.d, stream);
-  }
+  e = launch_gemm<EPI_SILU_MUL_F16>(reinterpret_cast<const uint16_t*>(p.w_gu), n, a, p.M, 2 * p.ff,
+                                    p.d, stream);
   if (e != hipSuccess) return e;
-  ProfileScope prof(KK_GEMM_DOWN, stream);
   return launch_gemm<EPI_STORE_BF16>(reinterpret_cast<const uint16_t*>(p.w_down), a, p.y, p.M,
                                      p.d, p.ff, stream);
 }

@@ -18,7 +18,6 @@ struct Record {
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Record> g_records;
-thread_local hipEvent_t t_pending = nullptr;
 
 void clear_locked() {
   for (Record& r : g_records) {
@@ -32,18 +31,18 @@ void clear_locked() {
 
 bool profiling_enabled() { return g_on.load(std::memory_order_relaxed); }
 
-void profile_record(int kind, hipStream_t stream, bool start) {
-  hipEvent_t ev = nullptr;
-  if (hipEventCreate(&ev) != hipSuccess) return;
-  hipEventRecord(ev, stream);
-  if (start) {
-    t_pending = ev;
-    return;
+bool profile_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (hipEventCreate(start) != hipSuccess) return false;
+  if (hipEventCreate(stop) != hipSuccess) {
+    hipEventDestroy(*start);
+    return false;
   }
+  return true;
+}
+
+void profile_push(int kind, hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (t_pending) g_records.push_back(Record{kind, t_pending, ev});
-  else hipEventDestroy(ev);
-  t_pending = nullptr;
+  g_records.push_back(Record{kind, start, stop});
 }
 
 }  // namespace fmlp

@@ -1,7 +1,11 @@
 // Optional per-kernel timing: while enabled (fmlp_profile_enable), every
-// kernel launch is bracketed by HIP events recorded on its own stream.
+// kernel is launched with hipExtLaunchKernelGGL and a start/stop event pair,
+// which the runtime timestamps at the dispatch's own begin and end on the
+// launch stream (so the figure is the kernel's execution time, the same
+// quantity a kernel trace reports, without the gap between launches).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 namespace fmlp {
@@ -22,19 +26,23 @@ enum KernelKind {
 };
 
 bool profiling_enabled();
-void profile_record(int kind, hipStream_t stream, bool start);
+// Two fresh timing events, or false (then the launch goes untimed).
+bool profile_events(hipEvent_t* start, hipEvent_t* stop);
+void profile_push(int kind, hipEvent_t start, hipEvent_t stop);
 
-// RAII bracket around one launch; costs one relaxed atomic load when disabled.
-struct ProfileScope {
-  int kind;
-  hipStream_t stream;
-  bool on;
-  ProfileScope(int k, hipStream_t s) : kind(k), stream(s), on(profiling_enabled()) {
-    if (on) profile_record(kind, stream, true);
+// Launch `kernel`; timed under `kind` while profiling is enabled. Costs one
+// relaxed atomic load when it is not. Launch errors are left for the caller's
+// hipGetLastError().
+template <typename... Params, typename... Args>
+inline void launch_kernel(int kind, void (*kernel)(Params...), dim3 grid, dim3 block,
+                          uint32_t shmem, hipStream_t stream, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (profiling_enabled() && profile_events(&start, &stop)) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start, stop, 0, args...);
+    profile_push(kind, start, stop);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
   }
-  ~ProfileScope() {
-    if (on) profile_record(kind, stream, false);
-  }
-};
+}
 
 }  // namespace fmlp
