@@ -68,12 +68,18 @@ def step_bytes(M, d, ff, wtype):
 
 def kernel_bytes(kernel, M, d, ff, wtype):
     """Algorithmic bytes of one launch of a decode kernel: its weights
-    (+ scales), its activation inputs and its outputs; the SiLU*mul
-    intermediate counts as fp32 (4 bytes per element)."""
+    (+ scales), its activation inputs and its outputs. bf16 path: gate/up
+    reads x and gamma and writes the SiLU*mul product as a bf16 hi + lo pair
+    (4 bytes per element), which down reads back. int4 path: gate/up reads
+    the prepared fp16 n, the product is fp16 (2 bytes per element)."""
     gu, dn = weight_bytes(d, ff, wtype)
+    a_elem = 2 if wtype == "int4" else 4
     if "gateup" in kernel:
-        return gu + M * d * 2 + d * 2 + M * ff * 4
-    return dn + M * ff * 4 + M * d * 2
+        act_in = M * d * 2 + (0 if wtype == "int4" else d * 2)
+        return gu + act_in + M * ff * a_elem
+    if kernel == "act_prep":
+        return M * d * 2 + d * 2 + M * d * 2
+    return dn + M * ff * a_elem + M * d * 2
 
 
 def gemm_bytes(kernel, M, d, ff):
@@ -262,7 +268,7 @@ def run_one(wname, M, steps, warmup, args):
                     "units_per_launch": dom_units,
                     "traffic": measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
-        if name.startswith("decode"):
+        if name.startswith("decode") or name == "act_prep":
             k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (k["avg_us"] * 1e3), 1)
         elif name == "gemm_gateup_silu_f16":
             k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (k["avg_us"] * 1e6), 1)
