@@ -18,81 +18,119 @@
 #include "profile.hpp"
 
 #include <mutex>
+#include <type_traits>
 
 namespace fmlp {
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
-  // n fp16 [M, d], a fp16 [M, ff]
-  return align256((size_t)M * d * 2) + align256((size_t)M * ff * 2);
+// GEMM activations (the normalised input n and the SiLU*mul product a) live
+// in the workspace "fragment-tiled": for token block tb (32 tokens) and
+// column block kb (32 columns) two 1 KB MFMA fragments q = 0, 1 of 32 tokens
+// x 16 columns; slot s of a fragment holds token 32 tb + s % 32, columns
+// 32 kb + 16 q + 8 (s / 32) .. +7. A wave then loads any operand fragment as
+// one contiguous 1 KB burst. Token blocks are padded to 32 tokens; the
+// padding slots are never read into a stored output.
+__device__ __forceinline__ int64_t act_tile_off(int t, int k, int K) {
+  const int tb = t >> 5, kb = k >> 5, q = (k >> 4) & 1, slot = ((k >> 3) & 1) * 32 + (t & 31);
+  return ((int64_t)(tb * (K >> 5) + kb) * 2 + q) * 512 + slot * 8 + (k & 7);
 }
 
+static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
+
 // ---------------------------------------------------------------- RMS pre-pass
-// One 256-thread workgroup per token row.
-__global__ __launch_bounds__(256) void k_rms_prep_f16(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ gamma,
-                                                      float eps, uint16_t* __restrict__ n, int d) {
-  __shared__ float part[4];
-  const int64_t m = blockIdx.x;
-  const uint16_t* xr = x + m * d;
-  uint16_t* nr = n + m * d;
-  const int chunks = d >> 3;
+// (a) r_t = 1/sqrt(mean(x_t^2) + eps), one wave per token.
+__global__ __launch_bounds__(256) void k_rms_scale(const uint16_t* __restrict__ x, float eps,
+                                                   float* __restrict__ r, int M, int d) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= M) return;
+  const uint16_t* xr = x + (int64_t)t * d;
   float ss = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
+  for (int c = lane; c < (d >> 3); c += 64) {
     const u32x4 v = ld16(xr + c * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = bf16_lo(v[j]), b = bf16_hi(v[j]);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
+      const float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
-  const float r = 1.0f / sqrtf(tot / (float)d + eps);
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const u32x4 v = ld16(xr + c * 8);
-    const u32x4 g = ld16(gamma + c * 8);
-    u32x4 o;
+  if (lane == 0) r[t] = 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+// (b) n = fp16(gamma * x * r) in the fragment-tiled layout, one 16-byte slot
+// per thread (consecutive threads write consecutive slots). Slots of padding
+// tokens get the last token's values (finite, never stored).
+__global__ __launch_bounds__(256) void k_rms_tile(const uint16_t* __restrict__ x,
+                                                  const uint16_t* __restrict__ gamma,
+                                                  const float* __restrict__ r,
+                                                  uint16_t* __restrict__ n, int M, int d,
+                                                  int64_t slots) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= slots) return;
+  const int slot = (int)(g & 63);
+  const int64_t frag = g >> 6;                       // = tb * (d/16) + f
+  const int fpb = d >> 4;                            // fragments per token block
+  const int tb = (int)(frag / fpb), f = (int)(frag - (int64_t)tb * fpb);
+  int t = tb * 32 + (slot & 31);
+  t = t < M ? t : M - 1;
+  const int k = (f >> 1) * 32 + (f & 1) * 16 + (slot >> 5) * 8;
+  const u32x4 v = ld16(x + (int64_t)t * d + k);
+  const u32x4 gm = ld16(gamma + k);
+  const float rt = r[t];
+  u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const _Float16 lo = (_Float16)(bf16_lo(v[j]) * bf16_lo(g[j]) * r);
-      const _Float16 hi = (_Float16)(bf16_hi(v[j]) * bf16_hi(g[j]) * r);
-      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    st16(nr + c * 8, o);
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = (_Float16)(bf16_lo(v[j]) * bf16_lo(gm[j]) * rt);
+    const _Float16 hi = (_Float16)(bf16_hi(v[j]) * bf16_hi(gm[j]) * rt);
+    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
+  st16(n + g * 8, o);
 }
 
 // ---------------------------------------------------------------- GEMM
-// C[f, t] = sum_k W[f, k] * Act[t, k]; W in the fragment-tiled bf16 layout
-// (converted to fp16 on its way into LDS), Act fp16 [M, K] row-major.
+// C[f, t] = sum_k W[f, k] * Act[t, k]; W in the fragment-tiled bf16 layout,
+// Act fp16 in the fragment-tiled activation layout above.
 //
 // MFMA 32x32x16 f16: measured on MI355X it sustains ~2.0 PFLOP/s from a
-// single wave per SIMD with two independent accumulators, where 16x16x32
-// needs several waves and many chains to pass ~1.3 PFLOP/s.
+// single wave per SIMD with independent accumulators, where 16x16x32 needs
+// several waves and many chains to pass ~1.3 PFLOP/s.
 // Operands: A = weights (32 rows x 16 K per fragment), B = activations
 // (32 tokens x 16 K); lane l supplies row/token l % 32, K slots
 // 8*(l/32) .. +7; the accumulator lane l holds column (token) l % 32 and
 // rows 8i + 4*(l/32) + j in register 4i + j, so each lane owns whole
 // gate/up pairs (rows 2p, 2p+1) for the SiLU*mul epilogue.
 //
-// Block tile BN features x BM tokens x 64 K, WGN x WGM waves each owning a
-// (BN/WGN) x (BM/WGM) sub-tile. LDS holds both operands in fragment order
-// (1 KB per 32 x 16 fragment, slot L at byte 16 L) in two stages; every MFMA
-// operand read is one contiguous ds_read_b128 per wave. Weights pass through
-// registers (bf16 -> fp16, and the 16 x 32 storage tile is re-cut into two
-// 32 x 16 fragments); activations are loaded straight into LDS in fragment
-// order (global_load_lds). Stage k+1 is filled while step k computes.
+// Block tile BN features x BM tokens, 4 waves in a 2 x 2 grid, each owning a
+// (BN/2) x (BM/2) sub-tile; one K step is one 32-column block. Both operands
+// go from memory straight into LDS (global_load_lds, 16 bytes per lane, no
+// register staging and no LDS writes by the waves), each wave instruction
+// one contiguous 1 KB: the weights as their bf16 16 x 32 storage tiles, the
+// activations as their fragments. The
+// LDS is a ring of 5 stages (160 KB at 256 x 256), so the loads of step
+// kt+4 are issued while step kt computes: four steps of MFMA work hide the
+// memory latency.
+//
+// Each step has two 16-column sub-steps. Fragments are read one sub-step
+// ahead into two register sets; a weight fragment gathers rows 0-15 and
+// 16-31 from two storage tiles (each 16-lane group reads 256 contiguous
+// bytes: no bank conflicts) and is converted bf16 -> fp16 in registers just
+// before its MFMAs (exact in the fp16 normal range). Before the second
+// sub-step's MFMAs each wave waits only for step kt+1's loads (vector memory
+// counts retire in issue order, so later steps' loads stay in flight), meets
+// the barrier, and reads step kt+1's first fragments under those MFMAs.
+// Loads and LDS reads are interleaved between the MFMAs (sched_group_barrier)
+// so they issue in the matrix pipe's shadow.
+//
 // Tiles are assigned XCD-major: each of the 8 XCDs takes a contiguous range
 // of tile indices, token tiles fastest, so workgroups sharing a weight band
 // run on the same XCD and share its L2.
-enum { EPI_SILU_MUL_F16 = 0, EPI_STORE_BF16 = 1 };
+// Epilogues: SiLU*mul to the fp16 tiled activations (gate/up), bf16 y, or
+// an fp32 split-K partial (slice blockIdx.y of [splits, M, N]).
+enum { EPI_SILU_MUL_F16 = 0, EPI_STORE_BF16 = 1, EPI_STORE_F32 = 2 };
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -101,35 +139,53 @@ __device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <int NB, int MB, int WGN, int WGM>  // 32-row blocks per tile; wave grid
+template <int NB, int MB, int WGN_, int WGM_>  // 32-row blocks per tile; wave grid
 struct GemmCfg {
-  static constexpr int W = WGN * WGM, THREADS = 64 * W;
+  static constexpr int WGN = WGN_, WGM = WGM_, W = WGN * WGM, THREADS = 64 * W;
   static constexpr int BN = NB * 32, BM = MB * 32;
-  static constexpr int WNB = NB / WGN, WMB = MB / WGM;     // 32-row blocks per wave
-  // per stage: NB*2 storage tiles of weights, MB*4 fragments of activations
-  static constexpr int A_PER_T = NB * 2 * 2 / W, B_PER_T = MB * 4 / W;  // 16-byte chunks
-  static constexpr int A_ELEMS = NB * 4 * 512, B_ELEMS = MB * 4 * 512;  // fp16 per stage
+  static constexpr int WNB = NB / WGN, WMB = MB / WGM;  // 32-row blocks per wave
+  // 16-byte chunks per thread and step: weights 2*NB storage tiles of 1 KB,
+  // activations 2*MB fragments of 1 KB
+  static constexpr int A_PER_T = NB * 2 / W, B_PER_T = MB * 2 / W, LD_PER_T = A_PER_T + B_PER_T;
+  static constexpr int A_ELEMS = NB * 1024, B_ELEMS = MB * 1024;  // 16-bit elements per stage
   static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  static constexpr size_t LDS_BYTES = 2 * STAGE_ELEMS * 2;
-  static_assert(A_PER_T >= 2 && A_PER_T % 2 == 0 && B_PER_T >= 4 && B_PER_T % 4 == 0, "tile");
+  static constexpr int STAGES = 5;
+  static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * 2;
+  // one wave per SIMD when the accumulators alone fill 256 registers
+  static constexpr int WAVES_PER_EU = (WNB * WMB >= 16) ? 1 : 2;
+  static_assert(W == 4 && WNB >= 1 && WMB >= 1 && A_PER_T * W == NB * 2 &&
+                B_PER_T * W == MB * 2, "tile");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(3 * LD_PER_T < 64, "vmcnt field");
 };
 
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
 
-// LDS fragment index of (32-row block, 16-column chunk q of the 64-column step).
-__device__ __forceinline__ int frag_at(int blk32, int q) { return blk32 * 4 + q; }
+// s_waitcnt immediate for vmcnt(vm) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]). The builtin, unlike
+// inline asm, is seen by the compiler's own wait insertion, which then adds
+// no redundant waits.
+constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | 0x70 | ((vm >> 4) << 14); }
+
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(v[j]);
+  return h;
+}
 
 template <int NB, int MB, int WGN, int WGM, int EPI>
-__global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_wf16(const uint16_t* __restrict__ Wt,
-                                                              const uint16_t* __restrict__ Act,
-                                                              uint16_t* __restrict__ out, int M,
-                                                              int N, int K) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
+k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
+            void* __restrict__ out, int M, int N, int K) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   extern __shared__ __align__(16) uint16_t lds[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WGN, wm = wave / WGN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int wn = wave % C::WGN, wm = wave / C::WGN;
 
   const int nN = (N + C::BN - 1) / C::BN, nM = (M + C::BM - 1) / C::BM;
   const int T = nN * nM;
@@ -139,35 +195,36 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_wf16(const uint16_t* __
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int tn = tile / nM, tm = tile % nM;
   const int n0 = tn * C::BN, m0 = tm * C::BM;
+  // split K: slice blockIdx.y of gridDim.y equal slices of 32-column blocks
   const int nkb = K >> 5, nrb = N >> 4;
+  const int nkt = nkb / (int)gridDim.y, kbeg = (int)blockIdx.y * nkt;
 
-  // Weight chunk i of a thread: storage tile (16-row block rbl, K block kbl),
-  // slot = lane; rbl = W*(i >> 1) + wave, kbl = i & 1. Its 8 values (row r'
-  // = lane % 16, columns 8*(lane/16) ..) land in fragment (rbl/2, 2 kbl +
-  // lane/32), slot 32*((lane/16) % 2) + 16*(rbl % 2) + lane % 16.
-  const uint16_t* wbase = Wt + (int64_t)(n0 >> 4) * nkb * 512;
-  uint32_t woff[C::A_PER_T];
-  int wdst[C::A_PER_T];
+  // Weight chunk i of a thread: 16-row storage tile rb = W*i + wave of the
+  // tile (rows past N clamped), slot = lane; its LDS image sits at rb * 1 KB.
+  const uint16_t* wsrc[C::A_PER_T];
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
-    const int rbl = C::W * (i >> 1) + wave, kbl = i & 1;
-    const int rbc = (n0 >> 4) + rbl < nrb ? rbl : nrb - 1 - (n0 >> 4);  // rows past N clamped
-    woff[i] = (uint32_t)((rbc * nkb + kbl) * 512 + lane * 8);
-    const int g = lane >> 4;
-    wdst[i] = (frag_at(rbl >> 1, 2 * kbl + (g >> 1)) * 64 + 32 * (g & 1) + 16 * (rbl & 1) +
-               (lane & 15)) * 8;
+    const int rb = C::W * i + wave;
+    const int rbc = (n0 >> 4) + rb < nrb ? (n0 >> 4) + rb : nrb - 1;
+    wsrc[i] = Wt + ((int64_t)rbc * nkb + kbeg) * 512 + lane * 8;
   }
-  // Activation chunk i: fragment (token block tb = W*(i >> 2) + wave... ) see below;
-  // fragment (tb, q) slot = lane covers token 32 tb + lane % 32, columns 16 q + 8 (lane/32).
-  const uint16_t* abase = Act + (int64_t)m0 * K;
-  uint32_t aoff[C::B_PER_T];
+  // Activation chunk i: fragment f = W*i + wave of the stage (token block
+  // f/2 of the tile, half q = f%2), one contiguous 1 KB fragment of the tiled
+  // activations (token blocks past the last one clamped to it).
+  const int ntb = (M + 31) >> 5;
+  const uint16_t* asrc[C::B_PER_T];
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
-    const int f = C::W * i + wave;  // fragment index within the stage: tb = f / 4, q = f % 4
-    int tl = (f >> 2) * 32 + (lane & 31);
-    tl = m0 + tl < M ? tl : M - 1 - m0;  // tokens past M clamped
-    aoff[i] = (uint32_t)(tl * K + (f & 3) * 16 + (lane >> 5) * 8);
+    const int f = C::W * i + wave;
+    int tb = (m0 >> 5) + (f >> 1);
+    tb = tb < ntb ? tb : ntb - 1;
+    asrc[i] = Act + (((int64_t)tb * nkb + kbeg) * 2 + (f & 1)) * 512 + lane * 8;
   }
+  // LDS element offsets of this lane's fragment reads (within a stage): the
+  // weight fragment of 32-row block b, half q gathers storage tiles 2b
+  // (lanes 0-15, 32-47) and 2b+1 (lanes 16-31, 48-63), slots (2q + l/32)*16 + l%16.
+  const int a_rd = (((lane >> 4) & 1) * 512) + (((lane >> 5) * 16 + (lane & 15)) * 8);
+  const int b_rd = C::A_ELEMS + lane * 8;
 
   f32x16 acc[C::WNB][C::WMB];
 #pragma unroll
@@ -175,80 +232,127 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_wf16(const uint16_t* __
 #pragma unroll
     for (int j = 0; j < C::WMB; ++j) acc[i][j] = f32x16{};
 
-  const int nkt = (nkb + 1) >> 1;
-  u32x4 rw[C::A_PER_T];
-  // weights of step kt -> registers (K block kb + 1 may not exist on the last step)
-  auto a_load = [&](int kt) {
-    const int kb = kt * 2;
-    const bool full = kb + 1 < nkb;
+  // the loads of step kt into stage st: weights, then activations
+  auto load_a = [&](int kt, int st) __attribute__((always_inline)) {
+    uint16_t* base = lds + st * C::STAGE_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i)
-      rw[i] = ((i & 1) == 0 || full) ? ld16(wbase + woff[i] + kb * 512) : u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_global_load_lds((gptr_t)(wsrc[i] + kt * 512),
+                                       (lptr_t)(base + (C::W * i + wave) * 512), 16, 0, 0);
   };
-  // registers -> LDS stage, bf16 -> fp16, re-cut into 32 x 16 fragments
-  auto a_store = [&](int stage) {
-    uint16_t* sA = lds + stage * C::STAGE_ELEMS;
+  auto load_b = [&](int kt, int st) __attribute__((always_inline)) {
+    uint16_t* base = lds + st * C::STAGE_ELEMS + C::A_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      u32x4 h;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(rw[i][j]);
-      *reinterpret_cast<u32x4*>(&sA[wdst[i]]) = h;
-    }
+    for (int i = 0; i < C::B_PER_T; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(asrc[i] + kt * 1024),
+                                       (lptr_t)(base + (C::W * i + wave) * 512), 16, 0, 0);
   };
-  // activations of step kt -> LDS stage directly; a missing last K block
-  // (fragments q = 2, 3) is zero-filled from registers instead
-  auto b_load = [&](int kt, int stage) {
-    const int kb = kt * 2;
-    const bool full = kb + 1 < nkb;
-    uint16_t* sB = lds + stage * C::STAGE_ELEMS + C::A_ELEMS;
+  auto load_step = [&](int kt, int st) __attribute__((always_inline)) {
+    load_a(kt, st);
+    load_b(kt, st);
+  };
+
+  u32x4 fa[2][C::WNB], fb[2][C::WMB];
+  auto frag_load = [&](int buf, int st, int q) __attribute__((always_inline)) {
+    const uint16_t* base = lds + st * C::STAGE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      const int f = C::W * i + wave;
-      uint16_t* dst = &sB[f * 512];
-      if ((f & 3) < 2 || full)
-        __builtin_amdgcn_global_load_lds((gptr_t)(abase + aoff[i] + kb * 32), (lptr_t)dst, 16, 0, 0);
-      else
-        *reinterpret_cast<u32x4*>(dst + lane * 8) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::WNB; ++i)
+      fa[buf][i] = *reinterpret_cast<const u32x4*>(
+          &base[a_rd + (wn * C::WNB + i) * 1024 + q * 256]);
+#pragma unroll
+    for (int j = 0; j < C::WMB; ++j)
+      fb[buf][j] = *reinterpret_cast<const u32x4*>(
+          &base[b_rd + ((wm * C::WMB + j) * 2 + q) * 512]);
+  };
+  // weight fragments bf16 -> fp16 in place (after their LDS reads land)
+  auto convert = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WNB; ++i) fa[buf][i] = bf16x8_to_f16x8(fa[buf][i]);
+  };
+  auto mma = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::WNB; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WMB; ++j) acc[i][j] = mfma32_f16(fa[buf][i], fb[buf][j], acc[i][j]);
+  };
+  // Interleave within one sub-step: the first MFMAs are each followed by a
+  // fragment read of the other register set, the later ones by the
+  // conversions of those fragments, and the NL loads are spread evenly over
+  // the sub-step, so everything issues in the matrix pipe's shadow and the
+  // four waves of a CU do not hand the address unit their loads in bursts.
+  auto interleave = [&](auto n_vmem_c) __attribute__((always_inline)) {
+    constexpr int NL = decltype(n_vmem_c)::value, NR = C::WNB + C::WMB;
+    constexpr int NMF = C::WNB * C::WMB, NV = C::WNB * 12, HALF = NMF / 2;
+    constexpr int LSTRIDE = NL > 0 ? (NMF / NL > 0 ? NMF / NL : 1) : NMF;
+#pragma unroll
+    for (int g = 0; g < NMF; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // MFMA
+      if (g < NR) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
+      if (NL > 0 && g % LSTRIDE == 0 && g / LSTRIDE < NL)
+        __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);             // VMEM read
+      if (g >= HALF)
+        __builtin_amdgcn_sched_group_barrier(0x0002, (NV + HALF - 1) / HALF, 0);  // VALU
     }
   };
 
-  // prologue: stage 0 <- step 0; registers <- weights of step 1
-  a_load(0);
-  b_load(0, 0);
-  a_store(0);
-  if (nkt > 1) a_load(1);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  // prologue: steps 0..3 -> stages 0..3; wait for step 0; its first fragments
+  const int npre = nkt < 4 ? nkt : 4;
+  for (int s = 0; s < npre; ++s) load_step(s, s);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
+  frag_load(0, 0, 0);
+  convert(0);
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    // stage nxt was released by the last barrier: fill it for step kt+1 while
-    // this step computes; the weights of step kt+2 start loading right away
-    if (kt + 1 < nkt) {
-      a_store(nxt);
-      if (kt + 2 < nkt) a_load(kt + 2);
-      b_load(kt + 1, nxt);
-    }
-    const uint16_t* sA = lds + cur * C::STAGE_ELEMS;
-    const uint16_t* sB = sA + C::A_ELEMS;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 af[C::WNB], bf[C::WMB];
-#pragma unroll
-      for (int i = 0; i < C::WNB; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&sA[frag_at(wn * C::WNB + i, q) * 512 + lane * 8]);
-#pragma unroll
-      for (int j = 0; j < C::WMB; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(&sB[frag_at(wm * C::WMB + j, q) * 512 + lane * 8]);
-#pragma unroll
-      for (int i = 0; i < C::WNB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::WMB; ++j) acc[i][j] = mfma32_f16(af[i], bf[j], acc[i][j]);
-    }
-    // stage nxt complete (direct loads and this wave's writes) before the barrier
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  // steady state: step kt computes from stage kt % 5 while step kt+4 loads
+  // into stage (kt+4) % 5, which step kt-1 released at its barrier
+  // Step kt+4's weights load during the first sub-step and its activations
+  // during the second, so at the barrier (between them) the loads issued
+  // after step kt+1's are those of steps kt+2, kt+3 and kt+4's weights.
+  int kt = 0, st = 0;
+  for (; kt + 4 < nkt; ++kt) {
+    const int st1 = st == 4 ? 0 : st + 1, st4 = st == 0 ? 4 : st - 1;
+#ifndef FMLP_EXP_NOLOAD
+    load_a(kt + 4, st4);
+#endif
+    frag_load(1, st, 1);
+    mma(0);
+    convert(1);
+    interleave(std::integral_constant<int, C::A_PER_T>{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T + C::A_PER_T));
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#ifndef FMLP_EXP_NOLOAD
+    load_b(kt + 4, st4);
+#endif
+    frag_load(0, st1, 0);
+    mma(1);
+    convert(0);
+    interleave(std::integral_constant<int, C::B_PER_T>{});
+    __builtin_amdgcn_sched_barrier(0);
+    st = st1;
+  }
+  // the last (up to 4) steps: nothing left to load
+  for (; kt < nkt; ++kt) {
+    const int st1 = st == 4 ? 0 : st + 1;
+    const int behind = nkt - 2 - kt;  // steps after kt+1 whose loads may be in flight
+    frag_load(1, st, 1);
+    mma(0);
+    convert(1);
+    if (behind >= 2)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T));
+    else if (behind == 1)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(C::LD_PER_T));
+    else
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    __builtin_amdgcn_s_barrier();
+    // (one copy of each MFMA group: accumulators that flow through
+    // duplicated MFMAs in branches get split across register files)
+    const bool more = kt + 1 < nkt;
+    if (more) frag_load(0, st1, 0);
+    mma(1);
+    if (more) convert(0);
+    st = st1;
   }
 
   // epilogue: lane holds token t = col of block (i, j) and rows 8r + 4 grp + e
@@ -270,21 +374,40 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_wf16(const uint16_t* __
           const _Float16 a1 = (_Float16)silu_mul(v2, v3);
           const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                                   ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-          *reinterpret_cast<uint32_t*>(out + (int64_t)t * (N / 2) + f0 / 2) = packed;
-        } else {
-          uint32_t* dst = reinterpret_cast<uint32_t*>(out + (int64_t)t * N + f0);
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) +
+                                       act_tile_off(t, f0 / 2, N / 2)) = packed;
+        } else if (EPI == EPI_STORE_BF16) {
+          uint32_t* dst =
+              reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (int64_t)t * N + f0);
           dst[0] = pack_bf16_rne(v0, v1);
           dst[1] = pack_bf16_rne(v2, v3);
+        } else {
+          float* dst = static_cast<float*>(out) + ((int64_t)blockIdx.y * M + t) * N + f0;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
         }
       }
     }
   }
 }
 
-// Launch one GEMM with a given block tile and wave grid.
+// y = bf16(sum over the split-K partials, in slice order): deterministic.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part,
+                                                       uint16_t* __restrict__ y, int64_t n4,
+                                                       int splits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4 outputs per thread
+  if (i >= n4) return;
+  f32x4 s = reinterpret_cast<const f32x4*>(part)[i];
+  for (int z = 1; z < splits; ++z) s += reinterpret_cast<const f32x4*>(part + z * n4 * 4)[i];
+  uint32_t* dst = reinterpret_cast<uint32_t*>(y + i * 4);
+  dst[0] = pack_bf16_rne(s[0], s[1]);
+  dst[1] = pack_bf16_rne(s[2], s[3]);
+}
+
+// Launch one GEMM with a given block tile and wave grid (splits > 1 only
+// with the fp32 partial epilogue).
 template <int NB, int MB, int WGN, int WGM, int EPI>
-static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, uint16_t* out, int M,
-                                int N, int K, hipStream_t stream) {
+static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
+                                int K, int splits, hipStream_t stream) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -296,55 +419,104 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, uint16_t
   if (attr_err != hipSuccess) return attr_err;
   const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
-                k_gemm_wf16<NB, MB, WGN, WGM, EPI>, dim3(tiles), dim3(C::THREADS),
+                k_gemm_wf16<NB, MB, WGN, WGM, EPI>, dim3(tiles, splits), dim3(C::THREADS),
                 (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K);
   return hipGetLastError();
 }
 
-// Estimated cost of a tile choice: waves of workgroups (one workgroup per CU
-// for the large tiles, two for 128 x 128) times the time of one tile, which
-// grows with its area and with the workgroups sharing a CU, discounted by how
-// well the tile size feeds the matrix cores.
-static double gemm_cost(int M, int N, int bn, int bm, double eff, int per_cu) {
-  const int tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
-  const int slots = 256 * per_cu;
-  const int waves = (tiles + slots - 1) / slots;
-  return (double)waves * bn * bm * per_cu / eff;
+// Tile shapes: 0 = 256 x 256 (2 x 2 waves), 1 = 256 x 128 (4 x 1), 2 = 128 x 128 (2 x 2).
+struct GemmPlan {
+  int shape, splits;
+};
+
+// Time model of one GEMM (microseconds): rounds of workgroups over the CUs
+// times the time of one workgroup at the per-CU rate measured for its shape
+// on MI355X (prefill GEMMs of Llama-8B-shaped layers), plus, for split K,
+// writing and re-reading the fp32 partials and the reduction launch.
+static double gemm_time_us(int M, int N, int K, int shape, int splits) {
+  static const int bn[3] = {256, 256, 128}, bm[3] = {256, 128, 128}, per_cu[3] = {1, 1, 2};
+  // TFLOP/s per CU with one workgroup on it, and with per_cu of them
+  static const double rate1[3] = {4.3, 3.7, 2.6}, rate_full[3] = {4.3, 3.7, 3.2};
+  const int64_t tiles =
+      (int64_t)((N + bn[shape] - 1) / bn[shape]) * ((M + bm[shape] - 1) / bm[shape]);
+  const int64_t wgs = tiles * splits, slots = 256 * per_cu[shape];
+  const int64_t rounds = (wgs + slots - 1) / slots;
+  const bool shared = wgs > 256 && per_cu[shape] > 1;  // several workgroups per CU
+  const double wg_flops = 2.0 * bn[shape] * bm[shape] * (double)K / splits;
+  double t = shared ? rounds * wg_flops * per_cu[shape] / (rate_full[shape] * 1e6)
+                    : rounds * wg_flops / (rate1[shape] * 1e6);
+  if (splits > 1) t += 2.0 * splits * (double)M * N * 4 / 5.0e6 + 3.0;
+  return t;
 }
 
-#ifndef FMLP_GEMM_TILE
-#define FMLP_GEMM_TILE 0  // 0: by cost; 1: 256x256 4 waves; 2: 128x256; 3: 128x128; 4: 256x256 8 waves
-#endif
+static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
+  GemmPlan best{0, 1};
+  double tb = 1e300;
+  for (int shape = 0; shape < 3; ++shape) {
+    for (int splits = 1; splits <= (may_split ? 8 : 1); splits *= 2) {
+      const int nkb = K >> 5;
+      if (nkb % splits != 0 || nkb / splits < 8) continue;
+      const double t = gemm_time_us(M, N, K, shape, splits);
+      if (t < tb) tb = t, best = GemmPlan{shape, splits};
+    }
+  }
+  return best;
+}
 
 template <int EPI>
-static hipError_t launch_gemm(const uint16_t* W, const uint16_t* Act, uint16_t* out, int M, int N,
-                              int K, hipStream_t stream) {
-  if (FMLP_GEMM_TILE == 1) return launch_gemm_t<8, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
-  if (FMLP_GEMM_TILE == 2) return launch_gemm_t<4, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
-  if (FMLP_GEMM_TILE == 3) return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, stream);
-  if (FMLP_GEMM_TILE == 4) return launch_gemm_t<8, 8, 2, 4, EPI>(W, Act, out, M, N, K, stream);
-  const double c256 = gemm_cost(M, N, 256, 256, 1.0, 1);
-  const double c128n = gemm_cost(M, N, 128, 256, 0.85, 1);
-  const double c128 = gemm_cost(M, N, 128, 128, 0.7, 2);
-  if (c256 <= c128n && c256 <= c128)
-    return launch_gemm_t<8, 8, 2, 4, EPI>(W, Act, out, M, N, K, stream);
-  if (c128n <= c128) return launch_gemm_t<4, 8, 2, 2, EPI>(W, Act, out, M, N, K, stream);
-  return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, stream);
+static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
+                                   void* out, int M, int N, int K, hipStream_t stream) {
+  if (g.shape == 0) return launch_gemm_t<8, 8, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream);
+  if (g.shape == 1) return launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream);
+  return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream);
+}
+
+#ifndef FMLP_GEMM_PLAN
+#define FMLP_GEMM_PLAN 0  // 0: by the time model; s*10 + k: shape s, k-way split of the down GEMM
+#endif
+
+static GemmPlan plan_down(int64_t M, int64_t d, int64_t ff) {
+  if (FMLP_GEMM_PLAN) return GemmPlan{FMLP_GEMM_PLAN / 10, FMLP_GEMM_PLAN % 10};
+  return plan_gemm((int)M, (int)d, (int)ff, true);
+}
+
+size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
+  // n fp16 [pad32(M), d] and a fp16 [pad32(M), ff], both fragment-tiled;
+  // r fp32 [M]; the down projection's split-K partials fp32 [splits, M, d]
+  const int splits = plan_down(M, d, ff).splits;
+  return align256((size_t)pad32(M) * d * 2) + align256((size_t)pad32(M) * ff * 2) +
+         align256((size_t)M * 4) + (splits > 1 ? align256((size_t)splits * M * d * 4) : 0);
 }
 
 hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   if (p.wtype != 0) return hipErrorNotSupported;
   uint16_t* n = reinterpret_cast<uint16_t*>(p.ws);
-  uint16_t* a = reinterpret_cast<uint16_t*>(p.ws + align256((size_t)p.M * p.d * 2));
-  launch_kernel(KK_RMS_PREP, k_rms_prep_f16, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps,
-                n, p.d);
+  uint16_t* a = reinterpret_cast<uint16_t*>(p.ws + align256((size_t)pad32(p.M) * p.d * 2));
+  float* r = reinterpret_cast<float*>(p.ws + align256((size_t)pad32(p.M) * p.d * 2) +
+                                     align256((size_t)pad32(p.M) * p.ff * 2));
+  launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
+                p.x, p.eps, r, (int)p.M, (int)p.d);
+  const int64_t slots = pad32(p.M) * p.d / 8;
+  launch_kernel(KK_RMS_TILE, k_rms_tile, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
+                stream, p.x, p.gamma, r, n, (int)p.M, (int)p.d, slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_gemm<EPI_SILU_MUL_F16>(reinterpret_cast<const uint16_t*>(p.w_gu), n, a, p.M, 2 * p.ff,
-                                    p.d, stream);
+  const GemmPlan g1 = plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false);
+  e = launch_gemm_plan<EPI_SILU_MUL_F16>(g1, reinterpret_cast<const uint16_t*>(p.w_gu), n, a,
+                                         (int)p.M, (int)(2 * p.ff), (int)p.d, stream);
   if (e != hipSuccess) return e;
-  return launch_gemm<EPI_STORE_BF16>(reinterpret_cast<const uint16_t*>(p.w_down), a, p.y, p.M,
-                                     p.d, p.ff, stream);
+  const GemmPlan g2 = plan_down(p.M, p.d, p.ff);
+  if (g2.splits == 1)
+    return launch_gemm_plan<EPI_STORE_BF16>(g2, reinterpret_cast<const uint16_t*>(p.w_down), a,
+                                            p.y, (int)p.M, (int)p.d, (int)p.ff, stream);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(r) + align256((size_t)p.M * 4));
+  e = launch_gemm_plan<EPI_STORE_F32>(g2, reinterpret_cast<const uint16_t*>(p.w_down), a, part,
+                                      (int)p.M, (int)p.d, (int)p.ff, stream);
+  if (e != hipSuccess) return e;
+  const int64_t n4 = p.M * p.d / 4;
+  launch_kernel(KK_SPLITK_REDUCE, k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                stream, part, p.y, n4, g2.splits);
+  return hipGetLastError();
 }
 
 }  // namespace fmlp

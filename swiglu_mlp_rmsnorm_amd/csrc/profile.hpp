@@ -22,6 +22,8 @@ enum KernelKind {
   KK_RMS_PREP,
   KK_GEMM_GATEUP,
   KK_GEMM_DOWN,
+  KK_RMS_TILE,
+  KK_SPLITK_REDUCE,
   KK_COUNT
 };
 
