@@ -88,9 +88,11 @@ def test_workspace_size():
     assert ws(32, 4096, 14336) >= ws(1, 4096, 14336)
     assert ws(2048, 4096, 14336) >= 2 * 2048 * (4096 + 14336)
     assert ws(1, 48, 704) == 0 and ws(-1, 256, 704) == 0 and ws(1, 256, 704, 5) == 0
-    # exactly the reported size is accepted by the host-side checks
+    # the reported size covers either path; at M=1 the prefill path (tokens
+    # padded to 32) is the larger, so one byte under it (beyond the 256-byte
+    # alignment slack) is rejected there
     need = ws(1, 256, 704)
-    assert fwd(ws_bytes=need - 256 - 1) == F.FMLP_ERR_WORKSPACE
+    assert fwd(ws_bytes=need - 256 - 1, path=F.FMLP_PATH_PREFILL) == F.FMLP_ERR_WORKSPACE
 
 
 def test_pack_quant_dequant_validation():
