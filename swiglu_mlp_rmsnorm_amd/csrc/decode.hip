@@ -61,6 +61,15 @@
 #ifndef FMLP_Q4_P
 #define FMLP_Q4_P 1   // int4 ring depth (super-tiles of 4 groups)
 #endif
+#ifndef FMLP_Q4_GU_RB
+#define FMLP_Q4_GU_RB 2  // int4 gate/up row blocks per workgroup
+#endif
+#ifndef FMLP_DN_RB
+#define FMLP_DN_RB 1     // down row blocks per workgroup (bf16)
+#endif
+#ifndef FMLP_Q4_DN_RB
+#define FMLP_Q4_DN_RB 2  // down row blocks per workgroup (int4)
+#endif
 
 namespace fmlp {
 
@@ -393,25 +402,26 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
 }
 
 // ------------------------------------------------------------ down kernel
-// Workgroup: one block of 16 W_down rows, S waves split K = ff.
-template <int WK, int NCB, int S, int P>
+// Workgroup: RB blocks of 16 W_down rows, S waves split K = ff.
+template <int WK, int NCB, int RB, int S, int P>
 __global__ __launch_bounds__(64 * S) void k_decode_down(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ a0,
     const uint16_t* __restrict__ a1, uint16_t* __restrict__ y, int M, int d, int ff) {
-  __shared__ f32x4 red[S * NCB * 64];
-  const int64_t rb0 = blockIdx.x;
-  f32x4 acc[1][NCB];
+  __shared__ f32x4 red[S * RB * NCB * 64];
+  const int64_t rb0 = (int64_t)blockIdx.x * RB;
+  f32x4 acc[RB][NCB];
   float ss[NCB];
-  gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, 1, S, P>(w, sc, a0, a1, rb0, ff, M, acc, ss);
-  stash<1, NCB>(red, acc);
+  gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, RB, S, P>(w, sc, a0, a1, rb0, ff, M, acc, ss);
+  stash<RB, NCB>(red, acc);
   __syncthreads();
-  for (int o = threadIdx.x; o < 16 * M; o += 64 * S) {
-    const int rl = o & 15, t = o >> 4;
+  for (int o = threadIdx.x; o < RB * 16 * M; o += 64 * S) {
+    const int rl = o % (RB * 16), t = o / (RB * 16);
+    const int rb = rl >> 4, r = rl & 15;
     const int cb = t >> 4, c = t & 15;
-    const int L = (c >> 2) * 16 + rl, e = c & 3;
+    const int L = (c >> 2) * 16 + r, e = c & 3;
     float sum = 0.f;
 #pragma unroll
-    for (int s = 0; s < S; ++s) sum += red[(s * NCB + cb) * 64 + L][e];
+    for (int s = 0; s < S; ++s) sum += red[((s * RB + rb) * NCB + cb) * 64 + L][e];
     y[(int64_t)t * d + rb0 * 16 + rl] = bf16_rne(sum);
   }
 }
@@ -421,9 +431,11 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
 template <int WK, int NCB>
 static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const DecodeWs ws = decode_ws(p);
-  constexpr int RB = (NCB == 1) ? FMLP_GU_RB : (FMLP_GU_RB > 2 ? 2 : FMLP_GU_RB);
+  constexpr int GRB = WK == WK_INT4 ? FMLP_Q4_GU_RB : FMLP_GU_RB;
+  constexpr int RB = (NCB == 1) ? GRB : (GRB > 2 ? 2 : GRB);
   constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
   constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
+  constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
   hipError_t e;
   if constexpr (WK == WK_INT4) {
     launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps,
@@ -433,14 +445,23 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
   const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
+  // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
   launch_kernel(WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16,
                 k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP>, dim3((2 * p.ff) / (16 * RB)),
                 dim3(64 * FMLP_GU_S), 0, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1,
                 p.M, p.d, p.ff);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
-                k_decode_down<WK, NCB, FMLP_DN_S, DP>, dim3(p.d / 16), dim3(64 * FMLP_DN_S), 0,
-                stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
+  // down: DRB row blocks per workgroup when they divide d and leave enough
+  // workgroups to cover the CUs, else one
+  if (DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256)
+    launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
+                  k_decode_down<WK, NCB, DRB, FMLP_DN_S, DP>, dim3(p.d / (16 * DRB)),
+                  dim3(64 * FMLP_DN_S), 0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M,
+                  p.d, p.ff);
+  else
+    launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
+                  k_decode_down<WK, NCB, 1, FMLP_DN_S, DP>, dim3(p.d / 16), dim3(64 * FMLP_DN_S),
+                  0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
   return hipGetLastError();
 }
 
