@@ -119,9 +119,10 @@ def kernel_source_sha(kernel):
 
 
 def measured_traffic(kernel, workload, M):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None
-    when there is none or the kernel source changed since it was taken."""
+    """HBM bytes per forward step of one kernel kind, from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE of its dispatches,
+    scaled by the copy-kernel calibration), or None when there is none or the
+    kernel source changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}_M{M}.txt")
     if not os.path.exists(path):
         return None
@@ -133,7 +134,7 @@ def measured_traffic(kernel, workload, M):
     if kv.get("source_sha") != kernel_source_sha(kernel):
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv["traffic_bytes_per_step"])
     except (KeyError, ValueError):
         return None
 
@@ -247,7 +248,10 @@ def run_one(wname, M, steps, warmup, args):
             step(i)
         torch.cuda.synchronize()
         for name, (n, ms) in F.fmlp_profile_read().items():
-            kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+            # a kernel kind may launch more than once per step (the gate/up
+            # GEMM's tail launch): rates below use its time per step
+            kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n,
+                             "launches_per_step": n / steps, "us_per_step": ms * 1e3 / steps}
         F.fmlp_profile_enable(False)
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
@@ -259,21 +263,25 @@ def run_one(wname, M, steps, warmup, args):
         dom = "gemm_gateup_silu_f16"
         dom_units = 2.0 * M * (2 * ff) * d
         unit, peak, bound = "TFLOP/s", MFMA_PEAK_TFLOPS, "mfma"
+    # the dominant kernel's algorithmic units and time per step (its launches
+    # in one step together: one for decode, one or two for the gate/up GEMM)
     roofline = None
     if dom in kernels:
-        avg_s = kernels[dom]["avg_us"] * 1e-6
-        achieved = dom_units / avg_s / (1e9 if unit == "GB/s" else 1e12)
+        step_s = kernels[dom]["us_per_step"] * 1e-6
+        achieved = dom_units / step_s / (1e9 if unit == "GB/s" else 1e12)
         roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                     "unit": unit, "frac": round(achieved / peak, 4),
-                    "units_per_launch": dom_units,
+                    "units_per_step": dom_units,
+                    "launches_per_step": kernels[dom]["launches_per_step"],
                     "traffic": measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
+        t = k["us_per_step"]
         if name.startswith("decode") or name == "act_prep":
-            k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (k["avg_us"] * 1e3), 1)
+            k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (t * 1e3), 1)
         elif name == "gemm_gateup_silu_f16":
-            k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (k["avg_us"] * 1e6), 1)
+            k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (t * 1e6), 1)
         elif name == "gemm_down_f16":
-            k["tflop_per_s"] = round(2.0 * M * ff * d / (k["avg_us"] * 1e6), 1)
+            k["tflop_per_s"] = round(2.0 * M * ff * d / (t * 1e6), 1)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -69,11 +69,13 @@ def pmc(args):
     copy_w = statistics.median(_counter(args.copy_write, "WRITE_SIZE", args.copy_match))
     k_f = _counter(args.fetch, "FETCH_SIZE", args.match)
     k_w = _counter(args.write, "WRITE_SIZE", args.match)
-    # counters are KiB per dispatch; the copy moves copy_bytes each way
+    # counters are KiB per dispatch; the copy moves copy_bytes each way. A
+    # kernel kind may dispatch more than once per forward step: traffic is
+    # summed over the run's dispatches and divided by its steps.
     fetch_scale = args.copy_bytes / (copy_f * 1024.0)
     write_scale = args.copy_bytes / (copy_w * 1024.0)
-    fetch_b = statistics.median(k_f) * 1024.0 * fetch_scale
-    write_b = statistics.median(k_w) * 1024.0 * write_scale
+    fetch_b = sum(k_f) * 1024.0 * fetch_scale / args.steps
+    write_b = sum(k_w) * 1024.0 * write_scale / args.steps
     traffic = fetch_b + write_b
     sha = kernel_source_sha(args.kernel)
     lines = [
@@ -81,15 +83,16 @@ def pmc(args):
         f"kernel: {args.kernel}",
         f"kernel_match: {args.match}",
         f"source_sha: {sha}",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
-        f"fetch_bytes_per_launch: {fetch_b:.0f}",
-        f"write_bytes_per_launch: {write_b:.0f}",
-        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_bytes_per_step: {traffic:.0f}",
+        f"fetch_bytes_per_step: {fetch_b:.0f}",
+        f"write_bytes_per_step: {write_b:.0f}",
+        f"algorithmic_bytes_per_step: {alg}",
+        f"steps_in_run: {args.steps}",
         f"traffic_over_algorithmic: {traffic / alg:.4f}",
         f"dispatches_fetch: {len(k_f)}",
         f"dispatches_write: {len(k_w)}",
-        f"fetch_kib_median: {statistics.median(k_f):.1f}",
-        f"write_kib_median: {statistics.median(k_w):.1f}",
+        f"fetch_kib_per_dispatch: {' '.join(f'{v:.0f}' for v in k_f)}",
+        f"write_kib_per_dispatch: {' '.join(f'{v:.0f}' for v in k_w)}",
         f"copy_bytes: {args.copy_bytes}",
         f"copy_fetch_kib: {copy_f:.1f}",
         f"copy_write_kib: {copy_w:.1f}",
@@ -122,6 +125,8 @@ def main():
     p.add_argument("--copy-match", default=".")
     p.add_argument("--copy-bytes", type=int, required=True)
     p.add_argument("--M", type=int, required=True)
+    p.add_argument("--steps", type=int, required=True,
+                   help="forward steps in the counted run (bench.py warmup + steps)")
     args = ap.parse_args()
     {"ktrace": ktrace, "pmc": pmc}[args.mode](args)
 

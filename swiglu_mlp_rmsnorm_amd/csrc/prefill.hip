@@ -153,7 +153,7 @@ struct GemmCfg {
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * 2;
   // one wave per SIMD when the accumulators alone fill 256 registers
   static constexpr int WAVES_PER_EU = (WNB * WMB >= 16) ? 1 : 2;
-  static_assert(W == 4 && WNB >= 1 && WMB >= 1 && A_PER_T * W == NB * 2 &&
+  static_assert((W == 4 || W == 8) && WNB >= 1 && WMB >= 1 && A_PER_T * W == NB * 2 &&
                 B_PER_T * W == MB * 2, "tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(3 * LD_PER_T < 64, "vmcnt field");
@@ -176,10 +176,10 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
 }
 
 template <int NB, int MB, int WGN, int WGM, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+__global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
     GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
 k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
-            void* __restrict__ out, int M, int N, int K) {
+            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -187,14 +187,15 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int wn = wave % C::WGN, wm = wave / C::WGN;
 
-  const int nN = (N + C::BN - 1) / C::BN, nM = (M + C::BM - 1) / C::BM;
+  // this launch covers feature rows n_begin .. n_end-1 of the N
+  const int nN = (n_end - n_begin + C::BN - 1) / C::BN, nM = (M + C::BM - 1) / C::BM;
   const int T = nN * nM;
   const int pid = blockIdx.x;
   const int xcd = pid & 7, idx = pid >> 3;
   const int per = T >> 3, rem = T & 7;
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int tn = tile / nM, tm = tile % nM;
-  const int n0 = tn * C::BN, m0 = tm * C::BM;
+  const int n0 = n_begin + tn * C::BN, m0 = tm * C::BM;
   // split K: slice blockIdx.y of gridDim.y equal slices of 32-column blocks
   const int nkb = K >> 5, nrb = N >> 4;
   const int nkt = nkb / (int)gridDim.y, kbeg = (int)blockIdx.y * nkt;
@@ -366,7 +367,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int f0 = n0 + (wn * C::WNB + i) * 32 + 8 * r + 4 * grp;
-        if (f0 >= N) continue;
+        if (f0 >= n_end) continue;
         const float v0 = acc[i][j][4 * r], v1 = acc[i][j][4 * r + 1];
         const float v2 = acc[i][j][4 * r + 2], v3 = acc[i][j][4 * r + 3];
         if (EPI == EPI_SILU_MUL_F16) {
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // with the fp32 partial epilogue).
 template <int NB, int MB, int WGN, int WGM, int EPI>
 static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
-                                int K, int splits, hipStream_t stream) {
+                                int K, int splits, hipStream_t stream, int n_begin, int n_end) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -417,16 +418,19 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
-  const int tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+  const int tiles = ((n_end - n_begin + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
                 k_gemm_wf16<NB, MB, WGN, WGM, EPI>, dim3(tiles, splits), dim3(C::THREADS),
-                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K);
+                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end);
   return hipGetLastError();
 }
 
-// Tile shapes: 0 = 256 x 256 (2 x 2 waves), 1 = 256 x 128 (4 x 1), 2 = 128 x 128 (2 x 2).
+// Tile shapes: 0 = 256 x 256 (8 waves, 4 x 2), 1 = 256 x 128 (4 waves, 4 x 1),
+// 2 = 128 x 128 (4 waves, 2 x 2). tail_rows > 0: the last tail_rows feature
+// rows run as a second launch of 256 x 128 tiles, so that a last round of
+// 256 x 256 tiles that would leave CUs idle becomes one round of half tiles.
 struct GemmPlan {
-  int shape, splits;
+  int shape, splits, tail_rows = 0;
 };
 
 // Time model of one GEMM (microseconds): rounds of workgroups over the CUs
@@ -466,9 +470,30 @@ static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
 template <int EPI>
 static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
                                    void* out, int M, int N, int K, hipStream_t stream) {
-  if (g.shape == 0) return launch_gemm_t<8, 8, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream);
-  if (g.shape == 1) return launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream);
-  return launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream);
+  const int n_main = N - g.tail_rows;
+  hipError_t e = hipSuccess;
+  if (n_main > 0) {
+    if (g.shape == 0)
+      e = launch_gemm_t<8, 8, 4, 2, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+    else if (g.shape == 1)
+      e = launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+    else
+      e = launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+  }
+  if (e != hipSuccess || g.tail_rows == 0) return e;
+  return launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream, n_main, N);
+}
+
+// Split off a tail launch when the 256 x 256 tiles fill r >= 1 whole rounds
+// of the 256 CUs and then at most half a round: the leftover bands of 256
+// rows run as 256 x 128 tiles, at most one round of them.
+static GemmPlan with_tail(GemmPlan g, int M, int N) {
+  if (g.shape != 0 || g.splits != 1 || N % 256 != 0) return g;
+  const int bands = N / 256, nM = (M + 255) / 256, tiles = bands * nM;
+  const int full = tiles / 256, left = tiles % 256;
+  if (full < 1 || left == 0 || left > 128 || left % nM != 0) return g;
+  g.tail_rows = (left / nM) * 256;
+  return g;
 }
 
 #ifndef FMLP_GEMM_PLAN
@@ -501,7 +526,8 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
                 stream, p.x, p.gamma, r, n, (int)p.M, (int)p.d, slots);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const GemmPlan g1 = plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false);
+  const GemmPlan g1 =
+      with_tail(plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false), (int)p.M, (int)(2 * p.ff));
   e = launch_gemm_plan<EPI_SILU_MUL_F16>(g1, reinterpret_cast<const uint16_t*>(p.w_gu), n, a,
                                          (int)p.M, (int)(2 * p.ff), (int)p.d, stream);
   if (e != hipSuccess) return e;

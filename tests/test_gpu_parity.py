@@ -129,7 +129,7 @@ def test_both_paths_at_the_crossover(tiny, M, path):
 
 @pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 40), (512, 1376, 5),
                                     (512, 1376, 70), (160, 224, 17), (256, 4096, 100),
-                                    (288, 2048, 33)])
+                                    (288, 2048, 33), (256, 38400, 33)])
 def test_odd_shapes(d, ff, M):
     layer = Bf16Layer(d, ff, 20 + d)
     x, g = bf16_inputs(M, d, 400 + M)
