@@ -64,6 +64,9 @@
 #ifndef FMLP_Q4_GU_RB
 #define FMLP_Q4_GU_RB 2  // int4 gate/up row blocks per workgroup
 #endif
+#ifndef FMLP_DN_SPLIT_S
+#define FMLP_DN_SPLIT_S 8  // waves per workgroup of a K-split down launch
+#endif
 #ifndef FMLP_DN_RB
 #define FMLP_DN_RB 1     // down row blocks per workgroup (bf16)
 #endif
@@ -77,20 +80,48 @@ enum { WK_BF16 = 0, WK_INT4 = 1 };
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Down-projection split along K (see k_decode_down): with d/16 row blocks,
+// split each into k slices when that spreads the work more evenly over the
+// 256 CUs (time ~ rounds of workgroups / k), keeping at least min_units K
+// units per slice; at most kMaxSplit.
+constexpr int kMaxSplit = 4;
+static int down_splits(int64_t d, int64_t ff, bool int4) {
+#ifdef FMLP_DN_SPLIT
+  return FMLP_DN_SPLIT;
+#endif
+  const int64_t blocks = d / 16, nu = int4 ? (ff + 127) / 128 : ff / 32;
+  const int64_t min_units = int4 ? 4 : 16;
+  int best = 1;
+  double tb = (double)((blocks + 255) / 256);
+  for (int k = 2; k <= kMaxSplit; ++k) {
+    if (nu / k < min_units) break;
+    const double t = (double)((blocks * k + 255) / 256) / k;
+    if (t < tb - 1e-9) tb = t, best = k;
+  }
+  return best;
+}
+
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
-  // n fp16 [M, d] (int4 only); a: bf16 hi + lo [M, ff] (int4: fp16 in the first half)
-  return align256((size_t)M * d * 2) + 2 * align256((size_t)M * ff * 2);
+  // n fp16 [M, d] (int4 only); a: bf16 hi + lo [M, ff] (int4: fp16 in the
+  // first half); split-K partials fp32 [kMaxSplit, M, d]; counters [d/16]
+  return align256((size_t)M * d * 2) + 2 * align256((size_t)M * ff * 2) +
+         align256((size_t)kMaxSplit * M * d * 4) + align256((size_t)(d / 16) * 4);
 }
 
 struct DecodeWs {
   uint16_t *n0, *a0, *a1;
+  float* part;
+  int* cnt;
 };
 
 static DecodeWs decode_ws(const Problem& p) {
   const size_t nb = align256((size_t)p.M * p.d * 2), ab = align256((size_t)p.M * p.ff * 2);
+  const size_t pb = align256((size_t)kMaxSplit * p.M * p.d * 4);
   char* b = p.ws;
   return DecodeWs{reinterpret_cast<uint16_t*>(b), reinterpret_cast<uint16_t*>(b + nb),
-                  reinterpret_cast<uint16_t*>(b + nb + ab)};
+                  reinterpret_cast<uint16_t*>(b + nb + ab),
+                  reinterpret_cast<float*>(b + nb + 2 * ab),
+                  reinterpret_cast<int*>(b + nb + 2 * ab + pb)};
 }
 
 // ------------------------------------------------------------ int4 helpers
@@ -169,7 +200,8 @@ __global__ __launch_bounds__(256) void k_act_prep_q4(const uint16_t* __restrict_
 //   ACT_HL  : bf16 weights; act0 / act1 = hi / lo bf16 [M, K], natural order
 //   ACT_Q4  : int4 weights; act0 = fp16 [M, K] in the int4 slot order
 // Weights: bf16 tiles (1 KB per 16 x 32 block) or int4 super-tiles (1 KB per
-// 16 rows x 4 groups) + scales. Each wave walks K units wave, wave+S, ...
+// 16 rows x 4 groups) + scales. The K units u0 .. u0+ucnt-1 are covered;
+// each wave walks units u0+wave, u0+wave+S, ...
 // with a P-deep ring of weight tiles and activation chunks in flight.
 enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2 };
 
@@ -178,7 +210,8 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                                           const uint16_t* __restrict__ sc,
                                           const uint16_t* __restrict__ act0,
                                           const uint16_t* __restrict__ act1, int64_t rb0, int K,
-                                          int M, f32x4 (&acc)[RB][NCB], float (&ss)[NCB]) {
+                                          int M, int u0, int ucnt, f32x4 (&acc)[RB][NCB],
+                                          float (&ss)[NCB]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int jmax = M >= 4 ? 4 : M;
@@ -200,11 +233,11 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
   if constexpr (MODE != ACT_Q4) {
     // unit = one 32-column group
     const uint16_t* wt = static_cast<const uint16_t*>(w) + lane * 8;
-    const int nit = wave < nkb ? (nkb - wave + S - 1) / S : 0;
+    const int nit = wave < ucnt ? (ucnt - wave + S - 1) / S : 0;
     u32x4 wb[P][RB], hb[P][NCB], lb[P][NCB];
     u32x4 gb[P];
     auto issue = [&](int slot, int it) {
-      const int kb = wave + it * S;
+      const int kb = u0 + wave + it * S;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) wb[slot][rb] = ld16_stream(wt + ((rb0 + rb) * nkb + kb) * 512);
 #pragma unroll
@@ -262,12 +295,12 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
     const int nq = (K + 127) >> 7;
     const uint8_t* qt = static_cast<const uint8_t*>(w) + lane * 16;
     const uint16_t* stl = sc + col * 4;
-    const int nit = wave < nq ? (nq - wave + S - 1) / S : 0;
+    const int nit = wave < ucnt ? (ucnt - wave + S - 1) / S : 0;
     const u32x4 negoff = {kNegOffA, kNegOffB, kNegOffA, kNegOffB};
     u32x4 qb[P][RB], ab[P][4][NCB];
     uint64_t sb[P][RB];
     auto issue = [&](int slot, int it) {
-      const int q = wave + it * S;
+      const int q = u0 + wave + it * S;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int64_t st = (rb0 + rb) * nq + q;
@@ -289,7 +322,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
       for (int p = 0; p < P; ++p) {
         const int it = i0 + p;
         if (it < nit) {
-          const int q = wave + it * S;
+          const int q = u0 + wave + it * S;
           u32x4 qv[RB], av[4][NCB];
           uint64_t sv[RB];
 #pragma unroll
@@ -345,18 +378,24 @@ __device__ __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RB][NCB]) {
 // Writes a = a0 + a1 (bf16 hi/lo, natural order, [M, ff]).
 // int4: activations are the prepared fp16 n (ACT_Q4); writes a0 = fp16 a in
 // the int4 slot order, [M, ff].
+// Workgroup 0 also clears the down kernel's split-K arrival counters (ncnt of
+// them; agent-coherent stores, read by that kernel's atomics).
 template <int WK, int NCB, int RB, int S, int P>
 __global__ __launch_bounds__(64 * S) void k_decode_gateup(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ act0,
     const uint16_t* __restrict__ act1, float eps, uint16_t* __restrict__ a0,
-    uint16_t* __restrict__ a1, int M, int d, int ff) {
+    uint16_t* __restrict__ a1, int M, int d, int ff, int* __restrict__ cnt, int ncnt) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ncnt; i += 64 * S)
+      __hip_atomic_store(cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __shared__ f32x4 red[S * RB * NCB * 64];
   __shared__ float ssred[S * NCB * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
   f32x4 acc[RB][NCB];
   float ss[NCB];
-  gemv_core<WK == WK_BF16 ? ACT_X : ACT_Q4, NCB, RB, S, P>(w, sc, act0, act1, rb0, d, M, acc, ss);
+  gemv_core<WK == WK_BF16 ? ACT_X : ACT_Q4, NCB, RB, S, P>(
+      w, sc, act0, act1, rb0, d, M, 0, WK == WK_BF16 ? d >> 5 : (d + 127) >> 7, acc, ss);
   stash<RB, NCB>(red, acc);
   if (WK == WK_BF16) {
     // lanes col, col+16, col+32, col+48 hold the same token
@@ -402,16 +441,31 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
 }
 
 // ------------------------------------------------------------ down kernel
-// Workgroup: RB blocks of 16 W_down rows, S waves split K = ff.
+// Workgroup: RB blocks of 16 W_down rows, S waves split its K range.
+// gridDim.y > 1 splits K = ff across workgroups as well (for layers with
+// fewer 16-row blocks than CUs): slice ks of gridDim.y equal ranges of K
+// units. Each slice stores its fp32 partial sums with agent-coherent stores,
+// waits for them to complete and counts itself in on an agent-scope atomic;
+// the last of a block's slices to arrive reads all partials back (agent-
+// coherent loads) and writes y = bf16(sum over slices in slice order), so
+// the result does not depend on arrival order. No workgroup waits for
+// another.
 template <int WK, int NCB, int RB, int S, int P>
 __global__ __launch_bounds__(64 * S) void k_decode_down(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ a0,
-    const uint16_t* __restrict__ a1, uint16_t* __restrict__ y, int M, int d, int ff) {
+    const uint16_t* __restrict__ a1, uint16_t* __restrict__ y, int M, int d, int ff,
+    float* __restrict__ part, int* __restrict__ cnt) {
   __shared__ f32x4 red[S * RB * NCB * 64];
+  __shared__ int last;
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
+  const int splits = gridDim.y, ks = blockIdx.y;
+  const int nu = WK == WK_BF16 ? ff >> 5 : (ff + 127) >> 7;  // K units
+  const int per = (nu + splits - 1) / splits;
+  const int u0 = ks * per, ucnt = nu - u0 < per ? nu - u0 : per;
   f32x4 acc[RB][NCB];
   float ss[NCB];
-  gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, RB, S, P>(w, sc, a0, a1, rb0, ff, M, acc, ss);
+  gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, RB, S, P>(w, sc, a0, a1, rb0, ff, M, u0,
+                                                            ucnt > 0 ? ucnt : 0, acc, ss);
   stash<RB, NCB>(red, acc);
   __syncthreads();
   for (int o = threadIdx.x; o < RB * 16 * M; o += 64 * S) {
@@ -422,7 +476,29 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
     float sum = 0.f;
 #pragma unroll
     for (int s = 0; s < S; ++s) sum += red[((s * RB + rb) * NCB + cb) * 64 + L][e];
-    y[(int64_t)t * d + rb0 * 16 + rl] = bf16_rne(sum);
+    const int64_t yi = (int64_t)t * d + rb0 * 16 + rl;
+    if (splits == 1)
+      y[yi] = bf16_rne(sum);
+    else
+      __hip_atomic_store(part + (int64_t)ks * M * d + yi, sum, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (splits == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+  __syncthreads();
+  if (!last) return;
+  for (int o = threadIdx.x; o < RB * 16 * M; o += 64 * S) {
+    const int rl = o % (RB * 16), t = o / (RB * 16);
+    const int64_t yi = (int64_t)t * d + rb0 * 16 + rl;
+    float sum = 0.f;
+    for (int k = 0; k < splits; ++k)
+      sum += __hip_atomic_load(part + (int64_t)k * M * d + yi, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    y[yi] = bf16_rne(sum);
   }
 }
 
@@ -445,23 +521,31 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
   const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
+  // down: DRB row blocks per workgroup when they divide d and leave enough
+  // workgroups to cover the CUs; else one, split along K when that helps
+  const bool drb = DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
+  const int splits = drb ? 1 : down_splits(p.d, p.ff, WK == WK_INT4);
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
   launch_kernel(WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16,
                 k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP>, dim3((2 * p.ff) / (16 * RB)),
                 dim3(64 * FMLP_GU_S), 0, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1,
-                p.M, p.d, p.ff);
+                p.M, p.d, p.ff, ws.cnt, splits > 1 ? (int)(p.d / 16) : 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // down: DRB row blocks per workgroup when they divide d and leave enough
-  // workgroups to cover the CUs, else one
-  if (DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256)
+  if (drb)
     launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
                   k_decode_down<WK, NCB, DRB, FMLP_DN_S, DP>, dim3(p.d / (16 * DRB)),
                   dim3(64 * FMLP_DN_S), 0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M,
-                  p.d, p.ff);
-  else
+                  p.d, p.ff, ws.part, ws.cnt);
+  else if (splits == 1)
     launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
                   k_decode_down<WK, NCB, 1, FMLP_DN_S, DP>, dim3(p.d / 16), dim3(64 * FMLP_DN_S),
-                  0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff);
+                  0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff, ws.part,
+                  ws.cnt);
+  else  // split slices are short: 8 waves each, so that more of them are resident per CU
+    launch_kernel(WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16,
+                  k_decode_down<WK, NCB, 1, FMLP_DN_SPLIT_S, DP>, dim3(p.d / 16, splits),
+                  dim3(64 * FMLP_DN_SPLIT_S), 0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y,
+                  p.M, p.d, p.ff, ws.part, ws.cnt);
   return hipGetLastError();
 }
 

@@ -136,6 +136,17 @@ def test_odd_shapes(d, ff, M):
     assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"d={d} ff={ff} M={M}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 17, 32])
+def test_decode_split_down(M):
+    # d/16 = 64 row blocks on 256 CUs: the down projection splits K four ways
+    # across workgroups and the last slice to arrive sums the partials
+    layer = Bf16Layer(1024, 2048, 77)
+    x, g = bf16_inputs(M, 1024, 700 + M)
+    y1 = layer.forward(x, g, EPS)
+    assert_parity(y1, layer.oracle(x, g, EPS), f"split down M={M}")
+    assert torch.equal(y1.view(torch.int16), layer.forward(x, g, EPS).view(torch.int16))
+
+
 @pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 5), (F.FMLP_PATH_PREFILL, 70)])
 def test_zero_weight_and_zero_input_cases(tiny, path, M):
     x, g = bf16_inputs(M, TINY_D, 9)
@@ -186,7 +197,8 @@ def test_decode_int4_ragged(M):
     assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 M={M}")
 
 
-@pytest.mark.parametrize("d,ff,M", [(128, 128, 1), (384, 640, 7), (256, 1024, 32)])
+@pytest.mark.parametrize("d,ff,M", [(128, 128, 1), (384, 640, 7), (256, 1024, 32), (1024, 2048, 1),
+                                    (1024, 2048, 20)])
 def test_decode_int4_shapes(d, ff, M):
     layer = Int4Layer(d, ff, 40 + d)
     x, g = bf16_inputs(M, d, 550 + M)
