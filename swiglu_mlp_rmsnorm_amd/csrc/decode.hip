@@ -146,49 +146,78 @@ constexpr uint32_t kNegOffA = 0xE408E408u, kNegOffB = 0xE480E480u;
 __device__ __forceinline__ int q4_slot(int m) { return (m & 1) ? 2 + ((m >> 1) & 1) * 4 + (m >> 2) : (m >> 1 & 1) * 4 + (m >> 2); }
 
 // ------------------------------------------------------------ act prep (int4)
-// One 256-thread workgroup per token: r = 1/sqrt(mean(x^2) + eps), then
+// One 512-thread workgroup per token: r = 1/sqrt(mean(x^2) + eps), then
 // n = x * gamma * r stored as fp16 [M, d] in the int4 slot order, the slots
-// of odd elements carrying n/16.
-__global__ __launch_bounds__(256) void k_act_prep_q4(const uint16_t* __restrict__ x,
+// of odd elements carrying n/16. Each thread issues all its x and gamma
+// loads at once and keeps x in registers between the two steps (d up to
+// kActPrepChunks * 8 * 512; larger d takes a second pass over x).
+constexpr int kActPrepChunks = 4;
+
+__device__ __forceinline__ u32x4 act_q4_chunk(u32x4 v, u32x4 g, float r) {
+  float n[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    n[2 * j] = bf16_lo(v[j]) * bf16_lo(g[j]) * r;
+    n[2 * j + 1] = bf16_hi(v[j]) * bf16_hi(g[j]) * r;
+  }
+  _Float16 h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[q4_slot(e)] = (_Float16)((e & 1) ? n[e] * 0.0625f : n[e]);
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * j]) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * j + 1]) << 16);
+  return o;
+}
+
+__global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma,
                                                      float eps, uint16_t* __restrict__ n0, int d) {
-  __shared__ float part[4];
+  __shared__ float part[8];
   const int64_t m = blockIdx.x;
   const uint16_t* xr = x + m * d;
-  const int chunks = d >> 3;
+  const int chunks = d >> 3, tid = threadIdx.x;
+  u32x4 v[kActPrepChunks], g[kActPrepChunks];
+#pragma unroll
+  for (int i = 0; i < kActPrepChunks; ++i) {
+    const int c = tid + i * 512;
+    v[i] = c < chunks ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    g[i] = c < chunks ? ld16(gamma + c * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
   float ss = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const u32x4 v = ld16(xr + c * 8);
+#pragma unroll
+  for (int i = 0; i < kActPrepChunks; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float a = bf16_lo(v[j]), b = bf16_hi(v[j]);
+      const float a = bf16_lo(v[i][j]), b = bf16_hi(v[i][j]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512) {  // only for very large d
+    const u32x4 w = ld16(xr + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
       ss = fmaf(a, a, ss);
       ss = fmaf(b, b, ss);
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
-  for (int c = threadIdx.x; c < chunks; c += 256) {
-    const u32x4 v = ld16(xr + c * 8), g = ld16(gamma + c * 8);
-    float n[8];
+  float tot = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      n[2 * j] = bf16_lo(v[j]) * bf16_lo(g[j]) * r;
-      n[2 * j + 1] = bf16_hi(v[j]) * bf16_hi(g[j]) * r;
-    }
-    _Float16 h[8];
+  for (int w = 0; w < 8; ++w) tot += part[w];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[q4_slot(e)] = (_Float16)((e & 1) ? n[e] * 0.0625f : n[e]);
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * j]) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * j + 1]) << 16);
-    st16(n0 + m * d + c * 8, o);
+  for (int i = 0; i < kActPrepChunks; ++i) {
+    const int c = tid + i * 512;
+    if (c < chunks) st16(n0 + m * d + c * 8, act_q4_chunk(v[i], g[i], r));
   }
+  for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512)
+    st16(n0 + m * d + c * 8, act_q4_chunk(ld16(xr + c * 8), ld16(gamma + c * 8), r));
 }
 
 // ------------------------------------------------------------ GEMV core
@@ -514,7 +543,7 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
   hipError_t e;
   if constexpr (WK == WK_INT4) {
-    launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(256), 0, stream, p.x, p.gamma, p.eps,
+    launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(512), 0, stream, p.x, p.gamma, p.eps,
                   ws.n0, p.d);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
