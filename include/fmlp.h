@@ -148,8 +148,11 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *                             w_down tiled bf16 [d, ff] (fmlp_pack_matrix);
  *                             gu_scales and down_scales ignored (may be NULL)
  *                FMLP_W_INT4_G32: tiled int4 codes + scales of the same two
- *                             logical matrices (fmlp_quantize_int4); int4
- *                             runs on the decode path only (M <= 32)
+ *                             logical matrices (fmlp_quantize_int4). Decode
+ *                             (M <= 32) dequantises in registers, exactly;
+ *                             prefill first expands both matrices to fp16
+ *                             tiles in the workspace (s*q rounded once to
+ *                             fp16), so its workspace holds 6*ff*d bytes more
  *   y          : bf16 [M, d], written (round to nearest even); must not
  *                overlap any other buffer.
  *   workspace  : device scratch of at least fmlp_workspace_size(M,d,ff,wtype)
@@ -170,8 +173,8 @@ int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
 
 /*
  * fmlp_forward with the kernel path chosen by the caller (enum fmlp_path);
- * used to test both paths at the same shapes. FMLP_PATH_DECODE with M > 32
- * returns FMLP_ERR_UNSUPPORTED_SHAPE.
+ * used to test both paths at the same shapes, for either weight type.
+ * FMLP_PATH_DECODE with M > 32 returns FMLP_ERR_UNSUPPORTED_SHAPE.
  */
 int fmlp_forward_path(const void* x, const void* gamma, float eps,
                       int32_t wtype, const void* w_gu, const void* gu_scales,
@@ -181,9 +184,9 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps,
 
 /*
  * Per-kernel timing (measurement support, not needed for computing).
- * fmlp_profile_enable(1) discards earlier records and starts bracketing every
- * kernel the library launches with a pair of HIP events recorded on the
- * launch's own stream; fmlp_profile_enable(0) stops recording (records are
+ * fmlp_profile_enable(1) discards earlier records and starts launching every
+ * kernel of the library with a pair of HIP events that the runtime stamps at
+ * the dispatch's start and end on its stream; fmlp_profile_enable(0) stops recording (records are
  * kept until the next enable). fmlp_profile_read synchronises the recorded
  * events of one kernel kind and returns how many launches were recorded and
  * their summed GPU time in milliseconds. Kinds are 0 .. n-1 in the order of

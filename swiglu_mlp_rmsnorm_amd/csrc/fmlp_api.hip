@@ -161,7 +161,7 @@ int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
   if (M < 0 || M > kMaxM || !shape_ok(d, ff) || (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32))
     return 0;
-  size_t b = fmlp::prefill_workspace_bytes(M, d, ff);
+  size_t b = fmlp::prefill_workspace_bytes(M, d, ff, wtype);
   if (M <= fmlp::kDecodeMaxM) {
     const size_t dec = fmlp::decode_workspace_bytes(M, d, ff);
     b = dec > b ? dec : b;
@@ -189,10 +189,9 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
 
   const bool decode = path == FMLP_PATH_DECODE || (path == FMLP_PATH_AUTO && M <= fmlp::kDecodeMaxM);
   if (decode && M > fmlp::kDecodeMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
-  if (!decode && int4) return FMLP_ERR_UNSUPPORTED_SHAPE;  // int4 runs on the decode kernels only
 
   const size_t need = decode ? fmlp::decode_workspace_bytes(M, d, ff)
-                             : fmlp::prefill_workspace_bytes(M, d, ff);
+                             : fmlp::prefill_workspace_bytes(M, d, ff, wtype);
   // align the workspace base to 256 bytes inside the caller's buffer
   const uintptr_t wbase = reinterpret_cast<uintptr_t>(workspace);
   const uintptr_t abase = (wbase + 255) & ~uintptr_t(255);

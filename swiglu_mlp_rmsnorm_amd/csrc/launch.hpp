@@ -32,7 +32,7 @@ inline int64_t int4_scale_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 
 
 // Workspace layout, shared by the sizing query and the launchers.
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff);
-size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff);
+size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype);
 
 hipError_t launch_pack(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* w_gu, int64_t ff,
                        int64_t d, hipStream_t stream);

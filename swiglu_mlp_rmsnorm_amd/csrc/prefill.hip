@@ -8,6 +8,11 @@
 //      fp16 (Figure 4 part2; the [M, 2ff] gate/up product never reaches HBM).
 //   2. y = a W_down^T on fp16 MFMA, stored bf16 (Figure 4 part3).
 //
+// int4 weights: a pre-pass dequantises both matrices into fp16 in the same
+// fragment-tiled geometry (w = s*q, exact in fp32, rounded once to fp16:
+// relative error <= 2^-11, far inside the accuracy bar), and the GEMMs read
+// those fp16 tiles without conversion.
+//
 // Operands are fp16 rather than bf16: rounding n to bf16 alone costs about
 // 2e-2 max / 3.3e-3 mean relative error on Llama-8B-shaped layers, over the
 // accuracy bar, while bf16 weights convert to fp16 exactly in the fp16 normal
@@ -89,6 +94,36 @@ __global__ __launch_bounds__(256) void k_rms_tile(const uint16_t* __restrict__ x
            ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
   }
   st16(n + g * 8, o);
+}
+
+// ---------------------------------------------------------------- int4 -> fp16 tiles
+// One thread per 16-byte chunk of the output (8 weights of one row): chunk
+// (tile, slot) of the fragment-tiled layout holds row 16*rb + slot%16,
+// columns 32*kb + 8*(slot/16) .. +7, tile = rb*(K/32) + kb. Its codes are one
+// word of the int4 super-tile of (rb, kb/4), its scale one fp16.
+__global__ __launch_bounds__(256) void k_dequant_f16_tiled(const uint32_t* __restrict__ qt,
+                                                           const uint16_t* __restrict__ st,
+                                                           int64_t R, int64_t K,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output chunk
+  const int64_t nkb = K >> 5, nq = (K + 127) >> 7;
+  if (c >= (R >> 4) * nkb * 64) return;
+  const int slot = (int)(c & 63);
+  const int64_t tile = c >> 6, rb = tile / nkb, kb = tile - rb * nkb;
+  const int64_t stile = rb * nq + (kb >> 2);
+  const uint32_t word = qt[stile * 256 + slot * 4 + (kb & 3)];
+  const float s = (float)__builtin_bit_cast(
+      _Float16, st[stile * 64 + (slot & 15) * 4 + (kb & 3)]);
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q0 = (int)((word >> (8 * j)) << 28) >> 28;      // code 2j (low nibble)
+    const int q1 = (int)((word >> (8 * j + 4)) << 28) >> 28;  // code 2j+1
+    const _Float16 w0 = (_Float16)(s * (float)q0), w1 = (_Float16)(s * (float)q1);
+    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
+  }
+  st16(out + c * 8, o);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -175,7 +210,8 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
   return h;
 }
 
-template <int NB, int MB, int WGN, int WGM, int EPI>
+// AF16: the weight tiles already hold fp16 (dequantised int4), no conversion.
+template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 __global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
     GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
 k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
@@ -267,8 +303,10 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   };
   // weight fragments bf16 -> fp16 in place (after their LDS reads land)
   auto convert = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (!AF16) {
 #pragma unroll
-    for (int i = 0; i < C::WNB; ++i) fa[buf][i] = bf16x8_to_f16x8(fa[buf][i]);
+      for (int i = 0; i < C::WNB; ++i) fa[buf][i] = bf16x8_to_f16x8(fa[buf][i]);
+    }
   };
   auto mma = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -283,7 +321,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   // four waves of a CU do not hand the address unit their loads in bursts.
   auto interleave = [&](auto n_vmem_c) __attribute__((always_inline)) {
     constexpr int NL = decltype(n_vmem_c)::value, NR = C::WNB + C::WMB;
-    constexpr int NMF = C::WNB * C::WMB, NV = C::WNB * 12, HALF = NMF / 2;
+    constexpr int NMF = C::WNB * C::WMB, NV = AF16 ? 0 : C::WNB * 12, HALF = NMF / 2;
     constexpr int LSTRIDE = NL > 0 ? (NMF / NL > 0 ? NMF / NL : 1) : NMF;
 #pragma unroll
     for (int g = 0; g < NMF; ++g) {
@@ -291,7 +329,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
       if (g < NR) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
       if (NL > 0 && g % LSTRIDE == 0 && g / LSTRIDE < NL)
         __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);             // VMEM read
-      if (g >= HALF)
+      if (NV > 0 && g >= HALF)
         __builtin_amdgcn_sched_group_barrier(0x0002, (NV + HALF - 1) / HALF, 0);  // VALU
     }
   };
@@ -406,7 +444,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 // Launch one GEMM with a given block tile and wave grid (splits > 1 only
 // with the fp32 partial epilogue).
-template <int NB, int MB, int WGN, int WGM, int EPI>
+template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
                                 int K, int splits, hipStream_t stream, int n_begin, int n_end) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
@@ -414,13 +452,13 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
     attr_err =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_wf16<NB, MB, WGN, WGM, EPI>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
   const int tiles = ((n_end - n_begin + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
-                k_gemm_wf16<NB, MB, WGN, WGM, EPI>, dim3(tiles, splits), dim3(C::THREADS),
+                k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>, dim3(tiles, splits), dim3(C::THREADS),
                 (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end);
   return hipGetLastError();
 }
@@ -467,21 +505,21 @@ static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
   return best;
 }
 
-template <int EPI>
+template <int EPI, bool AF16>
 static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
                                    void* out, int M, int N, int K, hipStream_t stream) {
   const int n_main = N - g.tail_rows;
   hipError_t e = hipSuccess;
   if (n_main > 0) {
     if (g.shape == 0)
-      e = launch_gemm_t<8, 8, 4, 2, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<8, 8, 4, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
     else if (g.shape == 1)
-      e = launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
     else
-      e = launch_gemm_t<4, 4, 2, 2, EPI>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
   }
   if (e != hipSuccess || g.tail_rows == 0) return e;
-  return launch_gemm_t<8, 4, 4, 1, EPI>(W, Act, out, M, N, K, g.splits, stream, n_main, N);
+  return launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, n_main, N);
 }
 
 // Split off a tail launch when the 256 x 256 tiles fill r >= 1 whole rounds
@@ -505,44 +543,90 @@ static GemmPlan plan_down(int64_t M, int64_t d, int64_t ff) {
   return plan_gemm((int)M, (int)d, (int)ff, true);
 }
 
-size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
-  // n fp16 [pad32(M), d] and a fp16 [pad32(M), ff], both fragment-tiled;
-  // r fp32 [M]; the down projection's split-K partials fp32 [splits, M, d]
-  const int splits = plan_down(M, d, ff).splits;
-  return align256((size_t)pad32(M) * d * 2) + align256((size_t)pad32(M) * ff * 2) +
-         align256((size_t)M * 4) + (splits > 1 ? align256((size_t)splits * M * d * 4) : 0);
+// Workspace regions, in order (each 256-byte aligned): n fp16 [pad32(M), d]
+// and a fp16 [pad32(M), ff], both fragment-tiled; r fp32 [M]; the down
+// projection's split-K partials fp32 [splits, M, d]; for int4 weights, the
+// dequantised fp16 W_gu [2ff, d] and W_down [d, ff], fragment-tiled.
+struct PrefillWs {
+  uint16_t *n, *a;
+  float *r, *part;
+  uint16_t *wgu16, *wd16;
+};
+
+static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, int splits, size_t* total) {
+  PrefillWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  w.n = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * d * 2));
+  w.a = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * ff * 2));
+  w.r = reinterpret_cast<float*>(take((size_t)M * 4));
+  w.part = reinterpret_cast<float*>(take(splits > 1 ? (size_t)splits * M * d * 4 : 0));
+  w.wgu16 = reinterpret_cast<uint16_t*>(take((size_t)2 * ff * d * 2));
+  w.wd16 = reinterpret_cast<uint16_t*>(take((size_t)d * ff * 2));
+  *total = off;
+  return w;
 }
 
-hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
-  if (p.wtype != 0) return hipErrorNotSupported;
-  uint16_t* n = reinterpret_cast<uint16_t*>(p.ws);
-  uint16_t* a = reinterpret_cast<uint16_t*>(p.ws + align256((size_t)pad32(p.M) * p.d * 2));
-  float* r = reinterpret_cast<float*>(p.ws + align256((size_t)pad32(p.M) * p.d * 2) +
-                                     align256((size_t)pad32(p.M) * p.ff * 2));
-  launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
-                p.x, p.eps, r, (int)p.M, (int)p.d);
-  const int64_t slots = pad32(p.M) * p.d / 8;
-  launch_kernel(KK_RMS_TILE, k_rms_tile, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
-                stream, p.x, p.gamma, r, n, (int)p.M, (int)p.d, slots);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype) {
+  size_t total = 0;
+  prefill_ws(nullptr, M, d, ff, plan_down(M, d, ff).splits, &total);
+  if (wtype == 0) total -= align256((size_t)2 * ff * d * 2) + align256((size_t)d * ff * 2);
+  return total;
+}
+
+template <bool AF16>
+static hipError_t prefill_gemms(const Problem& p, const PrefillWs& w, const uint16_t* wgu,
+                                const uint16_t* wd, const GemmPlan& g2, hipStream_t stream) {
   const GemmPlan g1 =
       with_tail(plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false), (int)p.M, (int)(2 * p.ff));
-  e = launch_gemm_plan<EPI_SILU_MUL_F16>(g1, reinterpret_cast<const uint16_t*>(p.w_gu), n, a,
-                                         (int)p.M, (int)(2 * p.ff), (int)p.d, stream);
+  hipError_t e = launch_gemm_plan<EPI_SILU_MUL_F16, AF16>(g1, wgu, w.n, w.a, (int)p.M,
+                                                          (int)(2 * p.ff), (int)p.d, stream);
   if (e != hipSuccess) return e;
-  const GemmPlan g2 = plan_down(p.M, p.d, p.ff);
   if (g2.splits == 1)
-    return launch_gemm_plan<EPI_STORE_BF16>(g2, reinterpret_cast<const uint16_t*>(p.w_down), a,
-                                            p.y, (int)p.M, (int)p.d, (int)p.ff, stream);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(r) + align256((size_t)p.M * 4));
-  e = launch_gemm_plan<EPI_STORE_F32>(g2, reinterpret_cast<const uint16_t*>(p.w_down), a, part,
-                                      (int)p.M, (int)p.d, (int)p.ff, stream);
+    return launch_gemm_plan<EPI_STORE_BF16, AF16>(g2, wd, w.a, p.y, (int)p.M, (int)p.d, (int)p.ff,
+                                                  stream);
+  e = launch_gemm_plan<EPI_STORE_F32, AF16>(g2, wd, w.a, w.part, (int)p.M, (int)p.d, (int)p.ff,
+                                            stream);
   if (e != hipSuccess) return e;
   const int64_t n4 = p.M * p.d / 4;
   launch_kernel(KK_SPLITK_REDUCE, k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                stream, part, p.y, n4, g2.splits);
+                stream, w.part, p.y, n4, g2.splits);
   return hipGetLastError();
+}
+
+static hipError_t launch_dequant_f16(const uint8_t* q, const uint16_t* s, int64_t R, int64_t K,
+                                     uint16_t* out, hipStream_t stream) {
+  const int64_t chunks = (R >> 4) * (K >> 5) * 64;
+  launch_kernel(KK_DEQUANT, k_dequant_f16_tiled, dim3((unsigned)((chunks + 255) / 256)), dim3(256),
+                0, stream, reinterpret_cast<const uint32_t*>(q), s, R, K, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
+  const GemmPlan g2 = plan_down(p.M, p.d, p.ff);
+  size_t total = 0;
+  const PrefillWs w = prefill_ws(p.ws, p.M, p.d, p.ff, g2.splits, &total);
+  launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
+                p.x, p.eps, w.r, (int)p.M, (int)p.d);
+  const int64_t slots = pad32(p.M) * p.d / 8;
+  launch_kernel(KK_RMS_TILE, k_rms_tile, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
+                stream, p.x, p.gamma, w.r, w.n, (int)p.M, (int)p.d, slots);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.wtype == 0)
+    return prefill_gemms<false>(p, w, reinterpret_cast<const uint16_t*>(p.w_gu),
+                                reinterpret_cast<const uint16_t*>(p.w_down), g2, stream);
+  if ((e = launch_dequant_f16(reinterpret_cast<const uint8_t*>(p.w_gu), p.s_gu, 2 * p.ff, p.d,
+                              w.wgu16, stream)) != hipSuccess)
+    return e;
+  if ((e = launch_dequant_f16(reinterpret_cast<const uint8_t*>(p.w_down), p.s_down, p.d, p.ff,
+                              w.wd16, stream)) != hipSuccess)
+    return e;
+  return prefill_gemms<true>(p, w, w.wgu16, w.wd16, g2, stream);
 }
 
 }  // namespace fmlp

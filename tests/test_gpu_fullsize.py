@@ -20,6 +20,8 @@ CASES = [
     ("llama8b_decode_d4096_ff14336", 16), ("llama8b_decode_d4096_ff14336", 32),
     ("llama8b_prefill_d4096_ff14336", 512), ("llama8b_prefill_d4096_ff14336", 2048),
     ("llama70b_int4_decode_d8192_ff28672", 1), ("llama70b_int4_decode_d8192_ff28672", 16),
+    # int4 weights on the prefill path (beyond the workload's own M values)
+    ("llama70b_int4_decode_d8192_ff28672", 64),
 ]
 
 

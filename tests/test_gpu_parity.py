@@ -205,6 +205,24 @@ def test_decode_int4_shapes(d, ff, M):
     assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 d={d} ff={ff} M={M}")
 
 
+@pytest.mark.parametrize("M,path", [(33, F.FMLP_PATH_AUTO), (70, F.FMLP_PATH_AUTO),
+                                    (200, F.FMLP_PATH_AUTO), (1, F.FMLP_PATH_PREFILL),
+                                    (32, F.FMLP_PATH_PREFILL)])
+def test_prefill_int4(M, path):
+    # int4 on the MFMA path: weights expanded to fp16 tiles, then the GEMMs
+    layer = Int4Layer(TINY_D, TINY_FF, 31)
+    x, g = bf16_inputs(M, TINY_D, 800 + M)
+    assert_parity(layer.forward(x, g, EPS, path=path), layer.oracle(x, g, EPS),
+                  f"int4 prefill M={M}")
+
+
+@pytest.mark.parametrize("d,ff,M", [(512, 1376, 70), (256, 4096, 100)])
+def test_prefill_int4_shapes(d, ff, M):
+    layer = Int4Layer(d, ff, 50 + d)
+    x, g = bf16_inputs(M, d, 850 + M)
+    assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 prefill d={d} ff={ff}")
+
+
 def test_int4_end_to_end_from_bf16(tiny):
     # quantise with the library; the oracle quantises the same seeded bf16
     # weights itself and runs Eq(1) on its own codes
