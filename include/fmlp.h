@@ -161,7 +161,8 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  * Accumulation is fp32. The normalised input and the SiLU*mul intermediate
  * are kept as bf16 hi + lo pairs (about 2^-17 relative) on the bf16 decode
  * path, and as fp16 on the int4 decode path and the MFMA prefill path
- * (|values| must stay below 65504 there). Not bitwise identical across
+ * (|values| must stay below 65504 there; the prefill path also converts the
+ * weights, or s*q, to fp16, so the same bound holds for them). Not bitwise identical across
  * paths; deterministic for a given path and shape. Concurrent calls must
  * not share a workspace.
  */
