@@ -13,6 +13,7 @@ configuration; `--all` prints one line per (workload, M).
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -45,6 +46,8 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--path", choices=sorted(PATHS), default="auto",
+                    help="kernel path (fmlp_forward_path); auto is fmlp_forward's own choice")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "known-size reference for the HBM byte counters) and exit")
@@ -52,6 +55,9 @@ def parse():
 
 
 # ----------------------------------------------------------------------------- bytes / flops
+
+PATHS = {"auto": 0, "decode": 1, "prefill": 2, "single_pass": 3}
+
 
 def weight_bytes(d, ff, wtype):
     """(W_gu bytes, W_down bytes), scales included for int4."""
@@ -71,9 +77,17 @@ def kernel_bytes(kernel, M, d, ff, wtype):
     (+ scales), its activation inputs and its outputs. bf16 path: gate/up
     reads x and gamma and writes the SiLU*mul product as a bf16 hi + lo pair
     (4 bytes per element), which down reads back. int4 path: gate/up reads
-    the prepared fp16 n, the product is fp16 (2 bytes per element)."""
+    the prepared fp16 n, the product is fp16 (2 bytes per element).
+    Single-pass decode: one kernel reads both matrices, x and gamma and
+    writes fp32 partial sums per 32-feature slice of ff, which the reduce
+    kernel reads back to write y."""
     gu, dn = weight_bytes(d, ff, wtype)
     a_elem = 2 if wtype == "int4" else 4
+    partials = (ff // 32) * M * d * 4  # single-pass decode: fp32 per 32-feature slice
+    if kernel == "decode_fused_bf16":
+        return gu + dn + M * d * 2 + d * 2 + partials
+    if kernel == "partial_reduce":
+        return partials + M * d * 2
     if "gateup" in kernel:
         act_in = M * d * 2 + (0 if wtype == "int4" else d * 2)
         return gu + act_in + M * ff * a_elem
@@ -108,7 +122,8 @@ def kernel_source_sha(kernel):
         "decode_gateup_bf16": "decode.hip", "decode_down_bf16": "decode.hip",
         "decode_gateup_int4": "decode.hip", "decode_down_int4": "decode.hip",
         "gemm_gateup_silu_f16": "prefill.hip", "gemm_down_f16": "prefill.hip",
-        "act_prep": "decode.hip",
+        "act_prep": "decode.hip", "decode_fused_bf16": "decode.hip",
+        "partial_reduce": "decode.hip",
     }.get(kernel)
     if src is None:
         return None
@@ -191,7 +206,8 @@ def run_one(wname, M, steps, warmup, args):
     w = synth.WORKLOADS[wname]
     dev = torch.device("cuda:0")
     d, ff = w.d, w.ff
-    path = "decode" if M <= 32 else "prefill"
+    path = args.path if args.path != "auto" else ("decode" if M <= 32 else "prefill")
+    pcode = None if args.path == "auto" else PATHS[args.path]  # None: fmlp_forward itself
     log(f"[bench] {wname} M={M}: building {w.sets} weight set(s)")
     layers, xs = [], []
     host0 = None  # row-major / untiled copies of set 0 for the CPU baseline
@@ -215,10 +231,12 @@ def run_one(wname, M, steps, warmup, args):
     def step(i):
         L = layers[i % w.sets]
         x, g = xs[i % w.sets]
+        fwd = F.fmlp_forward if pcode is None else functools.partial(F.fmlp_forward_path,
+                                                                      path=pcode)
         if w.wtype == "int4":
-            F.fmlp_forward(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws, ff=ff)
+            fwd(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws, ff=ff)
         else:
-            F.fmlp_forward(x, g, synth.EPS, L[0], L[1], y=y, workspace=ws)
+            fwd(x, g, synth.EPS, L[0], L[1], y=y, workspace=ws)
 
     for i in range(warmup):
         step(i)
@@ -255,7 +273,13 @@ def run_one(wname, M, steps, warmup, args):
         F.fmlp_profile_enable(False)
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
-    if path == "decode":
+    if "decode_fused_bf16" in kernels:
+        path = "single_pass"
+    if path == "single_pass":
+        dom = "decode_fused_bf16"
+        dom_units = kernel_bytes(dom, M, d, ff, w.wtype)
+        unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
+    elif path == "decode":
         dom = "decode_gateup_int4" if w.wtype == "int4" else "decode_gateup_bf16"
         dom_units = kernel_bytes(dom, M, d, ff, w.wtype)
         unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
@@ -276,7 +300,7 @@ def run_one(wname, M, steps, warmup, args):
                     "traffic": measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
         t = k["us_per_step"]
-        if name.startswith("decode") or name == "act_prep":
+        if name.startswith("decode") or name in ("act_prep", "partial_reduce"):
             k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (t * 1e3), 1)
         elif name == "gemm_gateup_silu_f16":
             k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (t * 1e6), 1)

@@ -64,7 +64,12 @@ enum fmlp_wtype {
 enum fmlp_path {
   FMLP_PATH_AUTO = 0,    /* decode kernels for M <= 32, MFMA GEMMs above */
   FMLP_PATH_DECODE = 1,  /* force the decode (weight-streaming) kernels; M <= 32 */
-  FMLP_PATH_PREFILL = 2  /* force the tiled MFMA GEMM path; any M */
+  FMLP_PATH_PREFILL = 2, /* force the tiled MFMA GEMM path; any M */
+  FMLP_PATH_SINGLE_PASS = 3 /* force the single-pass decode (gate/up, SiLU*mul
+                               and down in one kernel over the weights, then a
+                               reduction of per-slice partial sums; FastTPS
+                               review, section 3, Fusion MLP); bf16 weights,
+                               M <= 8 */
 };
 
 /*
@@ -134,8 +139,10 @@ int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows,
                       int64_t K, float* out, void* stream);
 
 /*
- * Bytes of scratch fmlp_forward needs for this problem (for either path),
- * or 0 when the shape is unsupported. Depends only on the arguments.
+ * Bytes of scratch fmlp_forward needs for this problem (for any path it may
+ * take), or 0 when the shape is unsupported. Depends only on the arguments,
+ * and never decreases as M grows with d, ff and wtype fixed, so a buffer
+ * sized for the largest M serves every smaller one.
  */
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
 
@@ -175,7 +182,8 @@ int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
 /*
  * fmlp_forward with the kernel path chosen by the caller (enum fmlp_path);
  * used to test both paths at the same shapes, for either weight type.
- * FMLP_PATH_DECODE with M > 32 returns FMLP_ERR_UNSUPPORTED_SHAPE.
+ * FMLP_PATH_DECODE with M > 32, and FMLP_PATH_SINGLE_PASS with M > 8 or
+ * int4 weights, return FMLP_ERR_UNSUPPORTED_SHAPE.
  */
 int fmlp_forward_path(const void* x, const void* gamma, float eps,
                       int32_t wtype, const void* w_gu, const void* gu_scales,

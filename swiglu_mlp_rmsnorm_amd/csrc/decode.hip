@@ -73,6 +73,18 @@
 #ifndef FMLP_Q4_DN_RB
 #define FMLP_Q4_DN_RB 2  // down row blocks per workgroup (int4)
 #endif
+#ifndef FMLP_FU_S
+#define FMLP_FU_S 16     // waves per single-pass workgroup
+#endif
+#ifndef FMLP_FU_P
+#define FMLP_FU_P 1      // single-pass gate/up ring depth
+#endif
+#ifndef FMLP_FU_DQ
+#define FMLP_FU_DQ 8     // single-pass down tiles in flight per wave
+#endif
+#ifndef FMLP_FU_DYN_LDS
+#define FMLP_FU_DYN_LDS 0  // extra (unused) LDS per single-pass workgroup, bytes
+#endif
 
 namespace fmlp {
 
@@ -99,6 +111,12 @@ static int down_splits(int64_t d, int64_t ff, bool int4) {
     if (t < tb - 1e-9) tb = t, best = k;
   }
   return best;
+}
+
+// Single-pass decode: fp32 partial sums [ff/32, M, d] from the start of the
+// workspace.
+size_t fused_partial_bytes(int64_t M, int64_t d, int64_t ff) {
+  return (size_t)(ff / 32) * M * d * 4;
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
@@ -529,6 +547,182 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
                                __HIP_MEMORY_SCOPE_AGENT);
     y[yi] = bf16_rne(sum);
   }
+}
+
+// ------------------------------------------------------------ single pass
+// Gate/up, SiLU*mul and down in one pass over the weights (FastTPS review,
+// section 3: the Fusion MLP keeps the intermediate on chip and moves only
+// the input and the output). Workgroup w owns the 32 features
+// [32w, 32w + 32) of ff:
+//   1. their 64 interleaved W_gu rows (row blocks 4w .. 4w+3) against
+//      gamma * x, S waves splitting K, the RMS factor folded into the
+//      epilogue exactly as in k_decode_gateup;
+//   2. a = SiLU(gate) * up for the 32 features, kept in LDS as the bf16
+//      hi + lo operand pair;
+//   3. the matching 32 columns of W_down (K unit w of every 16-row block,
+//      one 1 KB tile each) against a, each wave taking every S-th row block,
+//      giving the fp32 partial  part[w][t][j] = sum_{i in slice w}
+//      W_down[j][i] a[t][i].
+// The down tiles do not depend on a, so each wave issues its first DQ of
+// them as soon as its gate/up loads have landed, before the cross-wave
+// reduction. No workgroup waits for another; k_partial_reduce sums the
+// ff/32 partials afterwards.
+template <int S, int P, int DQ>
+__global__ __launch_bounds__(64 * S) void k_decode_fused(
+    const uint16_t* __restrict__ w_gu, const uint16_t* __restrict__ w_down,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
+    float* __restrict__ part, int M, int d, int ff) {
+  constexpr int RB = 4;  // 4 x 16 W_gu rows = 32 gate/up pairs
+  __shared__ f32x4 red[S * RB * 64];
+  __shared__ float ssred[S * 16];
+  __shared__ uint32_t abuf[2][16][17];  // [hi, lo][token][feature pair], padded
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int sl = blockIdx.x;
+  f32x4 acc[RB][1];
+  float ss[1];
+  gemv_core<ACT_X, 1, RB, S, P>(w_gu, nullptr, x, gamma, (int64_t)sl * RB, d, M, 0, d >> 5, acc,
+                                ss);
+
+  // down tiles (row block wave + j*S, K unit sl), j < nt
+  const int64_t tstride = (int64_t)(ff >> 5) * 512 * S;  // elements between a wave's tiles
+  const int nbd = d >> 4;
+  const int nt = wave < nbd ? (nbd - wave + S - 1) / S : 0;
+  const uint16_t* wd = w_down + ((int64_t)wave * (ff >> 5) + sl) * 512 + lane * 8;
+  u32x4 db[DQ];
+#pragma unroll
+  for (int q = 0; q < DQ; ++q)
+    if (q < nt) db[q] = ld16_stream(wd + q * tstride);
+
+  stash<RB, 1>(red, acc);
+  {
+    float v = ss[0];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (lane < 16) ssred[wave * 16 + lane] = v;
+  }
+  __syncthreads();
+  const float inv_d = 1.0f / (float)d;
+  for (int o = threadIdx.x; o < 16 * 16; o += 64 * S) {
+    const int pp = o & 15, t = o >> 4;  // features 2pp, 2pp+1 of the slice
+    uint32_t h = 0u, l = 0u;
+    if (t < M) {
+      const int L0 = (t >> 2) * 16, e = t & 3;
+      float sst = 0.f;
+#pragma unroll
+      for (int s = 0; s < S; ++s) sst += ssred[s * 16 + t];
+      const float r = 1.0f / sqrtf(sst * inv_d + eps);
+      float av[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int p = 2 * pp + k;
+        const int rb = p >> 3, lr = (p & 7) * 2;
+        float g = 0.f, u = 0.f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int base = (s * RB + rb) * 64 + L0 + lr;
+          g += red[base][e];
+          u += red[base + 1][e];
+        }
+        av[k] = silu_mul(g * r, u * r);
+      }
+      split_bf16_pair(av[0], av[1], h, l);
+    }
+    abuf[0][t][pp] = h;
+    abuf[1][t][pp] = l;
+  }
+  __syncthreads();
+  // A operand: token col, features 8*grp .. 8*grp+7 of the slice
+  u32x4 ah, al;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ah[i] = abuf[0][col][grp * 4 + i];
+    al[i] = abuf[1][col][grp * 4 + i];
+  }
+  float* pw = part + (int64_t)sl * M * d;
+  for (int j0 = 0; j0 < nt; j0 += DQ) {
+#pragma unroll
+    for (int q = 0; q < DQ; ++q) {
+      const int j = j0 + q;
+      if (j < nt) {
+        const u32x4 wv = db[q];
+        if (j + DQ < nt) db[q] = ld16_stream(wd + (j + DQ) * tstride);
+        f32x4 c = mfma_bf16(ah, wv, f32x4{0.f, 0.f, 0.f, 0.f});
+        c = mfma_bf16(al, wv, c);
+        const int row = (wave + j * S) * 16 + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = grp * 4 + e;
+          if (t < M) pw[(int64_t)t * d + row] = c[e];
+        }
+      }
+    }
+  }
+}
+
+// y[t][j] = bf16( sum over w of part[w][t][j] ). Workgroup: 16 outputs of
+// one token; thread i sums partials w = i, i+256, ... in order, then a fixed
+// two-level combination through LDS (deterministic for a given shape).
+__global__ __launch_bounds__(256) void k_partial_reduce(const float* __restrict__ part,
+                                                        uint16_t* __restrict__ y, int nw, int M,
+                                                        int d) {
+  __shared__ float s1[256][17];
+  __shared__ float s2[16][17];
+  const int j0 = blockIdx.x * 16, t = blockIdx.y;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int w = threadIdx.x; w < nw; w += 256) {
+    const float* p = part + ((int64_t)w * M + t) * d + j0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * c + e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s1[threadIdx.x][i] = acc[i];
+  __syncthreads();
+  {
+    const int i = threadIdx.x & 15, c = threadIdx.x >> 4;
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v += s1[c * 16 + k][i];
+    s2[c][i] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float v = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v += s2[c][threadIdx.x];
+    y[(int64_t)t * d + j0 + threadIdx.x] = bf16_rne(v);
+  }
+}
+
+// Measured on MI355X, the single pass loses to the two-kernel decode at
+// every workload shape (Phi-3 M=1: 28.1 us for the pass + 4.0 us for the
+// reduction against 30.5 us; Llama-8B M=1: 70.5 against 66.4 us): one
+// 150-350 MB stream runs no faster than the two separate ones, and the
+// partial-sum reduction costs more than the second launch saves. So the
+// automatic choice never takes it; FMLP_PATH_SINGLE_PASS forces it.
+bool single_pass_auto(int64_t M, int64_t d, int64_t ff, int wtype) {
+  (void)M, (void)d, (void)ff, (void)wtype;
+  return false;
+}
+
+hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
+  float* part = reinterpret_cast<float*>(p.ws);
+  const int nw = p.ff / 32;
+  launch_kernel(KK_DECODE_FUSED_BF16, k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ>, dim3(nw),
+                dim3(64 * FMLP_FU_S), FMLP_FU_DYN_LDS, stream, static_cast<const uint16_t*>(p.w_gu),
+                static_cast<const uint16_t*>(p.w_down), p.x, p.gamma, p.eps, part, p.M, p.d,
+                p.ff);
+  hipError_t e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  launch_kernel(KK_PARTIAL_REDUCE, k_partial_reduce, dim3(p.d / 16, p.M), dim3(256), 0, stream,
+                static_cast<const float*>(part), p.y, nw, p.M, p.d);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ launch

@@ -161,10 +161,17 @@ int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
   if (M < 0 || M > kMaxM || !shape_ok(d, ff) || (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32))
     return 0;
+  // the largest need of the paths the problem may take; the single-pass
+  // term is kept at its M = kFusedMaxM value above that, so the size never
+  // decreases as M grows (a buffer sized for the largest M serves them all)
   size_t b = fmlp::prefill_workspace_bytes(M, d, ff, wtype);
   if (M <= fmlp::kDecodeMaxM) {
     const size_t dec = fmlp::decode_workspace_bytes(M, d, ff);
     b = dec > b ? dec : b;
+  }
+  if (wtype == FMLP_W_BF16) {
+    const size_t one = fmlp::fused_partial_bytes(M < fmlp::kFusedMaxM ? M : fmlp::kFusedMaxM, d, ff);
+    b = one > b ? one : b;
   }
   return b + 256;  // room to align the base
 }
@@ -174,7 +181,8 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
                       const void* down_scales, void* y, int64_t M, int64_t d, int64_t ff,
                       void* workspace, size_t workspace_bytes, void* stream, int32_t path) {
   if (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32) return FMLP_ERR_INVALID_ARG;
-  if (path != FMLP_PATH_AUTO && path != FMLP_PATH_DECODE && path != FMLP_PATH_PREFILL)
+  if (path != FMLP_PATH_AUTO && path != FMLP_PATH_DECODE && path != FMLP_PATH_PREFILL &&
+      path != FMLP_PATH_SINGLE_PASS)
     return FMLP_ERR_INVALID_ARG;
   if (M < 0) return FMLP_ERR_INVALID_ARG;
   if (!shape_ok(d, ff) || M > kMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
@@ -187,11 +195,16 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
       !aligned16(y) || !aligned16(workspace) || (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))))
     return FMLP_ERR_ALIGNMENT;
 
-  const bool decode = path == FMLP_PATH_DECODE || (path == FMLP_PATH_AUTO && M <= fmlp::kDecodeMaxM);
+  const bool single = path == FMLP_PATH_SINGLE_PASS ||
+                      (path == FMLP_PATH_AUTO && fmlp::single_pass_auto(M, d, ff, wtype));
+  const bool decode = single || path == FMLP_PATH_DECODE ||
+                      (path == FMLP_PATH_AUTO && M <= fmlp::kDecodeMaxM);
   if (decode && M > fmlp::kDecodeMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (single && (int4 || M > fmlp::kFusedMaxM)) return FMLP_ERR_UNSUPPORTED_SHAPE;
 
-  const size_t need = decode ? fmlp::decode_workspace_bytes(M, d, ff)
-                             : fmlp::prefill_workspace_bytes(M, d, ff, wtype);
+  const size_t need = single   ? fmlp::fused_partial_bytes(M, d, ff)
+                      : decode ? fmlp::decode_workspace_bytes(M, d, ff)
+                               : fmlp::prefill_workspace_bytes(M, d, ff, wtype);
   // align the workspace base to 256 bytes inside the caller's buffer
   const uintptr_t wbase = reinterpret_cast<uintptr_t>(workspace);
   const uintptr_t abase = (wbase + 255) & ~uintptr_t(255);
@@ -230,7 +243,9 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
   p.ws = reinterpret_cast<char*>(abase);
   p.ws_bytes = workspace_bytes - (abase - wbase);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = decode ? fmlp::launch_decode(p, s) : fmlp::launch_prefill(p, s);
+  hipError_t e = single   ? fmlp::launch_decode_fused(p, s)
+                 : decode ? fmlp::launch_decode(p, s)
+                          : fmlp::launch_prefill(p, s);
   return e == hipSuccess ? FMLP_OK : hip_fail(e);
 }
 

@@ -25,6 +25,9 @@ struct Problem {
 };
 
 constexpr int kDecodeMaxM = 32;
+// Largest M of the single-pass decode (bf16 weights): its fp32 partials grow
+// as (ff/32) * M * d * 4 bytes.
+constexpr int kFusedMaxM = 8;
 
 // Sizes of the tiled int4 format for a logical [R, K] matrix.
 inline int64_t int4_code_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 127) / 128) * 1024; }
@@ -32,6 +35,7 @@ inline int64_t int4_scale_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 
 
 // Workspace layout, shared by the sizing query and the launchers.
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff);
+size_t fused_partial_bytes(int64_t M, int64_t d, int64_t ff);
 size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype);
 
 hipError_t launch_pack(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* w_gu, int64_t ff,
@@ -44,6 +48,9 @@ hipError_t launch_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows
                           float* out, hipStream_t stream);
 
 hipError_t launch_decode(const Problem& p, hipStream_t stream);
+hipError_t launch_decode_fused(const Problem& p, hipStream_t stream);
+// Whether FMLP_PATH_AUTO takes the single-pass decode for this problem.
+bool single_pass_auto(int64_t M, int64_t d, int64_t ff, int wtype);
 hipError_t launch_prefill(const Problem& p, hipStream_t stream);
 
 }  // namespace fmlp

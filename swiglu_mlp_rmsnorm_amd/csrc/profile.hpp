@@ -24,6 +24,8 @@ enum KernelKind {
   KK_GEMM_DOWN,
   KK_RMS_TILE,
   KK_SPLITK_REDUCE,
+  KK_DECODE_FUSED_BF16,
+  KK_PARTIAL_REDUCE,
   KK_COUNT
 };
 

@@ -34,6 +34,7 @@ FMLP_W_INT4_G32 = 1
 FMLP_PATH_AUTO = 0
 FMLP_PATH_DECODE = 1
 FMLP_PATH_PREFILL = 2
+FMLP_PATH_SINGLE_PASS = 3
 
 EXPORTS = (
     "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",

@@ -68,6 +68,9 @@ def fwd(M=1, d=256, ff=704, eps=1e-5, wtype=0, path=0, ws_bytes=BIG, **over):
     (dict(y=ctypes.c_void_p((7 << 36) + 8)), F.FMLP_ERR_ALIGNMENT),
     (dict(wgu=ctypes.c_void_p((3 << 36) + 4)), F.FMLP_ERR_ALIGNMENT),
     (dict(M=33, path=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=9, path=3), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=1, path=3, wtype=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(path=4), F.FMLP_ERR_INVALID_ARG),
     (dict(ws_bytes=100), F.FMLP_ERR_WORKSPACE),
     (dict(y=A["x"]), F.FMLP_ERR_INVALID_ARG),
     (dict(y=A["ws"]), F.FMLP_ERR_INVALID_ARG),
@@ -99,6 +102,12 @@ def test_workspace_size():
     # alignment slack) is rejected there
     need = ws(1, 256, 704)
     assert fwd(ws_bytes=need - 256 - 1, path=F.FMLP_PATH_PREFILL) == F.FMLP_ERR_WORKSPACE
+    # the single-pass decode keeps (ff/32) * M * d fp32 partial sums; at
+    # Phi-3 size and M = 8 that is the largest need of the three paths
+    assert ws(8, 3072, 8192) >= (8192 // 32) * 8 * 3072 * 4
+    need = ws(8, 3072, 8192)
+    assert fwd(M=8, d=3072, ff=8192, ws_bytes=need - 256 - 1,
+               path=F.FMLP_PATH_SINGLE_PASS) == F.FMLP_ERR_WORKSPACE
 
 
 def test_pack_quant_dequant_validation():

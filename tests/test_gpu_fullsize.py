@@ -52,3 +52,21 @@ def test_full_size_parity(wname, M):
     assert torch.all(torch.isfinite(y.float()))
     mx, l1 = assert_parity(y[rows], ref, f"{wname} M={M}")
     print(f"{wname} M={M} rows={rows}: max/rms={mx:.3e} L1={l1:.3e}")
+
+
+@pytest.mark.parametrize("wname,M", [("phi3mini_decode_d3072_ff8192", 1),
+                                     ("phi3mini_decode_d3072_ff8192", 8),
+                                     ("llama8b_decode_d4096_ff14336", 1),
+                                     ("llama8b_decode_d4096_ff14336", 4)])
+def test_full_size_single_pass(wname, M):
+    w = synth.WORKLOADS[wname]
+    x, g = synth.inputs(w, M, "cuda")
+    b = synth.bits
+    wg, wu, wd = synth.layer_bf16(w, 0, "cuda")
+    y = F.fmlp_forward_path(x, g, synth.EPS, F.fmlp_pack_interleaved(wg, wu),
+                            F.fmlp_pack_matrix(wd), path=F.FMLP_PATH_SINGLE_PASS)
+    rows = sample_rows(M, 8)
+    ref = oracle.forward_unfused(b(x)[rows], b(g), synth.EPS, b(wg), b(wu), b(wd))
+    torch.cuda.synchronize()
+    mx, l1 = assert_parity(y[rows], ref, f"single pass {wname} M={M}")
+    print(f"single pass {wname} M={M}: max/rms={mx:.3e} L1={l1:.3e}")

@@ -147,7 +147,40 @@ def test_decode_split_down(M):
     assert torch.equal(y1.view(torch.int16), layer.forward(x, g, EPS).view(torch.int16))
 
 
-@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 5), (F.FMLP_PATH_PREFILL, 70)])
+SP = F.FMLP_PATH_SINGLE_PASS
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8])
+def test_single_pass_ragged(tiny, M):
+    # ff = 704: 22 slices of 32 features; d = 256: 16 down row blocks over 8 waves
+    x, g = bf16_inputs(M, TINY_D, 150 + M)
+    assert_parity(tiny.forward(x, g, EPS, path=SP), tiny.oracle(x, g, EPS), f"single pass M={M}")
+
+
+@pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 8), (512, 1376, 5),
+                                    (1024, 2048, 2), (288, 2048, 1), (4128, 64, 1),
+                                    (3072, 8192, 1)])
+def test_single_pass_shapes(d, ff, M):
+    # d = 32: six of the eight waves own no down row block; d = 4128: 258
+    # row blocks, more than the 16 tiles a wave keeps in flight
+    layer = Bf16Layer(d, ff, 30 + d)
+    x, g = bf16_inputs(M, d, 450 + M)
+    y1 = layer.forward(x, g, EPS, path=SP)
+    assert_parity(y1, layer.oracle(x, g, EPS), f"single pass d={d} ff={ff} M={M}")
+    assert torch.equal(y1.view(torch.int16), layer.forward(x, g, EPS, path=SP).view(torch.int16))
+
+
+def test_single_pass_matches_two_kernel_path_closely(tiny):
+    # same operand precision (bf16 hi + lo activations, fp32 accumulation):
+    # the two decode variants differ only in summation order
+    x, g = bf16_inputs(4, TINY_D, 160)
+    y1 = tiny.forward(x, g, EPS, path=SP).float()
+    y2 = tiny.forward(x, g, EPS, path=F.FMLP_PATH_DECODE).float()
+    rms = float(y2.pow(2).mean().sqrt())
+    assert float((y1 - y2).abs().max()) <= 2 ** -7 * rms
+
+
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 5), (F.FMLP_PATH_PREFILL, 70), (SP, 3)])
 def test_zero_weight_and_zero_input_cases(tiny, path, M):
     x, g = bf16_inputs(M, TINY_D, 9)
     zero_gate = F.fmlp_pack_interleaved(torch.zeros_like(tiny.wg), tiny.wu)
@@ -160,7 +193,7 @@ def test_zero_weight_and_zero_input_cases(tiny, path, M):
 
 
 @pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 9), (F.FMLP_PATH_DECODE, 32),
-                                    (F.FMLP_PATH_PREFILL, 100)])
+                                    (F.FMLP_PATH_PREFILL, 100), (SP, 1), (SP, 8)])
 def test_every_output_written_and_deterministic(tiny, path, M):
     x, g = bf16_inputs(M, TINY_D, 55)
     y1 = torch.full((M, TINY_D), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -172,7 +205,7 @@ def test_every_output_written_and_deterministic(tiny, path, M):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 6), (F.FMLP_PATH_PREFILL, 80)])
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 6), (F.FMLP_PATH_PREFILL, 80), (SP, 6)])
 def test_nan_row_stays_in_its_row(tiny, path, M):
     x, g = bf16_inputs(M, TINY_D, 66)
     x[2, 7] = float("nan")
