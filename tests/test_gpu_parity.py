@@ -161,8 +161,8 @@ def test_single_pass_ragged(tiny, M):
                                     (1024, 2048, 2), (288, 2048, 1), (4128, 64, 1),
                                     (3072, 8192, 1)])
 def test_single_pass_shapes(d, ff, M):
-    # d = 32: six of the eight waves own no down row block; d = 4128: 258
-    # row blocks, more than the 16 tiles a wave keeps in flight
+    # d = 32: most waves own no down row block; d = 4128: 258 row blocks,
+    # more down tiles per wave than it keeps in flight
     layer = Bf16Layer(d, ff, 30 + d)
     x, g = bf16_inputs(M, d, 450 + M)
     y1 = layer.forward(x, g, EPS, path=SP)
@@ -231,7 +231,12 @@ def test_decode_int4_ragged(M):
 
 
 @pytest.mark.parametrize("d,ff,M", [(128, 128, 1), (384, 640, 7), (256, 1024, 32), (1024, 2048, 1),
-                                    (1024, 2048, 20)])
+                                    (1024, 2048, 20),
+                                    # activations staged in LDS (M <= 4) with more chunks
+                                    # than the staging registers hold: gate/up at d=8192,
+                                    # and a 4-way K-split down projection at ff=20480
+                                    (8192, 256, 3), (1024, 20480, 4), (1024, 20480, 2),
+                                    (4096, 1056, 1)])
 def test_decode_int4_shapes(d, ff, M):
     layer = Int4Layer(d, ff, 40 + d)
     x, g = bf16_inputs(M, d, 550 + M)
