@@ -82,6 +82,24 @@
 #ifndef FMLP_FU_DQ
 #define FMLP_FU_DQ 8     // single-pass down tiles in flight per wave
 #endif
+#ifndef FMLP_BIG_M
+#define FMLP_BIG_M 4       // above this M, the activation loads of each K unit are
+#endif                     // shared by more weight rows (the settings below)
+#ifndef FMLP_BIG_GU_RB
+#define FMLP_BIG_GU_RB 4   // bf16 gate/up row blocks per workgroup for M > FMLP_BIG_M
+#endif
+#ifndef FMLP_BIG_DN_RB
+#define FMLP_BIG_DN_RB 4   // down row blocks per workgroup for M > FMLP_BIG_M (split K)
+#endif
+#ifndef FMLP_BIG_DN_S
+#define FMLP_BIG_DN_S 8    // and its waves (M <= 16)
+#endif
+#ifndef FMLP_BIG_DN_S2
+#define FMLP_BIG_DN_S2 16  // and its waves (M > 16)
+#endif
+#ifndef FMLP_BIG_GU_RB2
+#define FMLP_BIG_GU_RB2 4  // bf16 gate/up row blocks per workgroup for M > 16
+#endif
 #ifndef FMLP_DEC_LDS
 #define FMLP_DEC_LDS 1     // stage small-M activations in LDS (0: read them per wave)
 #endif
@@ -95,16 +113,16 @@ enum { WK_BF16 = 0, WK_INT4 = 1 };
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-// Down-projection split along K (see k_decode_down): with d/16 row blocks,
-// split each into k slices when that spreads the work more evenly over the
+// Down-projection split along K (see k_decode_down): with `blocks` row-block
+// groups (d/16 over the row blocks per workgroup), split each into k slices when that spreads the work more evenly over the
 // 256 CUs (time ~ rounds of workgroups / k), keeping at least min_units K
 // units per slice; at most kMaxSplit.
 constexpr int kMaxSplit = 4;
-static int down_splits(int64_t d, int64_t ff, bool int4) {
+static int down_splits(int64_t blocks, int64_t ff, bool int4) {
 #ifdef FMLP_DN_SPLIT
   return FMLP_DN_SPLIT;
 #endif
-  const int64_t blocks = d / 16, nu = int4 ? (ff + 127) / 128 : ff / 32;
+  const int64_t nu = int4 ? (ff + 127) / 128 : ff / 32;
   const int64_t min_units = int4 ? 4 : 16;
   int best = 1;
   double tb = (double)((blocks + 255) / 256);
@@ -906,14 +924,48 @@ hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
 
 // ------------------------------------------------------------ launch
 
+// Down projection with DRB row blocks and S waves per workgroup, K split
+// `splits` ways across workgroups; activations staged in LDS when `lds`.
+template <int WK, int NCB, int DRB, int S, bool STAGE>
+static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool lds,
+                        int64_t lds_bytes, hipStream_t stream) {
+  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
+  const int kind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
+  const dim3 grid(p.d / (16 * DRB), splits), block(64 * S);
+  if (STAGE && lds)
+    launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, STAGE>, grid, block,
+                  (uint32_t)lds_bytes, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d,
+                  p.ff, ws.part, ws.cnt);
+  else
+    launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, false>, grid, block, 0, stream,
+                  p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff, ws.part, ws.cnt);
+}
+
+template <int WK, int NCB, int RB>
+static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
+                          const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
+                          hipStream_t stream) {
+  constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
+  constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
+  const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
+  // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
+  const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * FMLP_GU_S);
+  if (kStage && lds)
+    launch_kernel(kind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, kStage>, grid, block,
+                  (uint32_t)lds_bytes, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1,
+                  p.M, p.d, p.ff, ws.cnt, ncnt);
+  else
+    launch_kernel(kind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false>, grid, block, 0, stream,
+                  p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt);
+}
+
 template <int WK, int NCB>
 static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const DecodeWs ws = decode_ws(p);
   constexpr int GRB = WK == WK_INT4 ? FMLP_Q4_GU_RB : FMLP_GU_RB;
   constexpr int RB = (NCB == 1) ? GRB : (GRB > 2 ? 2 : GRB);
-  constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
-  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
   constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
+  constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
   hipError_t e;
   if constexpr (WK == WK_INT4) {
     launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(512), 0, stream, p.x, p.gamma, p.eps,
@@ -923,57 +975,52 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
   const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
+  // Larger M: every K unit's activation loads (M tokens per wave) cost as
+  // much as its weight loads, so more weight rows share them: bf16 gate/up
+  // takes FMLP_BIG_GU_RB row blocks per workgroup, and the down projection
+  // FMLP_BIG_DN_RB, split along K to keep enough workgroups.
+  const bool big = p.M > FMLP_BIG_M;
   // down: DRB row blocks per workgroup when they divide d and leave enough
   // workgroups to cover the CUs; else one, split along K when that helps
-  const bool drb = DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
-  const int splits = drb ? 1 : down_splits(p.d, p.ff, WK == WK_INT4);
+  constexpr int BDRB = FMLP_BIG_DN_RB;
+  const bool bdrb = big && p.d % (16 * BDRB) == 0;
+  const bool drb = !bdrb && DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
+  const int dn_rb = bdrb ? BDRB : drb ? DRB : 1;
+  const int splits = drb ? 1 : down_splits(p.d / (16 * dn_rb), p.ff, WK == WK_INT4);
   // int4 activations staged in LDS for small M, when they fit without
   // lowering the number of workgroups resident per CU (bytes per workgroup).
   // Measured on MI355X: 70B-shaped int4 layers at M=1 gain 13 % (gate/up) and
   // 10 % (down); bf16 layers gain at most 3 % in gate/up and lose up to 14 %
   // in down, so they keep reading their activations per wave.
-  constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
   auto lds_budget = [](int64_t wgs) -> int64_t { return wgs <= 256 ? 96 * 1024 : 32 * 1024; };
-  const int64_t gu_wgs = (2 * p.ff) / (16 * RB);
+  constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2;
+  const bool gu_big = big && WK == WK_BF16;
+  const int64_t gu_wgs = (2 * p.ff) / (16 * (gu_big ? BGRB : RB));
   const int64_t gu_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * p.d;
   const bool gl = kStage && p.M <= kLdsMaxM && gu_lds <= lds_budget(gu_wgs);
   const int ukd = WK == WK_BF16 ? 32 : 128, nud = (p.ff + ukd - 1) / ukd;
-  const int64_t dn_wgs = drb ? p.d / (16 * DRB) : (p.d / 16) * splits;
+  const int64_t dn_wgs = (p.d / (16 * dn_rb)) * splits;
   const int64_t dn_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * ((nud + splits - 1) / splits) * ukd;
   const bool dl = kStage && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
-  // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
-  const int gkind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
-  const dim3 ggrid((2 * p.ff) / (16 * RB)), gblock(64 * FMLP_GU_S);
+
   const int ncnt = splits > 1 ? (int)(p.d / 16) : 0;
-  if (gl)
-    launch_kernel(gkind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, kStage>, ggrid, gblock,
-                  (uint32_t)gu_lds, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M,
-                  p.d, p.ff, ws.cnt, ncnt);
+  if (gu_big)
+    launch_gateup<WK, NCB, WK == WK_BF16 ? BGRB : RB>(p, ws, act0, act1, ncnt, gl, gu_lds,
+                                                      stream);
   else
-    launch_kernel(gkind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false>, ggrid, gblock, 0,
-                  stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M, p.d, p.ff, ws.cnt,
-                  ncnt);
+    launch_gateup<WK, NCB, RB>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int dkind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
-  auto down = [&](auto kern_lds, auto kern, dim3 grid, dim3 block) {
-    if (dl)
-      launch_kernel(dkind, kern_lds, grid, block, (uint32_t)dn_lds, stream, p.w_down, p.s_down,
-                    ws.a0, ws.a1, p.y, p.M, p.d, p.ff, ws.part, ws.cnt);
-    else
-      launch_kernel(dkind, kern, grid, block, 0, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y,
-                    p.M, p.d, p.ff, ws.part, ws.cnt);
-  };
-  if (drb)
-    down(k_decode_down<WK, NCB, DRB, FMLP_DN_S, DP, kStage>,
-         k_decode_down<WK, NCB, DRB, FMLP_DN_S, DP, false>, dim3(p.d / (16 * DRB)),
-         dim3(64 * FMLP_DN_S));
+  if (bdrb)
+    // (int4 with two token blocks keeps 8 waves: its registers do not fit 16)
+    launch_down<WK, NCB, BDRB, (NCB == 1 || WK == WK_INT4) ? FMLP_BIG_DN_S : FMLP_BIG_DN_S2,
+                kStage>(p, ws, splits, dl, dn_lds, stream);
+  else if (drb)
+    launch_down<WK, NCB, DRB, (NCB == 2 && WK == WK_INT4) ? 8 : FMLP_DN_S, kStage>(
+        p, ws, splits, dl, dn_lds, stream);
   else if (splits == 1)
-    down(k_decode_down<WK, NCB, 1, FMLP_DN_S, DP, kStage>,
-         k_decode_down<WK, NCB, 1, FMLP_DN_S, DP, false>, dim3(p.d / 16), dim3(64 * FMLP_DN_S));
+    launch_down<WK, NCB, 1, FMLP_DN_S, kStage>(p, ws, splits, dl, dn_lds, stream);
   else  // split slices are short: 8 waves each, so that more of them are resident per CU
-    down(k_decode_down<WK, NCB, 1, FMLP_DN_SPLIT_S, DP, kStage>,
-         k_decode_down<WK, NCB, 1, FMLP_DN_SPLIT_S, DP, false>, dim3(p.d / 16, splits),
-         dim3(64 * FMLP_DN_SPLIT_S));
+    launch_down<WK, NCB, 1, FMLP_DN_SPLIT_S, kStage>(p, ws, splits, dl, dn_lds, stream);
   return hipGetLastError();
 }
 
