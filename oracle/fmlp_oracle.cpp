@@ -24,6 +24,18 @@
 //       q = clamp(round_half_even(fp32(w / s)), -8, 7), q = 0 when s == 0,
 //       two's-complement nibbles, even k in the low nibble.
 //
+//   Variants beyond Eq(1) (also readings, listed in the design doc):
+//     activation of the gate branch: SiLU (Eq(1)), or GELU, the activation the
+//       Together AI fusion post (blog.hotdry.top) names for its fused MLP;
+//       the pages give no GELU formula, so both usual forms are offered:
+//       erf form t * Phi(t) = 0.5 t (1 + erf(t / sqrt 2)), and tanh form
+//       0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3)));
+//     residual prologue: with a residual input r (the previous sublayer's
+//       output), the residual stream h = bf16_rne(x + r) is formed, written
+//       out, and normalised in place of x (the residual add fused with the
+//       following RMSNorm; same post, where the add/all-reduce is fused into
+//       the next normalisation).
+//
 // Summation order is fixed (k ascending), and OpenMP only splits independent
 // outputs, so results do not depend on the thread count.
 
@@ -91,13 +103,61 @@ static uint16_t f16_bits_rne(float f) {
   return (uint16_t)(sign | bits);
 }
 
+// double -> bf16 with round-to-nearest-even, written from the format
+// definition (8 significant bits, exponent range of binary32): scale the
+// magnitude so the kept bits are the integer part, round that integer
+// half-to-even, scale back; the rounded value is exact in binary32, whose
+// top 16 bits are the bf16 pattern.
+static uint16_t bf16_bits_rne(double v) {
+  if (std::isnan(v)) return std::signbit(v) ? 0xffc0u : 0x7fc0u;
+  const double a = std::fabs(v);
+  const int old_mode = std::fegetround();
+  std::fesetround(FE_TONEAREST);
+  double r;
+  if (a < std::ldexp(1.0, -126)) {
+    r = std::ldexp(std::nearbyint(std::ldexp(a, 133)), -133);  // subnormal unit 2^-133
+  } else {
+    int e2;
+    std::frexp(a, &e2);                                   // a in [2^(e2-1), 2^e2)
+    r = std::ldexp(std::nearbyint(std::ldexp(a, 8 - e2)), e2 - 8);  // 8 significant bits
+  }
+  std::fesetround(old_mode);
+  const float f = (float)(std::signbit(v) ? -r : r);      // exact, or +-inf past the range
+  uint32_t u;
+  std::memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
 double oracle_bf16_to_double(uint16_t b) { return bf16_value(b); }
+uint16_t oracle_bf16_rne(double v) { return bf16_bits_rne(v); }
 double oracle_f16_to_double(uint16_t h) { return f16_value(h); }
 uint16_t oracle_f32_to_f16_rne(float f) { return f16_bits_rne(f); }
 
 // SiLU(t) = t * sigmoid(t) = t / (1 + e^-t). For t -> -inf, e^-t overflows to
 // +inf and the quotient is -0, the correct limit.
 double oracle_silu(double t) { return t / (1.0 + std::exp(-t)); }
+
+// GELU, erf form: t * Phi(t), Phi the standard normal distribution function.
+double oracle_gelu_erf(double t) { return 0.5 * t * (1.0 + std::erf(t / std::sqrt(2.0))); }
+
+// GELU, tanh form: Phi(t) approximated by 0.5 (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))).
+double oracle_gelu_tanh(double t) {
+  const double c = std::sqrt(2.0 / std::acos(-1.0));
+  return 0.5 * t * (1.0 + std::tanh(c * (t + 0.044715 * t * t * t)));
+}
+
+// Gate activation by code: 0 SiLU, 1 GELU (tanh form), 2 GELU (erf form).
+static double gate_act(int act, double t) {
+  if (act == 1) return oracle_gelu_tanh(t);
+  if (act == 2) return oracle_gelu_erf(t);
+  return oracle_silu(t);
+}
+
+// h[i] = bf16_rne(x[i] + r[i]) over n elements (bit patterns); the sum of
+// two bf16 values is exact in double.
+void oracle_residual_add(const uint16_t* x, const uint16_t* r, int64_t n, uint16_t* h) {
+  for (int64_t i = 0; i < n; ++i) h[i] = bf16_bits_rne(bf16_value(x[i]) + bf16_value(r[i]));
+}
 
 // ---------------------------------------------------------------- RMSNorm
 
@@ -296,24 +356,34 @@ struct WeightView {
   }
 };
 
-// y[m, :] = Wd (SiLU(Wg n_m) * (Wu n_m)), n_m = RMSNorm(x_m).
-// gate row i is (g_view, g_row0 + g_stride*i), up row i likewise.
-static void forward_core(const uint16_t* x, const uint16_t* gamma, double eps,
+// y[m, :] = Wd (act(Wg n_m) * (Wu n_m)), n_m = RMSNorm(h_m), with h = x, or
+// h = bf16_rne(x + res) when res is given (then also written to h_out when
+// that is given). gate row i is (g_view, g_row0 + g_stride*i), up row i
+// likewise.
+static void forward_core(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
+                         const uint16_t* gamma, double eps, int act,
                          const WeightView& gv, int64_t g_row0, int64_t g_stride,
                          const WeightView& uv, int64_t u_row0, int64_t u_stride,
                          const WeightView& dv, int64_t M, int64_t d, int64_t ff,
                          double* y) {
   double* n = new double[d];
   double* a = new double[ff];
+  uint16_t* h = new uint16_t[d];
   for (int64_t m = 0; m < M; ++m) {
-    oracle_rmsnorm(x + m * d, gamma, eps, 1, d, n);
+    const uint16_t* xm = x + m * d;
+    if (res) {
+      oracle_residual_add(xm, res + m * d, d, h);
+      if (h_out) std::memcpy(h_out + m * d, h, (size_t)d * sizeof(uint16_t));
+      xm = h;
+    }
+    oracle_rmsnorm(xm, gamma, eps, 1, d, n);
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < ff; ++i) {
       double g = 0.0, u = 0.0;
       const int64_t gr = g_row0 + g_stride * i, ur = u_row0 + u_stride * i;
       for (int64_t k = 0; k < d; ++k) g += gv.at(gr, k) * n[k];
       for (int64_t k = 0; k < d; ++k) u += uv.at(ur, k) * n[k];
-      a[i] = oracle_silu(g) * u;
+      a[i] = gate_act(act, g) * u;
     }
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < d; ++j) {
@@ -324,17 +394,28 @@ static void forward_core(const uint16_t* x, const uint16_t* gamma, double eps,
   }
   delete[] n;
   delete[] a;
+  delete[] h;
 }
 
-// Eq(1) from separate gate and up matrices (the unfused ordering).
+// Eq(1) from separate gate and up matrices (the unfused ordering), with the
+// activation `act` and the optional residual prologue (res, h_out nullable).
+void oracle_forward_unfused_ex(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
+                               const uint16_t* gamma, double eps, int act,
+                               const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, int64_t M, int64_t d, int64_t ff,
+                               double* y) {
+  WeightView g{0, w_gate, nullptr, nullptr, d};
+  WeightView u{0, w_up, nullptr, nullptr, d};
+  WeightView dn{0, w_down, nullptr, nullptr, ff};
+  forward_core(x, res, h_out, gamma, eps, act, g, 0, 1, u, 0, 1, dn, M, d, ff, y);
+}
+
 void oracle_forward_unfused(const uint16_t* x, const uint16_t* gamma,
                             double eps, const uint16_t* w_gate,
                             const uint16_t* w_up, const uint16_t* w_down,
                             int64_t M, int64_t d, int64_t ff, double* y) {
-  WeightView g{0, w_gate, nullptr, nullptr, d};
-  WeightView u{0, w_up, nullptr, nullptr, d};
-  WeightView dn{0, w_down, nullptr, nullptr, ff};
-  forward_core(x, gamma, eps, g, 0, 1, u, 0, 1, dn, M, d, ff, y);
+  oracle_forward_unfused_ex(x, nullptr, nullptr, gamma, eps, 0, w_gate, w_up, w_down, M, d, ff,
+                            y);
 }
 
 // Eq(1) from the interleaved matrix w_gu [2ff, d] (gate at even rows).
@@ -343,17 +424,27 @@ void oracle_forward_bf16(const uint16_t* x, const uint16_t* gamma, double eps,
                          int64_t M, int64_t d, int64_t ff, double* y) {
   WeightView gu{0, w_gu, nullptr, nullptr, d};
   WeightView dn{0, w_down, nullptr, nullptr, ff};
-  forward_core(x, gamma, eps, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
+  forward_core(x, nullptr, nullptr, gamma, eps, 0, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
 }
 
-// Eq(1) with int4 weights: w = s * q, widened exactly to double.
+// Eq(1) with int4 weights: w = s * q, widened exactly to double; activation
+// and residual prologue as in oracle_forward_unfused_ex.
+void oracle_forward_int4_ex(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
+                            const uint16_t* gamma, double eps, int act, const uint8_t* q_gu,
+                            const uint16_t* s_gu, const uint8_t* q_down,
+                            const uint16_t* s_down, int64_t M, int64_t d, int64_t ff,
+                            double* y) {
+  WeightView gu{1, nullptr, q_gu, s_gu, d};
+  WeightView dn{1, nullptr, q_down, s_down, ff};
+  forward_core(x, res, h_out, gamma, eps, act, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
+}
+
 void oracle_forward_int4(const uint16_t* x, const uint16_t* gamma, double eps,
                          const uint8_t* q_gu, const uint16_t* s_gu,
                          const uint8_t* q_down, const uint16_t* s_down,
                          int64_t M, int64_t d, int64_t ff, double* y) {
-  WeightView gu{1, nullptr, q_gu, s_gu, d};
-  WeightView dn{1, nullptr, q_down, s_down, ff};
-  forward_core(x, gamma, eps, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
+  oracle_forward_int4_ex(x, nullptr, nullptr, gamma, eps, 0, q_gu, s_gu, q_down, s_down, M, d,
+                         ff, y);
 }
 
 // Threads the parallel loops above will use.

@@ -55,6 +55,14 @@ def _load():
             "oracle_f16_to_double": (D, [ctypes.c_uint16]),
             "oracle_f32_to_f16_rne": (ctypes.c_uint16, [ctypes.c_float]),
             "oracle_silu": (D, [D]),
+            "oracle_gelu_erf": (D, [D]),
+            "oracle_gelu_tanh": (D, [D]),
+            "oracle_bf16_rne": (ctypes.c_uint16, [D]),
+            "oracle_residual_add": (None, [P, P, I64, P]),
+            "oracle_forward_unfused_ex": (None, [P, P, P, P, D, ctypes.c_int, P, P, P, I64, I64,
+                                                 I64, P]),
+            "oracle_forward_int4_ex": (None, [P, P, P, P, D, ctypes.c_int, P, P, P, P, I64, I64,
+                                              I64, P]),
             "oracle_rms_scale": (None, [P, I64, I64, D, P]),
             "oracle_rmsnorm": (None, [P, P, D, I64, I64, P]),
             "oracle_pack_interleaved": (None, [P, P, P, I64, I64]),
@@ -109,6 +117,33 @@ def f32_to_f16_rne(f: float) -> int:
 def silu(t: float) -> float:
     """SiLU(t) = t / (1 + exp(-t))."""
     return _load().oracle_silu(t)
+
+
+ACT_SILU, ACT_GELU_TANH, ACT_GELU_ERF = 0, 1, 2
+
+
+def gelu_erf(t: float) -> float:
+    """GELU(t) = t * Phi(t) = 0.5 t (1 + erf(t / sqrt 2))."""
+    return _load().oracle_gelu_erf(t)
+
+
+def gelu_tanh(t: float) -> float:
+    """GELU(t) ~ 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3)))."""
+    return _load().oracle_gelu_tanh(t)
+
+
+def bf16_rne(v: float) -> int:
+    """double -> bf16 bit pattern, round to nearest even."""
+    return _load().oracle_bf16_rne(v)
+
+
+def residual_add(x: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """h = bf16_rne(x + r), element-wise on bf16 bit patterns."""
+    x, r = _c(x, np.uint16), _c(r, np.uint16)
+    assert x.shape == r.shape
+    h = np.empty(x.shape, np.uint16)
+    _load().oracle_residual_add(_p(x), _p(r), x.size, _p(h))
+    return h
 
 
 def rms_scale(x: np.ndarray, eps: float) -> np.ndarray:
@@ -170,6 +205,23 @@ def forward_unfused(x, gamma, eps, w_gate, w_up, w_down) -> np.ndarray:
     return y
 
 
+def forward_unfused_ex(x, gamma, eps, w_gate, w_up, w_down, act=ACT_SILU, residual=None):
+    """Eq(1) with gate activation `act` and, when `residual` is given, the
+    residual prologue h = bf16_rne(x + residual) normalised in place of x.
+    Returns (y fp64 [M, d], h bf16 bits [M, d] or None)."""
+    x, gamma = _c(x, np.uint16), _c(gamma, np.uint16)
+    w_gate, w_up, w_down = (_c(a, np.uint16) for a in (w_gate, w_up, w_down))
+    M, d = x.shape
+    ff = w_gate.shape[0]
+    y = np.empty((M, d), np.float64)
+    res = None if residual is None else _c(residual, np.uint16)
+    h = None if residual is None else np.empty((M, d), np.uint16)
+    _load().oracle_forward_unfused_ex(_p(x), None if res is None else _p(res),
+                                      None if h is None else _p(h), _p(gamma), eps, act,
+                                      _p(w_gate), _p(w_up), _p(w_down), M, d, ff, _p(y))
+    return y, h
+
+
 def forward_bf16(x, gamma, eps, w_gu, w_down) -> np.ndarray:
     """Eq(1) with RMSNorm prologue, from the interleaved w_gu [2ff, d]; fp64."""
     x, gamma = _c(x, np.uint16), _c(gamma, np.uint16)
@@ -193,6 +245,23 @@ def forward_int4(x, gamma, eps, q_gu, s_gu, q_down, s_down) -> np.ndarray:
     _load().oracle_forward_int4(_p(x), _p(gamma), eps, _p(q_gu), _p(s_gu),
                                 _p(q_down), _p(s_down), M, d, ff, _p(y))
     return y
+
+
+def forward_int4_ex(x, gamma, eps, q_gu, s_gu, q_down, s_down, act=ACT_SILU, residual=None):
+    """forward_int4 with gate activation `act` and the optional residual
+    prologue; returns (y, h) as forward_unfused_ex."""
+    x, gamma = _c(x, np.uint16), _c(gamma, np.uint16)
+    q_gu, q_down = _c(q_gu, np.uint8), _c(q_down, np.uint8)
+    s_gu, s_down = _c(s_gu, np.uint16), _c(s_down, np.uint16)
+    M, d = x.shape
+    ff = q_gu.shape[0] // 2
+    y = np.empty((M, d), np.float64)
+    res = None if residual is None else _c(residual, np.uint16)
+    h = None if residual is None else np.empty((M, d), np.uint16)
+    _load().oracle_forward_int4_ex(_p(x), None if res is None else _p(res),
+                                   None if h is None else _p(h), _p(gamma), eps, act,
+                                   _p(q_gu), _p(s_gu), _p(q_down), _p(s_down), M, d, ff, _p(y))
+    return y, h
 
 
 # ---------------------------------------------------------------- tiled layouts

@@ -14,7 +14,7 @@ MUTATIONS = {
     "sum_not_mean": ("std::sqrt(ss / (double)d + eps)", "std::sqrt(ss + eps)"),
     "gamma_dropped": ("* r * bf16_value(gamma[k])", "* r"),
     "gate_up_rows_swapped": ("gu, 0, 2, gu, 1, 2", "gu, 1, 2, gu, 0, 2"),
-    "silu_on_up_branch": ("oracle_silu(g) * u", "oracle_silu(u) * g"),
+    "silu_on_up_branch": ("gate_act(act, g) * u", "gate_act(act, u) * g"),
     "w_down_transposed": ("acc += dv.at(j, i) * a[i]", "acc += dv.at(i % dv.K, j % ff) * a[i]"),
     "round_half_away": ("float rq = std::nearbyint(ratio_k);", "float rq = std::round(ratio_k);"),
     "nibble_order_swapped": ("const uint8_t byte = qrow[k / 2];\n  const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);",
@@ -23,6 +23,11 @@ MUTATIONS = {
                              "((r % 16) * 4 + (k % 32) / 8) * 8 + k % 8"),
     "int4_tile_word_order": ("lane * 4 + g % 4", "(g % 4) * 64 + lane"),
     "sigmoid_not_silu": ("return t / (1.0 + std::exp(-t));", "return 1.0 / (1.0 + std::exp(-t));"),
+    "gelu_erf_unscaled": ("std::erf(t / std::sqrt(2.0))", "std::erf(t)"),
+    "gelu_tanh_cubic_coefficient": ("0.044715 * t * t * t", "0.0447 * t * t * t"),
+    "gelu_forms_swapped": ("if (act == 1) return oracle_gelu_tanh(t);", "if (act == 1) return oracle_gelu_erf(t);"),
+    "bf16_round_toward_zero": ("std::nearbyint(std::ldexp(a, 8 - e2))", "std::trunc(std::ldexp(a, 8 - e2))"),
+    "residual_not_normalised": ("      xm = h;\n", "      (void)xm;\n"),
 }
 
 

@@ -385,3 +385,126 @@ def test_tile_int4_padding_is_zero():
     words = qt.view(np.uint32).reshape(64, 4)
     assert np.all(words[:, 3] == 0)
     assert np.all(st.reshape(16, 4)[:, 3] == 0)
+
+
+# ------------------------------------------------------------ variants: GELU gate, residual prologue
+# The Together AI fusion post (blog.hotdry.top) fuses an MLP whose activation
+# is GELU, and fuses the residual add / all-reduce into the next
+# normalisation; the pages give neither formula, so the oracle's readings are
+# pinned here against the standard normal table, odd-part identities and
+# torch's own implementations.
+
+PHI_1 = 0.8413447460685429  # standard normal distribution function at 1 (tables)
+
+
+def test_gelu_closed_form_values():
+    assert oracle.gelu_erf(0.0) == 0.0 and oracle.gelu_tanh(0.0) == 0.0
+    assert oracle.gelu_erf(1.0) == pytest.approx(PHI_1, abs=1e-15)
+    assert oracle.gelu_erf(-1.0) == pytest.approx(-(1.0 - PHI_1), abs=1e-15)
+    # GELU(t) - GELU(-t) = t for both forms (Phi(t) + Phi(-t) = 1; tanh is odd)
+    for t in (-6.0, -1.3, -0.2, 0.07, 0.9, 2.5, 7.0):
+        for f in (oracle.gelu_erf, oracle.gelu_tanh):
+            assert f(t) - f(-t) == pytest.approx(t, rel=1e-14, abs=1e-15)
+    # the tanh form approximates the erf form to ~1e-3 absolute
+    for t in np.linspace(-5, 5, 41):
+        assert abs(oracle.gelu_tanh(float(t)) - oracle.gelu_erf(float(t))) < 1e-3
+    # limits: -> t for large t, -> 0 for very negative t
+    for f in (oracle.gelu_erf, oracle.gelu_tanh):
+        assert f(40.0) == pytest.approx(40.0, rel=1e-15)
+        assert abs(f(-40.0)) < 1e-300 or f(-40.0) == 0.0
+
+
+@pytest.mark.parametrize("approximate,fn", [("none", "gelu_erf"), ("tanh", "gelu_tanh")])
+def test_gelu_matches_torch(approximate, fn):
+    t = torch.linspace(-12, 12, 1201, dtype=torch.float64)
+    ref = F.gelu(t, approximate=approximate).numpy()
+    got = np.array([getattr(oracle, fn)(float(v)) for v in t])
+    # 1 + tanh(.) cancels for very negative t: compare there on an absolute scale
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def test_bf16_rne_ties_subnormals_and_overflow():
+    r = oracle.bf16_rne
+    assert r(1.0 + 2 ** -8) == 0x3F80           # tie between 1 and 1+2^-7: even
+    assert r(1.0 + 3 * 2 ** -8) == 0x3F82       # tie between 1+2^-7 and 1+2^-6: even
+    assert r(1.0 + 2 ** -8 + 2 ** -40) == 0x3F81  # just above the tie
+    assert r(-(2.0 + 2 ** -7)) == 0xC000        # tie at the next binade: even
+    assert r(-0.0) == 0x8000 and r(0.0) == 0
+    assert r(2 ** -133) == 0x0001 and r(2 ** -134) == 0 and r(3 * 2 ** -135) == 0x0001
+    assert r(3.3895313892515355e38) == 0x7F7F   # largest finite bf16
+    assert r(3.5e38) == 0x7F80 and r(-math.inf) == 0xFF80
+    assert (r(math.nan) & 0x7FFF) > 0x7F80
+
+
+def test_bf16_rne_matches_torch_on_float32_values():
+    # every binary32 value is exact in double, and torch rounds binary32 to
+    # bf16 to nearest even: the two must agree bit for bit
+    g = torch.Generator().manual_seed(7)
+    v = torch.cat([torch.randn(4000, generator=g) * 10.0 ** float(e) for e in range(-30, 31, 6)])
+    want = v.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.bf16_rne(float(a)) for a in v], np.uint16)
+    assert np.array_equal(got, want)
+
+
+def test_residual_add_matches_torch():
+    # bf16 + bf16 in binary32 then rounded to bf16 is the correctly rounded
+    # sum (24 >= 2*8 + 2 bits: the double rounding is innocuous)
+    x = rand_bf16((8, 512), 1.0, 71)
+    r = rand_bf16((8, 512), 3.0, 72)
+    r[0, :8] = bf16_bits([1e-30, -1e-30, 2.0 ** -8, 2.0 ** 100, -1.0, 0.0, 1.0 + 2 ** -7, 7.0])
+    want = (torch.from_numpy(bf16_values(x)).float() + torch.from_numpy(bf16_values(r)).float())
+    want = want.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.residual_add(x, r), want)
+
+
+def test_forward_ex_defaults_are_eq1():
+    x, g, wg, wu, wd = _rand_layer(3, 64, 96, 800)
+    y, h = oracle.forward_unfused_ex(x, g, 1e-5, wg, wu, wd)
+    assert h is None
+    assert np.array_equal(y, oracle.forward_unfused(x, g, 1e-5, wg, wu, wd))
+
+
+@pytest.mark.parametrize("act,approx", [(oracle.ACT_SILU, None), (oracle.ACT_GELU_TANH, "tanh"),
+                                        (oracle.ACT_GELU_ERF, "none")])
+@pytest.mark.parametrize("with_res", [False, True])
+def test_forward_ex_matches_torch_composition(act, approx, with_res):
+    M, d, ff = 3, 128, 160
+    x, g, wg, wu, wd = _rand_layer(M, d, ff, 810 + act)
+    res = rand_bf16((M, d), 2.0, 820 + act) if with_res else None
+    X = torch.from_numpy(bf16_values(x))
+    if with_res:
+        hb = (X.float() + torch.from_numpy(bf16_values(res)).float()).to(torch.bfloat16)
+        X = hb.double()
+    G, WG, WU, WD = (torch.from_numpy(bf16_values(a)) for a in (g, wg, wu, wd))
+    n = F.rms_norm(X, (d,), G, 1e-5)
+    z = n @ WG.T
+    gate = F.silu(z) if approx is None else F.gelu(z, approximate=approx)
+    ref = ((gate * (n @ WU.T)) @ WD.T).numpy()
+    y, h = oracle.forward_unfused_ex(x, g, 1e-5, wg, wu, wd, act=act, residual=res)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+    if with_res:
+        assert np.array_equal(h, hb.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_int4_forward_ex_matches_torch_composition():
+    # int4 variant: the same composition with w = s*q built here from the nibbles
+    rng = np.random.default_rng(9)
+    M, d, ff = 2, 128, 96
+    x = rand_bf16((M, d), 1.0, 832)
+    g = rand_bf16((d,), 0.1, 833, mean=1.0)
+    res = rand_bf16((M, d), 1.0, 834)
+    q_gu = rng.integers(0, 256, (2 * ff, d // 2), dtype=np.uint8)
+    s_gu = (rng.random((2 * ff, d // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    q_d = rng.integers(0, 256, (d, ff // 2), dtype=np.uint8)
+    s_d = (rng.random((d, ff // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    wgu = np.repeat(s_gu.view(np.float16).astype(np.float64), 32, 1) * _nibbles(q_gu)
+    wdn = np.repeat(s_d.view(np.float16).astype(np.float64), 32, 1) * _nibbles(q_d)
+    hb = (torch.from_numpy(bf16_values(x)).float() + torch.from_numpy(bf16_values(res)).float())
+    hb = hb.to(torch.bfloat16)
+    n = F.rms_norm(hb.double(), (d,), torch.from_numpy(bf16_values(g)), 1e-5)
+    WGU = torch.from_numpy(wgu)
+    ref = ((F.gelu(n @ WGU[0::2].T) * (n @ WGU[1::2].T)) @ torch.from_numpy(wdn).T).numpy()
+    y, h = oracle.forward_int4_ex(x, g, 1e-5, q_gu, s_gu, q_d, s_d, act=oracle.ACT_GELU_ERF,
+                                  residual=res)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+    assert np.array_equal(h, hb.view(torch.int16).numpy().view(np.uint16))
