@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
     ap.add_argument("--path", choices=sorted(PATHS), default="auto",
                     help="kernel path (fmlp_forward_path); auto is fmlp_forward's own choice")
+    ap.add_argument("--activation", choices=sorted(ACTS), default="silu",
+                    help="gate activation; other than silu runs fmlp_forward_ex")
+    ap.add_argument("--residual", action="store_true",
+                    help="add a residual input before the norm (fmlp_forward_ex)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "known-size reference for the HBM byte counters) and exit")
@@ -57,6 +61,7 @@ def parse():
 # ----------------------------------------------------------------------------- bytes / flops
 
 PATHS = {"auto": 0, "decode": 1, "prefill": 2, "single_pass": 3}
+ACTS = {"silu": 0, "gelu_tanh": 1, "gelu_erf": 2}
 
 
 def weight_bytes(d, ff, wtype):
@@ -208,6 +213,7 @@ def run_one(wname, M, steps, warmup, args):
     d, ff = w.d, w.ff
     path = args.path if args.path != "auto" else ("decode" if M <= 32 else "prefill")
     pcode = None if args.path == "auto" else PATHS[args.path]  # None: fmlp_forward itself
+    ex = args.activation != "silu" or args.residual  # the variants run fmlp_forward_ex
     log(f"[bench] {wname} M={M}: building {w.sets} weight set(s)")
     layers, xs = [], []
     host0 = None  # row-major / untiled copies of set 0 for the CPU baseline
@@ -227,12 +233,19 @@ def run_one(wname, M, steps, warmup, args):
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(F.fmlp_workspace_size(M, d, ff, 1 if w.wtype == "int4" else 0),
                      dtype=torch.uint8, device=dev)
+    res = synth.activations(M, d, 977, dev) if args.residual else None
+    hout = torch.empty((M, d), dtype=torch.bfloat16, device=dev) if args.residual else None
 
     def step(i):
         L = layers[i % w.sets]
         x, g = xs[i % w.sets]
-        fwd = F.fmlp_forward if pcode is None else functools.partial(F.fmlp_forward_path,
-                                                                      path=pcode)
+        if ex:
+            fwd = functools.partial(F.fmlp_forward_ex, path=pcode or 0,
+                                    activation=ACTS[args.activation], residual=res, h_out=hout)
+        elif pcode is None:
+            fwd = F.fmlp_forward
+        else:
+            fwd = functools.partial(F.fmlp_forward_path, path=pcode)
         if w.wtype == "int4":
             fwd(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws, ff=ff)
         else:
@@ -254,7 +267,7 @@ def run_one(wname, M, steps, warmup, args):
     ms_per_step = e0.elapsed_time(e1) / steps
     wall_ms_per_step = (t1 - t0) * 1e3 / steps
     tokens_per_s = M / (ms_per_step * 1e-3)
-    sb = step_bytes(M, d, ff, w.wtype)
+    sb = step_bytes(M, d, ff, w.wtype) + (4 * M * d if args.residual else 0)  # + r in, h out
     log(f"[bench] {ms_per_step*1e3:.2f} us/step (host wall {wall_ms_per_step*1e3:.2f}), "
         f"{sb / ms_per_step / 1e6:.1f} GB/s step")
 
@@ -308,7 +321,7 @@ def run_one(wname, M, steps, warmup, args):
             k["tflop_per_s"] = round(2.0 * M * ff * d / (t * 1e6), 1)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not ex:  # the oracle baseline times the plain Eq(1) step
         host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
         log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
         cpu = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds)
@@ -329,7 +342,8 @@ def run_one(wname, M, steps, warmup, args):
         "dtype": "int4-bf16" if w.wtype == "int4" else "bf16",
         "data": "synthetic",
         "config": {"workload": wname, "M": M, "d": d, "ff": ff, "weight_sets": w.sets,
-                   "wtype": w.wtype, "path": path, "parallelism": "none (1 GPU)"},
+                   "wtype": w.wtype, "path": path, "activation": args.activation,
+                   "residual": bool(args.residual), "parallelism": "none (1 GPU)"},
         "step_gb_per_s": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_tflop_per_s": round(step_tflops, 2),

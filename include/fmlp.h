@@ -72,6 +72,12 @@ enum fmlp_path {
                                M <= 8 */
 };
 
+enum fmlp_activation {
+  FMLP_ACT_SILU = 0,      /* SiLU(t) = t / (1 + e^-t): Eq(1), the default */
+  FMLP_ACT_GELU_TANH = 1, /* 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))) */
+  FMLP_ACT_GELU_ERF = 2   /* 0.5 t (1 + erf(t / sqrt 2)) = t Phi(t) */
+};
+
 /*
  * Weight storage. The library keeps every weight matrix in a
  * "fragment-tiled" layout: a storage permutation of the logical row-major
@@ -190,6 +196,29 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps,
                       const void* w_down, const void* down_scales, void* y,
                       int64_t M, int64_t d, int64_t ff, void* workspace,
                       size_t workspace_bytes, void* stream, int32_t path);
+
+/*
+ * fmlp_forward_path with two variants of the layer around Eq(1), both from
+ * the Together AI fusion post (blog.hotdry.top), which fuses a GELU MLP and
+ * fuses the residual add into the next normalisation:
+ *   activation : gate activation, enum fmlp_activation (FMLP_ACT_SILU is
+ *                Eq(1) of the FastTPS review; the GELU forms make the GeGLU
+ *                variant: a = GELU(W_gate n) * (W_up n)).
+ *   residual   : NULL, or bf16 [M, d], the previous sublayer's output r.
+ *                Then the row normalised is the residual stream
+ *                h = bf16_rne(x + r) (correctly rounded), and
+ *   h_out      : bf16 [M, d] receives h; NULL exactly when residual is NULL.
+ *                It must not overlap x, residual, gamma, the weights, y or
+ *                the workspace (it is written while they are read).
+ * Other arguments, errors and paths as fmlp_forward_path; an unknown
+ * activation, or only one of residual / h_out given, is
+ * FMLP_ERR_INVALID_ARG. The workspace size does not depend on either.
+ */
+int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void* gamma,
+                    float eps, int32_t activation, int32_t wtype, const void* w_gu,
+                    const void* gu_scales, const void* w_down, const void* down_scales, void* y,
+                    int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
+                    void* stream, int32_t path);
 
 /*
  * Per-kernel timing (measurement support, not needed for computing).

@@ -210,19 +210,29 @@ __device__ __forceinline__ u32x4 act_q4_chunk(u32x4 v, u32x4 g, float r) {
   return o;
 }
 
+// With res, the row normalised is the residual stream h = bf16_rne(x + res),
+// which is also stored to hout.
 __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma,
-                                                     float eps, uint16_t* __restrict__ n0, int d) {
+                                                     float eps, uint16_t* __restrict__ n0, int d,
+                                                     const uint16_t* __restrict__ res,
+                                                     uint16_t* __restrict__ hout) {
   __shared__ float part[8];
   const int64_t m = blockIdx.x;
   const uint16_t* xr = x + m * d;
   const int chunks = d >> 3, tid = threadIdx.x;
+  // chunk c of the row being normalised
+  auto row = [&](int c) {
+    const u32x4 xv = ld16(xr + c * 8);
+    return res ? add_bf16x8(xv, ld16(res + m * d + c * 8)) : xv;
+  };
   u32x4 v[kActPrepChunks], g[kActPrepChunks];
 #pragma unroll
   for (int i = 0; i < kActPrepChunks; ++i) {
     const int c = tid + i * 512;
-    v[i] = c < chunks ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    v[i] = c < chunks ? row(c) : u32x4{0u, 0u, 0u, 0u};
     g[i] = c < chunks ? ld16(gamma + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    if (hout && c < chunks) st16(hout + m * d + c * 8, v[i]);
   }
   float ss = 0.f;
 #pragma unroll
@@ -234,7 +244,8 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
       ss = fmaf(b, b, ss);
     }
   for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512) {  // only for very large d
-    const u32x4 w = ld16(xr + c * 8);
+    const u32x4 w = row(c);
+    if (hout) st16(hout + m * d + c * 8, w);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float a = bf16_lo(w[j]), b = bf16_hi(w[j]);
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
     if (c < chunks) st16(n0 + m * d + c * 8, act_q4_chunk(v[i], g[i], r));
   }
   for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512)
-    st16(n0 + m * d + c * 8, act_q4_chunk(ld16(xr + c * 8), ld16(gamma + c * 8), r));
+    st16(n0 + m * d + c * 8, act_q4_chunk(row(c), ld16(gamma + c * 8), r));
 }
 
 // ------------------------------------------------------------ GEMV core
@@ -269,6 +280,8 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
 //   ACT_Q4     : int4 weights; act0 = fp16 [M, K] in the int4 slot order
 //   ACT_HL_LDS : as ACT_HL, act0 / act1 staged in LDS by the workgroup
 //   ACT_Q4_LDS : as ACT_Q4, act0 staged in LDS by the workgroup
+//   ACT_XR     : as ACT_X on the residual stream h = bf16_rne(x + res) (res
+//                [M, K] like x); h is also stored to hout when that is given
 // Global activations are read into the ring with the weights. Staged ones
 // are [M, astride] rows whose first element is k = kbase; they are read
 // from LDS as they are used. stage_load() issues the workgroup's loads of
@@ -279,7 +292,7 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
 // 16 rows x 4 groups) + scales. The K units u0 .. u0+ucnt-1 are covered;
 // each wave walks units u0+wave, u0+wave+S, ...
 // with a P-deep ring of weight tiles (and global activation chunks) in flight.
-enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4 };
+enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5 };
 
 template <int MODE, int NCB, int RB, int S, int P, class StageLoad, class StageStore>
 __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
@@ -288,7 +301,9 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                                           const uint16_t* __restrict__ act1, int64_t rb0, int K,
                                           int M, int u0, int ucnt, f32x4 (&acc)[RB][NCB],
                                           float (&ss)[NCB], int astride, int kbase,
-                                          StageLoad&& stage_load, StageStore&& stage_store) {
+                                          StageLoad&& stage_load, StageStore&& stage_store,
+                                          const uint16_t* __restrict__ res = nullptr,
+                                          uint16_t* __restrict__ hout = nullptr) {
   constexpr bool kLds = MODE == ACT_HL_LDS || MODE == ACT_Q4_LDS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -308,7 +323,8 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (MODE == ACT_X || MODE == ACT_HL || MODE == ACT_HL_LDS) {
+  constexpr bool kX = MODE == ACT_X || MODE == ACT_XR;  // activations from x (and res)
+  if constexpr (kX || MODE == ACT_HL || MODE == ACT_HL_LDS) {
     // unit = one 32-column group
     const uint16_t* wt = static_cast<const uint16_t*>(w) + lane * 8;
     const int nit = wave < ucnt ? (ucnt - wave + S - 1) / S : 0;
@@ -327,8 +343,9 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
         for (int cb = 0; cb < NCB; ++cb) {
           hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
           if (MODE == ACT_HL) lb[slot][cb] = ld16(act1 + aoff[cb] + kb * 32);
+          if (MODE == ACT_XR) lb[slot][cb] = ld16(res + aoff[cb] + kb * 32);  // residual
         }
-        if (MODE == ACT_X) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
+        if (kX) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
       }
     };
     // no branches around the first loads, so that the compiler's wait for
@@ -369,9 +386,13 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
           if (it + P < nit) issue(p, it + P);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            if (MODE == ACT_X) {
-              // h holds x; build the hi/lo pair of gamma * x in place
-              const u32x4 xv = h[cb];
+            if (kX) {
+              // h holds x (l the residual); build the hi/lo pair of gamma * x in place
+              u32x4 xv = h[cb];
+              if (MODE == ACT_XR) {
+                xv = add_bf16x8(xv, l[cb]);
+                if (hout != nullptr && tok[cb]) st16(hout + aoff[cb] + kb * 32, xv);
+              }
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const float x0 = bf16_lo(xv[j]), x1 = bf16_hi(xv[j]);
@@ -510,11 +531,14 @@ constexpr int kLdsMaxM = 4;           // staged activations: at most this many t
 constexpr int kStageRegs = 2;         // staged chunks a gate/up thread holds in registers
 constexpr int kStageRegsDown = 4;     // the same for the down kernel
 
-template <int WK, int NCB, int RB, int S, int P, bool LDS>
+// RES (bf16): the activations are the residual stream h = bf16_rne(x + res);
+// workgroup 0 stores h to hout. act: the gate activation.
+template <int WK, int NCB, int RB, int S, int P, bool LDS, bool RES>
 __global__ __launch_bounds__(64 * S) void k_decode_gateup(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ act0,
     const uint16_t* __restrict__ act1, float eps, uint16_t* __restrict__ a0,
-    uint16_t* __restrict__ a1, int M, int d, int ff, int* __restrict__ cnt, int ncnt) {
+    uint16_t* __restrict__ a1, int M, int d, int ff, int* __restrict__ cnt, int ncnt, int act,
+    const uint16_t* __restrict__ res, uint16_t* __restrict__ hout) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < ncnt; i += 64 * S)
       __hip_atomic_store(cnt + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -595,8 +619,9 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
         w, sc, lhi, llo, rb0, d, M, 0, units, acc, ss, d, 0, stage_load, stage_store);
     stash<RB, NCB>(red, acc);
   } else {
-    gemv_core<WK == WK_BF16 ? ACT_X : ACT_Q4, NCB, RB, S, P>(w, sc, act0, act1, rb0, d, M, 0,
-                                                            units, acc, ss, d, 0, [] {}, [] {});
+    gemv_core<WK == WK_BF16 ? (RES ? ACT_XR : ACT_X) : ACT_Q4, NCB, RB, S, P>(
+        w, sc, act0, act1, rb0, d, M, 0, units, acc, ss, d, 0, [] {}, [] {}, res,
+        blockIdx.x == 0 ? hout : nullptr);
     stash<RB, NCB>(red, acc);
     if (WK == WK_BF16) {
       // lanes col, col+16, col+32, col+48 hold the same token
@@ -629,12 +654,12 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
     const int i = (int)(rb0 * 8) + p;  // index along ff
     if (WK == WK_BF16) {
       const float r = 1.0f / sqrtf(sst * inv_d + eps);
-      const float av = silu_mul(g * r, u * r);
+      const float av = act_mul(act, g * r, u * r);
       const uint16_t h = bf16_rne(av);
       a0[(int64_t)t * ff + i] = h;
       a1[(int64_t)t * ff + i] = bf16_rne(av - __uint_as_float((uint32_t)h << 16));
     } else {
-      const float av = silu_mul(g, u);
+      const float av = act_mul(act, g, u);
       const int mm = i & 7;
       const _Float16 hv = (_Float16)((mm & 1) ? av * 0.0625f : av);
       a0[(int64_t)t * ff + (i & ~7) + q4_slot(mm)] = __builtin_bit_cast(uint16_t, hv);
@@ -764,11 +789,14 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
 // them as soon as its gate/up loads have landed, before the cross-wave
 // reduction. No workgroup waits for another; k_partial_reduce sums the
 // ff/32 partials afterwards.
-template <int S, int P, int DQ>
+// RES: on the residual stream h = bf16_rne(x + res), which workgroup 0 stores
+// to hout; act: the gate activation.
+template <int S, int P, int DQ, bool RES>
 __global__ __launch_bounds__(64 * S) void k_decode_fused(
     const uint16_t* __restrict__ w_gu, const uint16_t* __restrict__ w_down,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
-    float* __restrict__ part, int M, int d, int ff) {
+    float* __restrict__ part, int M, int d, int ff, int act, const uint16_t* __restrict__ res,
+    uint16_t* __restrict__ hout) {
   constexpr int RB = 4;  // 4 x 16 W_gu rows = 32 gate/up pairs
   __shared__ f32x4 red[S * RB * 64];
   __shared__ float ssred[S * 16];
@@ -778,8 +806,9 @@ __global__ __launch_bounds__(64 * S) void k_decode_fused(
   const int sl = blockIdx.x;
   f32x4 acc[RB][1];
   float ss[1];
-  gemv_core<ACT_X, 1, RB, S, P>(w_gu, nullptr, x, gamma, (int64_t)sl * RB, d, M, 0, d >> 5, acc,
-                                ss, d, 0, [] {}, [] {});
+  gemv_core<RES ? ACT_XR : ACT_X, 1, RB, S, P>(w_gu, nullptr, x, gamma, (int64_t)sl * RB, d, M, 0,
+                                               d >> 5, acc, ss, d, 0, [] {}, [] {}, res,
+                                               blockIdx.x == 0 ? hout : nullptr);
 
   // down tiles (row block wave + j*S, K unit sl), j < nt
   const int64_t tstride = (int64_t)(ff >> 5) * 512 * S;  // elements between a wave's tiles
@@ -821,7 +850,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_fused(
           g += red[base][e];
           u += red[base + 1][e];
         }
-        av[k] = silu_mul(g * r, u * r);
+        av[k] = act_mul(act, g * r, u * r);
       }
       split_bf16_pair(av[0], av[1], h, l);
     }
@@ -911,10 +940,16 @@ bool single_pass_auto(int64_t M, int64_t d, int64_t ff, int wtype) {
 hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
   float* part = reinterpret_cast<float*>(p.ws);
   const int nw = p.ff / 32;
-  launch_kernel(KK_DECODE_FUSED_BF16, k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ>, dim3(nw),
-                dim3(64 * FMLP_FU_S), FMLP_FU_DYN_LDS, stream, static_cast<const uint16_t*>(p.w_gu),
-                static_cast<const uint16_t*>(p.w_down), p.x, p.gamma, p.eps, part, p.M, p.d,
-                p.ff);
+  auto go = [&](auto kern) {
+    launch_kernel(KK_DECODE_FUSED_BF16, kern, dim3(nw), dim3(64 * FMLP_FU_S), FMLP_FU_DYN_LDS,
+                  stream, static_cast<const uint16_t*>(p.w_gu),
+                  static_cast<const uint16_t*>(p.w_down), p.x, p.gamma, p.eps, part, p.M, p.d,
+                  p.ff, p.act, p.res, p.hout);
+  };
+  if (p.res)
+    go(k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ, true>);
+  else
+    go(k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ, false>);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   launch_kernel(KK_PARTIAL_REDUCE, k_partial_reduce, dim3(p.d / 16, p.M), dim3(256), 0, stream,
@@ -950,13 +985,17 @@ static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* 
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
   const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * FMLP_GU_S);
+  auto go = [&](auto kern, uint32_t shmem) {
+    launch_kernel(kind, kern, grid, block, shmem, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0,
+                  ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt, p.act, p.res, p.hout);
+  };
+  // the int4 path has added the residual in its prep kernel already
   if (kStage && lds)
-    launch_kernel(kind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, kStage>, grid, block,
-                  (uint32_t)lds_bytes, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1,
-                  p.M, p.d, p.ff, ws.cnt, ncnt);
+    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, kStage, false>, (uint32_t)lds_bytes);
+  else if (WK == WK_BF16 && p.res)
+    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false, WK == WK_BF16>, 0);
   else
-    launch_kernel(kind, k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false>, grid, block, 0, stream,
-                  p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0, ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt);
+    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false, false>, 0);
 }
 
 template <int WK, int NCB>
@@ -969,7 +1008,7 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   hipError_t e;
   if constexpr (WK == WK_INT4) {
     launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(512), 0, stream, p.x, p.gamma, p.eps,
-                  ws.n0, p.d);
+                  ws.n0, p.d, p.res, p.hout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // bf16 reads x and gamma directly; int4 reads the prepared fp16 n

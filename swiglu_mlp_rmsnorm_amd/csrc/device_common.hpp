@@ -85,4 +85,24 @@ __device__ __forceinline__ float silu_mul(float t, float u) {
   return t / (1.0f + expf(-t)) * u;
 }
 
+// Gate activations (enum fmlp_activation): 0 SiLU; 1 GELU, tanh form
+// 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))); 2 GELU, erf form
+// 0.5 t (1 + erf(t / sqrt 2)). Both GELU forms tend to -0 for t -> -inf.
+__device__ __forceinline__ float act_mul(int act, float t, float u) {
+  if (act == 1) return 0.5f * t * (1.0f + tanhf(0.7978845608028654f * (t + 0.044715f * t * t * t))) * u;
+  if (act == 2) return 0.5f * t * (1.0f + erff(t * 0.7071067811865476f)) * u;
+  return silu_mul(t, u);
+}
+
+// The residual stream: eight bf16 sums x + r, each rounded to bf16 (nearest
+// even). The binary32 sum of two bf16 values rounded to bf16 is the correctly
+// rounded sum (24 >= 2*8 + 2 bits, so the double rounding is innocuous).
+__device__ __forceinline__ u32x4 add_bf16x8(u32x4 x, u32x4 r) {
+  u32x4 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    h[j] = pack_bf16_rne(bf16_lo(x[j]) + bf16_lo(r[j]), bf16_hi(x[j]) + bf16_hi(r[j]));
+  return h;
+}
+
 }  // namespace fmlp

@@ -176,11 +176,16 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
   return b + 256;  // room to align the base
 }
 
-int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype,
-                      const void* w_gu, const void* gu_scales, const void* w_down,
-                      const void* down_scales, void* y, int64_t M, int64_t d, int64_t ff,
-                      void* workspace, size_t workspace_bytes, void* stream, int32_t path) {
+int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void* gamma,
+                    float eps, int32_t activation, int32_t wtype, const void* w_gu,
+                    const void* gu_scales, const void* w_down, const void* down_scales, void* y,
+                    int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
+                    void* stream, int32_t path) {
   if (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32) return FMLP_ERR_INVALID_ARG;
+  if (activation != FMLP_ACT_SILU && activation != FMLP_ACT_GELU_TANH &&
+      activation != FMLP_ACT_GELU_ERF)
+    return FMLP_ERR_INVALID_ARG;
+  if ((residual == nullptr) != (h_out == nullptr)) return FMLP_ERR_INVALID_ARG;
   if (path != FMLP_PATH_AUTO && path != FMLP_PATH_DECODE && path != FMLP_PATH_PREFILL &&
       path != FMLP_PATH_SINGLE_PASS)
     return FMLP_ERR_INVALID_ARG;
@@ -192,7 +197,8 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
   if (!x || !gamma || !w_gu || !w_down || !y || !workspace) return FMLP_ERR_INVALID_ARG;
   if (int4 && (!gu_scales || !down_scales)) return FMLP_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(gamma) || !aligned16(w_gu) || !aligned16(w_down) ||
-      !aligned16(y) || !aligned16(workspace) || (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))))
+      !aligned16(y) || !aligned16(workspace) || (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))) ||
+      !aligned16(residual) || !aligned16(h_out))
     return FMLP_ERR_ALIGNMENT;
 
   const bool single = path == FMLP_PATH_SINGLE_PASS ||
@@ -224,6 +230,18 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
   if (overlap(sw, span(x, (size_t)M * d * 2)) || overlap(sw, span(gamma, (size_t)d * 2)) ||
       overlap(sw, span(w_gu, wgu_b)) || overlap(sw, span(w_down, wd_b)))
     return FMLP_ERR_INVALID_ARG;
+  if (residual) {
+    // the residual stream is written while x and the residual are still read
+    const Span sr = span(residual, (size_t)M * d * 2), sh = span(h_out, (size_t)M * d * 2);
+    if (overlap(sh, span(x, (size_t)M * d * 2)) || overlap(sh, sr) ||
+        overlap(sh, span(gamma, (size_t)d * 2)) || overlap(sh, span(w_gu, wgu_b)) ||
+        overlap(sh, span(w_down, wd_b)) || overlap(sh, sy) || overlap(sh, sw) ||
+        overlap(sy, sr) || overlap(sw, sr))
+      return FMLP_ERR_INVALID_ARG;
+    if (int4 && (overlap(sh, span(gu_scales, (size_t)fmlp::int4_scale_bytes(2 * ff, d))) ||
+                 overlap(sh, span(down_scales, (size_t)fmlp::int4_scale_bytes(d, ff)))))
+      return FMLP_ERR_INVALID_ARG;
+  }
 
   if (int st = check_device()) return st;
 
@@ -242,11 +260,23 @@ int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype
   p.ff = (int)ff;
   p.ws = reinterpret_cast<char*>(abase);
   p.ws_bytes = workspace_bytes - (abase - wbase);
+  p.act = activation;
+  p.res = static_cast<const uint16_t*>(residual);
+  p.hout = static_cast<uint16_t*>(h_out);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = single   ? fmlp::launch_decode_fused(p, s)
                  : decode ? fmlp::launch_decode(p, s)
                           : fmlp::launch_prefill(p, s);
   return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype,
+                      const void* w_gu, const void* gu_scales, const void* w_down,
+                      const void* down_scales, void* y, int64_t M, int64_t d, int64_t ff,
+                      void* workspace, size_t workspace_bytes, void* stream, int32_t path) {
+  return fmlp_forward_ex(x, nullptr, nullptr, gamma, eps, FMLP_ACT_SILU, wtype, w_gu, gu_scales,
+                         w_down, down_scales, y, M, d, ff, workspace, workspace_bytes, stream,
+                         path);
 }
 
 int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype, const void* w_gu,

@@ -22,6 +22,9 @@ struct Problem {
   int M, d, ff;
   char* ws;                // workspace base (256-byte aligned)
   size_t ws_bytes;
+  int act = 0;             // gate activation (enum fmlp_activation)
+  const uint16_t* res = nullptr;  // bf16 [M, d] residual input, or null
+  uint16_t* hout = nullptr;       // bf16 [M, d] residual stream x + res (when res)
 };
 
 constexpr int kDecodeMaxM = 32;

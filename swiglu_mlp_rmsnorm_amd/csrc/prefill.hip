@@ -46,13 +46,15 @@ static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
 // ---------------------------------------------------------------- RMS pre-pass
 // (a) r_t = 1/sqrt(mean(x_t^2) + eps), one wave per token.
 __global__ __launch_bounds__(256) void k_rms_scale(const uint16_t* __restrict__ x, float eps,
-                                                   float* __restrict__ r, int M, int d) {
+                                                   float* __restrict__ r, int M, int d,
+                                                   const uint16_t* __restrict__ res) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= M) return;
   const uint16_t* xr = x + (int64_t)t * d;
   float ss = 0.f;
   for (int c = lane; c < (d >> 3); c += 64) {
-    const u32x4 v = ld16(xr + c * 8);
+    u32x4 v = ld16(xr + c * 8);
+    if (res) v = add_bf16x8(v, ld16(res + (int64_t)t * d + c * 8));  // residual stream
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
@@ -72,17 +74,22 @@ __global__ __launch_bounds__(256) void k_rms_tile(const uint16_t* __restrict__ x
                                                   const uint16_t* __restrict__ gamma,
                                                   const float* __restrict__ r,
                                                   uint16_t* __restrict__ n, int M, int d,
-                                                  int64_t slots) {
+                                                  int64_t slots, const uint16_t* __restrict__ res,
+                                                  uint16_t* __restrict__ hout) {
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= slots) return;
   const int slot = (int)(g & 63);
   const int64_t frag = g >> 6;                       // = tb * (d/16) + f
   const int fpb = d >> 4;                            // fragments per token block
   const int tb = (int)(frag / fpb), f = (int)(frag - (int64_t)tb * fpb);
-  int t = tb * 32 + (slot & 31);
-  t = t < M ? t : M - 1;
+  const int t0 = tb * 32 + (slot & 31);
+  const int t = t0 < M ? t0 : M - 1;  // padding tokens repeat the last one
   const int k = (f >> 1) * 32 + (f & 1) * 16 + (slot >> 5) * 8;
-  const u32x4 v = ld16(x + (int64_t)t * d + k);
+  u32x4 v = ld16(x + (int64_t)t * d + k);
+  if (res) {  // the residual stream h = bf16_rne(x + res), stored once per element
+    v = add_bf16x8(v, ld16(res + (int64_t)t * d + k));
+    if (t0 < M) st16(hout + (int64_t)t * d + k, v);
+  }
   const u32x4 gm = ld16(gamma + k);
   const float rt = r[t];
   u32x4 o;
@@ -215,7 +222,7 @@ template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 __global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
     GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
 k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
-            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end) {
+            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end, int act) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -409,8 +416,8 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
         const float v0 = acc[i][j][4 * r], v1 = acc[i][j][4 * r + 1];
         const float v2 = acc[i][j][4 * r + 2], v3 = acc[i][j][4 * r + 3];
         if (EPI == EPI_SILU_MUL_F16) {
-          const _Float16 a0 = (_Float16)silu_mul(v0, v1);
-          const _Float16 a1 = (_Float16)silu_mul(v2, v3);
+          const _Float16 a0 = (_Float16)act_mul(act, v0, v1);
+          const _Float16 a1 = (_Float16)act_mul(act, v2, v3);
           const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                                   ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
           *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) +
@@ -446,7 +453,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // with the fp32 partial epilogue).
 template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
-                                int K, int splits, hipStream_t stream, int n_begin, int n_end) {
+                                int K, int splits, hipStream_t stream, int n_begin, int n_end,
+                                int act) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -459,9 +467,16 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
   const int tiles = ((n_end - n_begin + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
                 k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>, dim3(tiles, splits), dim3(C::THREADS),
-                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end);
+                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end, act);
   return hipGetLastError();
 }
+
+#ifndef FMLP_S0_WGN
+#define FMLP_S0_WGN 4  // wave grid of the 256 x 256 tile
+#endif
+#ifndef FMLP_S0_WGM
+#define FMLP_S0_WGM 2
+#endif
 
 // Tile shapes: 0 = 256 x 256 (8 waves, 4 x 2), 1 = 256 x 128 (4 waves, 4 x 1),
 // 2 = 128 x 128 (4 waves, 2 x 2). tail_rows > 0: the last tail_rows feature
@@ -507,19 +522,24 @@ static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
 
 template <int EPI, bool AF16>
 static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
-                                   void* out, int M, int N, int K, hipStream_t stream) {
+                                   void* out, int M, int N, int K, hipStream_t stream,
+                                   int act = 0) {
   const int n_main = N - g.tail_rows;
   hipError_t e = hipSuccess;
   if (n_main > 0) {
     if (g.shape == 0)
-      e = launch_gemm_t<8, 8, 4, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<8, 8, FMLP_S0_WGN, FMLP_S0_WGM, EPI, AF16>(W, Act, out, M, N, K, g.splits,
+                                                                  stream, 0, n_main, act);
     else if (g.shape == 1)
-      e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main,
+                                               act);
     else
-      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main,
+                                               act);
   }
   if (e != hipSuccess || g.tail_rows == 0) return e;
-  return launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, n_main, N);
+  return launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, n_main, N,
+                                              act);
 }
 
 // Split off a tail launch when the 256 x 256 tiles fill r >= 1 whole rounds
@@ -584,7 +604,8 @@ static hipError_t prefill_gemms(const Problem& p, const PrefillWs& w, const uint
   const GemmPlan g1 =
       with_tail(plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false), (int)p.M, (int)(2 * p.ff));
   hipError_t e = launch_gemm_plan<EPI_SILU_MUL_F16, AF16>(g1, wgu, w.n, w.a, (int)p.M,
-                                                          (int)(2 * p.ff), (int)p.d, stream);
+                                                          (int)(2 * p.ff), (int)p.d, stream,
+                                                          p.act);
   if (e != hipSuccess) return e;
   if (g2.splits == 1)
     return launch_gemm_plan<EPI_STORE_BF16, AF16>(g2, wd, w.a, p.y, (int)p.M, (int)p.d, (int)p.ff,
@@ -611,10 +632,10 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   size_t total = 0;
   const PrefillWs w = prefill_ws(p.ws, p.M, p.d, p.ff, g2.splits, &total);
   launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
-                p.x, p.eps, w.r, (int)p.M, (int)p.d);
+                p.x, p.eps, w.r, (int)p.M, (int)p.d, p.res);
   const int64_t slots = pad32(p.M) * p.d / 8;
   launch_kernel(KK_RMS_TILE, k_rms_tile, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
-                stream, p.x, p.gamma, w.r, w.n, (int)p.M, (int)p.d, slots);
+                stream, p.x, p.gamma, w.r, w.n, (int)p.M, (int)p.d, slots, p.res, p.hout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.wtype == 0)

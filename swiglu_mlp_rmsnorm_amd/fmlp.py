@@ -36,9 +36,13 @@ FMLP_PATH_DECODE = 1
 FMLP_PATH_PREFILL = 2
 FMLP_PATH_SINGLE_PASS = 3
 
+FMLP_ACT_SILU = 0
+FMLP_ACT_GELU_TANH = 1
+FMLP_ACT_GELU_ERF = 2
+
 EXPORTS = (
     "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",
-    "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path",
+    "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
     "fmlp_profile_read", "fmlp_kernel_name",
 )
@@ -75,6 +79,8 @@ def lib() -> ctypes.CDLL:
         fwd = [P, P, ctypes.c_float, I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
         L.fmlp_forward.argtypes = fwd
         L.fmlp_forward_path.argtypes = fwd + [I32]
+        L.fmlp_forward_ex.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, P, P, P, P, P, I64, I64,
+                                      I64, P, SZ, P, I32]
         L.fmlp_status_string.argtypes = [ctypes.c_int]
         L.fmlp_status_string.restype = ctypes.c_char_p
         L.fmlp_last_hip_error.argtypes = []
@@ -85,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.fmlp_kernel_name.restype = ctypes.c_char_p
         for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
                      "fmlp_quantize_int4", "fmlp_dequant_int4",
-                     "fmlp_forward", "fmlp_forward_path", "fmlp_last_hip_error",
+                     "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex", "fmlp_last_hip_error",
                      "fmlp_profile_enable", "fmlp_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -198,7 +204,7 @@ def fmlp_workspace_size(M: int, d: int, ff: int, wtype: int = FMLP_W_BF16) -> in
 
 
 def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream, path,
-             ff=None):
+             ff=None, activation=None, residual=None, h_out=None):
     _need(x, torch.bfloat16, "x")
     _need(gamma, torch.bfloat16, "gamma")
     M, d = x.shape
@@ -236,6 +242,25 @@ def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, 
     args = (_ptr(x), _ptr(gamma), float(eps), wtype, _ptr(w_gu), _ptr(gu_scales), _ptr(w_down),
             _ptr(down_scales), _ptr(y), M, d, ff, _ptr(workspace), workspace.numel(),
             _stream(stream))
+    if activation is not None:  # fmlp_forward_ex
+        if residual is not None:
+            _need(residual, torch.bfloat16, "residual")
+            if residual.shape != (M, d):
+                raise ValueError("residual must be [M, d]")
+            if h_out is None:
+                h_out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+            _need(h_out, torch.bfloat16, "h_out")
+            if h_out.shape != (M, d):
+                raise ValueError("h_out must be [M, d]")
+        elif h_out is not None:
+            raise ValueError("h_out is written only together with a residual")
+        _check(lib().fmlp_forward_ex(_ptr(x), _ptr(residual), _ptr(h_out), _ptr(gamma),
+                                     float(eps), int(activation), wtype, _ptr(w_gu),
+                                     _ptr(gu_scales), _ptr(w_down), _ptr(down_scales), _ptr(y),
+                                     M, d, ff, _ptr(workspace), workspace.numel(),
+                                     _stream(stream), FMLP_PATH_AUTO if path is None else path),
+               "fmlp_forward_ex")
+        return y, h_out
     if path is None:
         _check(lib().fmlp_forward(*args), "fmlp_forward")
     else:
@@ -261,6 +286,16 @@ def fmlp_forward_path(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=N
     """fmlp_forward with the kernel path chosen by the caller (FMLP_PATH_*)."""
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
                     path, ff)
+
+
+def fmlp_forward_ex(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
+                    workspace=None, stream=None, path=FMLP_PATH_AUTO, ff=None,
+                    activation=FMLP_ACT_SILU, residual=None, h_out=None):
+    """fmlp_forward_path with a gate activation (FMLP_ACT_*) and an optional
+    residual input: then the row normalised is h = bf16(x + residual), also
+    returned in h_out. Returns (y, h_out or None)."""
+    return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
+                    path, ff, activation, residual, h_out)
 
 
 def fmlp_kernel_names() -> list:

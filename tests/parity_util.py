@@ -53,6 +53,14 @@ class Bf16Layer:
     def forward(self, x, g, eps, **kw):
         return F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **kw)
 
+    def oracle_ex(self, x, g, eps, act, res):
+        wg, wu, wd = self.host
+        return oracle.forward_unfused_ex(synth.bits(x), synth.bits(g), eps, wg, wu, wd, act=act,
+                                         residual=None if res is None else synth.bits(res))
+
+    def forward_ex(self, x, g, eps, **kw):
+        return F.fmlp_forward_ex(x, g, eps, self.wgu_t, self.wd_t, **kw)
+
 
 class Int4Layer:
     """Synthetic tiled int4 weights; the oracle untiles the same seeded bytes."""
@@ -72,6 +80,14 @@ class Int4Layer:
     def forward(self, x, g, eps, **kw):
         return F.fmlp_forward_path(x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d,
                                    ff=self.ff, **kw)
+
+    def oracle_ex(self, x, g, eps, act, res):
+        return oracle.forward_int4_ex(synth.bits(x), synth.bits(g), eps, *self.host, act=act,
+                                      residual=None if res is None else synth.bits(res))
+
+    def forward_ex(self, x, g, eps, **kw):
+        return F.fmlp_forward_ex(x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d, ff=self.ff,
+                                 **kw)
 
 
 def bf16_inputs(M, d, seed, device="cuda"):

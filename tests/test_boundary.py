@@ -80,6 +80,43 @@ def test_forward_rejects_before_any_hip_call(kw, status):
     assert fwd(**kw) == status
 
 
+A_EX = dict(A, r=ctypes.c_void_p(9 << 36), h=ctypes.c_void_p(10 << 36))
+
+
+def fwd_ex(M=1, d=256, ff=704, eps=1e-5, act=0, wtype=0, path=0, ws_bytes=BIG, **over):
+    p = dict(A_EX)
+    p.update(over)
+    return F.lib().fmlp_forward_ex(p["x"], p["r"], p["h"], p["g"], eps, act, wtype, p["wgu"],
+                                   p["sgu"], p["wd"], p["sd"], p["y"], M, d, ff, p["ws"],
+                                   ws_bytes, None, path)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act=3), F.FMLP_ERR_INVALID_ARG),
+    (dict(act=-1), F.FMLP_ERR_INVALID_ARG),
+    (dict(h=None), F.FMLP_ERR_INVALID_ARG),                  # residual without h_out
+    (dict(r=None), F.FMLP_ERR_INVALID_ARG),                  # h_out without residual
+    (dict(r=ctypes.c_void_p((9 << 36) + 2)), F.FMLP_ERR_ALIGNMENT),
+    (dict(h=ctypes.c_void_p((10 << 36) + 8)), F.FMLP_ERR_ALIGNMENT),
+    (dict(h=A["x"]), F.FMLP_ERR_INVALID_ARG),                # h_out over x
+    (dict(h=A["y"]), F.FMLP_ERR_INVALID_ARG),                # h_out over y
+    (dict(h=A["ws"]), F.FMLP_ERR_INVALID_ARG),               # h_out over the workspace
+    (dict(h=ctypes.c_void_p((9 << 36) + 256)), F.FMLP_ERR_INVALID_ARG),  # h_out over residual
+    (dict(r=A["y"]), F.FMLP_ERR_INVALID_ARG),                # y over residual
+    (dict(act=1, path=3, wtype=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(act=2, ws_bytes=100), F.FMLP_ERR_WORKSPACE),
+])
+def test_forward_ex_rejects_before_any_hip_call(kw, status):
+    assert fwd_ex(**kw) == status
+
+
+def test_forward_ex_zero_tokens_and_defaults():
+    assert fwd_ex(M=0, x=None, y=None, ws=None, r=None, h=None) == F.FMLP_OK
+    # without a residual and with SiLU the checks are those of fmlp_forward_path
+    for kw in (dict(d=48), dict(M=33, path=1), dict(ws_bytes=100)):
+        assert fwd_ex(r=None, h=None, **kw) == fwd(**kw)
+
+
 def test_int4_prefill_passes_the_host_checks():
     # int4 weights at M > 32 take the prefill path: the host-side checks
     # accept them exactly as they accept bf16 (the call then needs a GPU)

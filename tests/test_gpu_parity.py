@@ -273,3 +273,43 @@ def test_int4_end_to_end_from_bf16(tiny):
     y = F.fmlp_forward(x, g, EPS, q_gu, q_d, s_gu, s_d, ff=TINY_FF)
     b = synth.bits
     assert_parity(y, oracle.forward_int4(b(x), b(g), EPS, qg_o, sg_o, qd_o, sd_o), "int4 e2e")
+
+
+# ----------------------------------------------------------------- variants
+# Gate activation (SiLU / GELU tanh form / GELU erf form) and the residual
+# prologue h = bf16_rne(x + r) on every path; h is compared bit for bit.
+
+def _check_ex(layer, M, d, act, with_res, seed, **kw):
+    x, g = bf16_inputs(M, d, seed)
+    res = synth.activations(M, d, seed + 7, "cuda") if with_res else None
+    y, h = layer.forward_ex(x, g, EPS, activation=act, residual=res, **kw)
+    ref, href = layer.oracle_ex(x, g, EPS, act, res)
+    assert_parity(y, ref, f"act={act} res={with_res} M={M} {kw}")
+    if with_res:
+        assert np.array_equal(synth.bits(h), href), "residual stream differs"
+    else:
+        assert h is None
+
+
+@pytest.mark.parametrize("act", [F.FMLP_ACT_SILU, F.FMLP_ACT_GELU_TANH, F.FMLP_ACT_GELU_ERF])
+@pytest.mark.parametrize("with_res", [False, True])
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 3), (F.FMLP_PATH_DECODE, 20),
+                                    (SP, 2), (F.FMLP_PATH_PREFILL, 70)])
+def test_variants_bf16(tiny, act, with_res, path, M):
+    _check_ex(tiny, M, TINY_D, act, with_res, 900 + M, path=path)
+
+
+@pytest.mark.parametrize("act", [F.FMLP_ACT_GELU_TANH, F.FMLP_ACT_GELU_ERF])
+@pytest.mark.parametrize("with_res", [False, True])
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 1), (F.FMLP_PATH_DECODE, 9),
+                                    (F.FMLP_PATH_DECODE, 17), (F.FMLP_PATH_PREFILL, 40)])
+def test_variants_int4(act, with_res, path, M):
+    layer = Int4Layer(1024, 2048, 61)
+    _check_ex(layer, M, 1024, act, with_res, 930 + M, path=path)
+
+
+@pytest.mark.parametrize("d,ff,M", [(3072, 8192, 1), (4096, 1024, 16), (18432, 64, 2)])
+def test_residual_stream_bit_exact_at_larger_d(d, ff, M):
+    # d = 18432 makes the int4 prep take its second pass over the row
+    _check_ex(Bf16Layer(d, ff, 62), M, d, F.FMLP_ACT_GELU_ERF, True, 960 + M)
+    _check_ex(Int4Layer(d, ff, 63), M, d, F.FMLP_ACT_SILU, True, 970 + M)
