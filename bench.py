@@ -320,6 +320,17 @@ def run_one(wname, M, steps, warmup, args):
         elif name == "gemm_down_f16":
             k["tflop_per_s"] = round(2.0 * M * ff * d / (t * 1e6), 1)
 
+    # The HBM read rate a plain streaming kernel reaches on exactly the bytes
+    # the dominant decode kernel streams (the gate/up weights of each rotated
+    # set, read once per launch): the practical ceiling its roofline fraction
+    # should be read against.
+    ceiling = None
+    if path == "decode" and not args.no_profile:
+        ceiling = read_ceiling([L[0] for L in layers], steps)
+        if roofline is not None and ceiling:
+            ceiling["dominant_kernel_frac_of_ceiling"] = round(
+                roofline["achieved"] / ceiling["gb_per_s"], 4)
+
     cpu = None
     if not args.no_cpu_baseline and not ex:  # the oracle baseline times the plain Eq(1) step
         host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
@@ -350,12 +361,40 @@ def run_one(wname, M, steps, warmup, args):
         "step_mfma_frac": round(step_tflops / MFMA_PEAK_TFLOPS, 4),
         "host_wall_ms_per_step": round(wall_ms_per_step, 6),
         "roofline": roofline,
+        "read_ceiling": ceiling,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
     del layers, xs
     torch.cuda.empty_cache()
     return rec
+
+
+def read_ceiling(buffers, steps):
+    """Streaming-read probe (fmlp_read_probe) over the rotated weight buffers,
+    timed with the library's dispatch-stamped events; the best of three grid
+    sizes."""
+    import torch
+    from swiglu_mlp_rmsnorm_amd import fmlp as F
+    nbytes = buffers[0].numel() * buffers[0].element_size()
+    best = None
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device=buffers[0].device)
+    for wgs in (512, 1024, 2048):
+        for i in range(2 * len(buffers)):
+            F.fmlp_read_probe(buffers[i % len(buffers)], sink, wgs)
+        torch.cuda.synchronize()
+        F.fmlp_profile_enable(True)
+        for i in range(steps):
+            F.fmlp_read_probe(buffers[i % len(buffers)], sink, wgs)
+        torch.cuda.synchronize()
+        n, ms = F.fmlp_profile_read().get("read_probe", (0, 0.0))
+        F.fmlp_profile_enable(False)
+        if n:
+            gbs = nbytes * n / (ms * 1e-3) / 1e9
+            if best is None or gbs > best["gb_per_s"]:
+                best = {"bytes_per_launch": nbytes, "workgroups": wgs,
+                        "us_per_launch": round(ms * 1e3 / n, 3), "gb_per_s": round(gbs, 1)}
+    return best
 
 
 def default_steps(w, M):
@@ -385,8 +424,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
-              "multi-GPU path: every workload runs on a single MI355X.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the fused MLP here "
+              "has no multi-GPU path, and every workload runs on a single MI355X.", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -233,6 +233,20 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
  * throughput runs.
  */
 int fmlp_profile_enable(int32_t on);
+
+/*
+ * Streaming-read probe (measurement support, not part of the computation):
+ * reads `bytes` of device memory at src once, with 16-byte nontemporal loads
+ * in a grid-stride loop over `workgroups` workgroups of 256 threads, and
+ * stores one 32-bit XOR of its reads per thread to sink (workgroups*256
+ * words, caller-owned). It gives the HBM read rate that a kernel reading the
+ * same number of bytes per launch can reach, the yardstick for the weight
+ * streams of the decode kernels. Timed like the other kernels while
+ * profiling is enabled (kind "read_probe"). src 16-byte aligned, bytes a
+ * multiple of 16, sink 4-byte aligned; else FMLP_ERR_ALIGNMENT. Asynchronous.
+ */
+int fmlp_read_probe(const void* src, int64_t bytes, void* sink, int32_t workgroups,
+                    void* stream);
 int fmlp_profile_read(int32_t kind, int64_t* launches, double* total_ms);
 const char* fmlp_kernel_name(int32_t kind);
 

@@ -26,6 +26,7 @@ enum KernelKind {
   KK_SPLITK_REDUCE,
   KK_DECODE_FUSED_BF16,
   KK_PARTIAL_REDUCE,
+  KK_READ_PROBE,
   KK_COUNT
 };
 

@@ -44,7 +44,7 @@ EXPORTS = (
     "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",
     "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
-    "fmlp_profile_read", "fmlp_kernel_name",
+    "fmlp_profile_read", "fmlp_kernel_name", "fmlp_read_probe",
 )
 
 
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.fmlp_profile_enable.argtypes = [I32]
         L.fmlp_profile_read.argtypes = [I32, ctypes.POINTER(ctypes.c_int64),
                                         ctypes.POINTER(ctypes.c_double)]
+        L.fmlp_read_probe.argtypes = [P, I64, P, I32, P]
+        L.fmlp_read_probe.restype = ctypes.c_int
         L.fmlp_kernel_name.argtypes = [I32]
         L.fmlp_kernel_name.restype = ctypes.c_char_p
         for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
@@ -296,6 +298,17 @@ def fmlp_forward_ex(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=Non
     returned in h_out. Returns (y, h_out or None)."""
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
                     path, ff, activation, residual, h_out)
+
+
+def fmlp_read_probe(src, sink, workgroups: int, stream=None) -> None:
+    """Read all of the device tensor src once (measurement probe); sink is
+    an int32 device tensor of at least workgroups*256 elements."""
+    if not (src.is_cuda and sink.is_cuda):
+        raise ValueError("fmlp_read_probe takes device tensors")
+    if sink.numel() * sink.element_size() < workgroups * 256 * 4:
+        raise ValueError("sink too small")
+    _check(lib().fmlp_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 int(workgroups), _stream(stream)), "fmlp_read_probe")
 
 
 def fmlp_kernel_names() -> list:

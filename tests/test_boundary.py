@@ -117,6 +117,17 @@ def test_forward_ex_zero_tokens_and_defaults():
         assert fwd_ex(r=None, h=None, **kw) == fwd(**kw)
 
 
+def test_read_probe_validation():
+    L = F.lib()
+    src, sink = ctypes.c_void_p(1 << 36), ctypes.c_void_p(2 << 36)
+    assert L.fmlp_read_probe(None, 1024, sink, 256, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_read_probe(src, 0, sink, 256, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_read_probe(src, 1024, sink, 0, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_read_probe(src, 1000, sink, 256, None) == F.FMLP_ERR_ALIGNMENT
+    assert L.fmlp_read_probe(ctypes.c_void_p((1 << 36) + 8), 1024, sink, 256,
+                             None) == F.FMLP_ERR_ALIGNMENT
+
+
 def test_int4_prefill_passes_the_host_checks():
     # int4 weights at M > 32 take the prefill path: the host-side checks
     # accept them exactly as they accept bf16 (the call then needs a GPU)
