@@ -52,6 +52,12 @@
 #ifndef FMLP_GU_P
 #define FMLP_GU_P 2   // ring depth (tiles in flight per wave and row block)
 #endif
+#ifndef FMLP_GU_S_MANY
+#define FMLP_GU_S_MANY 4     // waves per gate/up workgroup when there are many workgroups
+#endif
+#ifndef FMLP_GU_MANY_WGS
+#define FMLP_GU_MANY_WGS 768  // "many": at least this many gate/up workgroups
+#endif
 #ifndef FMLP_DN_S
 #define FMLP_DN_S 16
 #endif
@@ -99,6 +105,9 @@
 #endif
 #ifndef FMLP_BIG_GU_RB2
 #define FMLP_BIG_GU_RB2 4  // bf16 gate/up row blocks per workgroup for M > 16
+#endif
+#ifndef FMLP_MASK_ACT
+#define FMLP_MASK_ACT 0    // activation loads only in lanes that hold a token
 #endif
 #ifndef FMLP_DEC_LDS
 #define FMLP_DEC_LDS 1     // stage small-M activations in LDS (0: read them per wave)
@@ -339,6 +348,19 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) wb[slot][rb] = ld16_stream(wt + ((rb0 + rb) * nkb + kb) * 512);
       if constexpr (!kLds) {
+#if FMLP_MASK_ACT
+        // only lanes that hold a token load activations (at M = 1 that is 4
+        // lanes of 64; the rest would re-read the same 64 bytes)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          if (tok[cb]) {
+            hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
+            if (MODE == ACT_HL) lb[slot][cb] = ld16(act1 + aoff[cb] + kb * 32);
+            if (MODE == ACT_XR) lb[slot][cb] = ld16(res + aoff[cb] + kb * 32);  // residual
+          }
+        }
+        if (kX && tok[0]) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
+#else
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
@@ -346,6 +368,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
           if (MODE == ACT_XR) lb[slot][cb] = ld16(res + aoff[cb] + kb * 32);  // residual
         }
         if (kX) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
+#endif
       }
     };
     // no branches around the first loads, so that the compiler's wait for
@@ -436,7 +459,8 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
         for (int j = 0; j < 4; ++j) {
           const int kb = q * 4 + j < nkb ? q * 4 + j : nkb - 1;  // padding groups are skipped
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) ab[slot][j][cb] = ld16(act0 + aoff[cb] + kb * 32);
+          for (int cb = 0; cb < NCB; ++cb)
+            if (!FMLP_MASK_ACT || tok[cb]) ab[slot][j][cb] = ld16(act0 + aoff[cb] + kb * 32);
         }
       }
     };
@@ -528,7 +552,7 @@ __device__ __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RB][NCB]) {
 // Workgroup 0 also clears the down kernel's split-K arrival counters (ncnt of
 // them; agent-coherent stores, read by that kernel's atomics).
 constexpr int kLdsMaxM = 4;           // staged activations: at most this many tokens
-constexpr int kStageRegs = 2;         // staged chunks a gate/up thread holds in registers
+constexpr int kStageRegs = 2;         // staged chunks a gate/up thread holds in registers (8 waves)
 constexpr int kStageRegsDown = 4;     // the same for the down kernel
 
 // RES (bf16): the activations are the residual stream h = bf16_rne(x + res);
@@ -554,10 +578,11 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
     uint16_t* lhi = stage_lds;
     uint16_t* llo = stage_lds + (int64_t)M * d;
     const int cpt = d >> 3, nch = M * cpt;  // 16-byte chunks per token, in all
-    u32x4 sx[kStageRegs], sg[kStageRegs];
+    constexpr int kSR = kStageRegs * 8 / S > 0 ? kStageRegs * 8 / S : 1;  // chunks per thread
+    u32x4 sx[kSR], sg[kSR];
     auto stage_load = [&]() {
 #pragma unroll
-      for (int i = 0; i < kStageRegs; ++i) {
+      for (int i = 0; i < kSR; ++i) {
         int c = threadIdx.x + i * 64 * S;
         c = c < nch ? c : nch - 1;  // loaded, not stored
         const int t = c / cpt, kc = c - t * cpt;
@@ -596,11 +621,11 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
       // unconditional stores keep the compiler from sinking the staged
       // loads below the weight loads
 #pragma unroll
-      for (int i = 0; i < kStageRegs; ++i) {
+      for (int i = 0; i < kSR; ++i) {
         const int c = threadIdx.x + i * 64 * S;
         put(c < nch ? c : nch - 1, sx[i], sg[i], c < nch);
       }
-      for (int c = threadIdx.x + kStageRegs * 64 * S; c < nch; c += 64 * S) {
+      for (int c = threadIdx.x + kSR * 64 * S; c < nch; c += 64 * S) {
         const int kc = c % cpt;
         put(c, ld16(act0 + (int64_t)(c / cpt) * d + kc * 8),
             WK == WK_BF16 ? ld16(act1 + kc * 8) : u32x4{0u, 0u, 0u, 0u}, true);
@@ -976,26 +1001,40 @@ static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool l
                   p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d, p.ff, ws.part, ws.cnt);
 }
 
-template <int WK, int NCB, int RB>
-static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
-                          const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
-                          hipStream_t stream) {
+template <int WK, int NCB, int RB, int S>
+static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
+                            const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
+                            hipStream_t stream) {
   constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
   constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
-  const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * FMLP_GU_S);
+  const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * S);
   auto go = [&](auto kern, uint32_t shmem) {
     launch_kernel(kind, kern, grid, block, shmem, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0,
                   ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt, p.act, p.res, p.hout);
   };
   // the int4 path has added the residual in its prep kernel already
   if (kStage && lds)
-    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, kStage, false>, (uint32_t)lds_bytes);
+    go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false>, (uint32_t)lds_bytes);
   else if (WK == WK_BF16 && p.res)
-    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false, WK == WK_BF16>, 0);
+    go(k_decode_gateup<WK, NCB, RB, S, GP, false, WK == WK_BF16>, 0);
   else
-    go(k_decode_gateup<WK, NCB, RB, FMLP_GU_S, GP, false, false>, 0);
+    go(k_decode_gateup<WK, NCB, RB, S, GP, false, false>, 0);
+}
+
+// Waves per workgroup: with many bf16 workgroups (Llama-8B-sized layers and
+// up) fewer waves per CU stream faster (measured on MI355X: Llama-8B gate/up
+// 44 -> 41 us at 4 waves, M = 1 and 4); Phi-3-sized layers, and int4 (whose
+// 4-wave version measured 10 % slower), keep 8.
+template <int WK, int NCB, int RB>
+static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
+                          const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
+                          hipStream_t stream) {
+  if (WK == WK_BF16 && NCB == 1 && (2 * p.ff) / (16 * RB) >= FMLP_GU_MANY_WGS)
+    launch_gateup_s<WK, NCB, RB, FMLP_GU_S_MANY>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
+  else
+    launch_gateup_s<WK, NCB, RB, FMLP_GU_S>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
 }
 
 template <int WK, int NCB>

@@ -129,7 +129,9 @@ def test_both_paths_at_the_crossover(tiny, M, path):
 
 @pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 40), (512, 1376, 5),
                                     (512, 1376, 70), (160, 224, 17), (256, 4096, 100),
-                                    (288, 2048, 33), (256, 38400, 33)])
+                                    (288, 2048, 33), (256, 38400, 33),
+                                    # >= 768 gate/up workgroups: the 4-wave gate/up launch
+                                    (256, 6144, 1), (96, 6176, 3)])
 def test_odd_shapes(d, ff, M):
     layer = Bf16Layer(d, ff, 20 + d)
     x, g = bf16_inputs(M, d, 400 + M)
@@ -308,7 +310,8 @@ def test_variants_int4(act, with_res, path, M):
     _check_ex(layer, M, 1024, act, with_res, 930 + M, path=path)
 
 
-@pytest.mark.parametrize("d,ff,M", [(3072, 8192, 1), (4096, 1024, 16), (18432, 64, 2)])
+@pytest.mark.parametrize("d,ff,M", [(3072, 8192, 1), (4096, 1024, 16), (18432, 64, 2),
+                                    (256, 6144, 2)])
 def test_residual_stream_bit_exact_at_larger_d(d, ff, M):
     # d = 18432 makes the int4 prep take its second pass over the row
     _check_ex(Bf16Layer(d, ff, 62), M, d, F.FMLP_ACT_GELU_ERF, True, 960 + M)
