@@ -172,7 +172,22 @@ __global__ __launch_bounds__(256) void k_dequant_f16_tiled(const uint32_t* __res
 // run on the same XCD and share its L2.
 // Epilogues: SiLU*mul to the fp16 tiled activations (gate/up), bf16 y, or
 // an fp32 split-K partial (slice blockIdx.y of [splits, M, N]).
-enum { EPI_SILU_MUL_F16 = 0, EPI_STORE_BF16 = 1, EPI_STORE_F32 = 2 };
+// Epilogues. The three gate epilogues differ only in the activation, which
+// is a compile-time constant: a runtime choice inlines every activation at
+// each of the unrolled output sites and triples the kernel's code.
+enum {
+  EPI_SILU_MUL_F16 = 0,
+  EPI_STORE_BF16 = 1,
+  EPI_STORE_F32 = 2,
+  EPI_GELU_TANH_MUL_F16 = 3,
+  EPI_GELU_ERF_MUL_F16 = 4
+};
+constexpr bool epi_gate(int epi) {
+  return epi == EPI_SILU_MUL_F16 || epi == EPI_GELU_TANH_MUL_F16 || epi == EPI_GELU_ERF_MUL_F16;
+}
+constexpr int epi_act(int epi) {  // enum fmlp_activation
+  return epi == EPI_GELU_TANH_MUL_F16 ? 1 : epi == EPI_GELU_ERF_MUL_F16 ? 2 : 0;
+}
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
@@ -222,7 +237,7 @@ template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 __global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
     GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
 k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
-            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end, int act) {
+            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -415,9 +430,9 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
         if (f0 >= n_end) continue;
         const float v0 = acc[i][j][4 * r], v1 = acc[i][j][4 * r + 1];
         const float v2 = acc[i][j][4 * r + 2], v3 = acc[i][j][4 * r + 3];
-        if (EPI == EPI_SILU_MUL_F16) {
-          const _Float16 a0 = (_Float16)act_mul(act, v0, v1);
-          const _Float16 a1 = (_Float16)act_mul(act, v2, v3);
+        if (epi_gate(EPI)) {
+          const _Float16 a0 = (_Float16)act_mul(epi_act(EPI), v0, v1);
+          const _Float16 a1 = (_Float16)act_mul(epi_act(EPI), v2, v3);
           const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                                   ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
           *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) +
@@ -453,8 +468,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 // with the fp32 partial epilogue).
 template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
-                                int K, int splits, hipStream_t stream, int n_begin, int n_end,
-                                int act) {
+                                int K, int splits, hipStream_t stream, int n_begin, int n_end) {
   using C = GemmCfg<NB, MB, WGN, WGM>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -465,9 +479,9 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
   });
   if (attr_err != hipSuccess) return attr_err;
   const int tiles = ((n_end - n_begin + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
-  launch_kernel(EPI == EPI_SILU_MUL_F16 ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
+  launch_kernel(epi_gate(EPI) ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
                 k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>, dim3(tiles, splits), dim3(C::THREADS),
-                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end, act);
+                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end);
   return hipGetLastError();
 }
 
@@ -522,24 +536,20 @@ static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
 
 template <int EPI, bool AF16>
 static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
-                                   void* out, int M, int N, int K, hipStream_t stream,
-                                   int act = 0) {
+                                   void* out, int M, int N, int K, hipStream_t stream) {
   const int n_main = N - g.tail_rows;
   hipError_t e = hipSuccess;
   if (n_main > 0) {
     if (g.shape == 0)
       e = launch_gemm_t<8, 8, FMLP_S0_WGN, FMLP_S0_WGM, EPI, AF16>(W, Act, out, M, N, K, g.splits,
-                                                                  stream, 0, n_main, act);
+                                                                  stream, 0, n_main);
     else if (g.shape == 1)
-      e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main,
-                                               act);
+      e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
     else
-      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main,
-                                               act);
+      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
   }
   if (e != hipSuccess || g.tail_rows == 0) return e;
-  return launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, n_main, N,
-                                              act);
+  return launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, n_main, N);
 }
 
 // Split off a tail launch when the 256 x 256 tiles fill r >= 1 whole rounds
@@ -603,9 +613,13 @@ static hipError_t prefill_gemms(const Problem& p, const PrefillWs& w, const uint
                                 const uint16_t* wd, const GemmPlan& g2, hipStream_t stream) {
   const GemmPlan g1 =
       with_tail(plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false), (int)p.M, (int)(2 * p.ff));
-  hipError_t e = launch_gemm_plan<EPI_SILU_MUL_F16, AF16>(g1, wgu, w.n, w.a, (int)p.M,
-                                                          (int)(2 * p.ff), (int)p.d, stream,
-                                                          p.act);
+  const int N1 = (int)(2 * p.ff), M1 = (int)p.M, K1 = (int)p.d;
+  hipError_t e =
+      p.act == 1   ? launch_gemm_plan<EPI_GELU_TANH_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1,
+                                                                  stream)
+      : p.act == 2 ? launch_gemm_plan<EPI_GELU_ERF_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1,
+                                                                 stream)
+                   : launch_gemm_plan<EPI_SILU_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1, stream);
   if (e != hipSuccess) return e;
   if (g2.splits == 1)
     return launch_gemm_plan<EPI_STORE_BF16, AF16>(g2, wd, w.a, p.y, (int)p.M, (int)p.d, (int)p.ff,
