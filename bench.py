@@ -46,6 +46,8 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the five repeat windows and the graph-captured timing")
     ap.add_argument("--path", choices=sorted(PATHS), default="auto",
                     help="kernel path (fmlp_forward_path); auto is fmlp_forward's own choice")
     ap.add_argument("--activation", choices=sorted(ACTS), default="silu",
@@ -271,6 +273,29 @@ def run_one(wname, M, steps, warmup, args):
     log(f"[bench] {ms_per_step*1e3:.2f} us/step (host wall {wall_ms_per_step*1e3:.2f}), "
         f"{sb / ms_per_step / 1e6:.1f} GB/s step")
 
+    # Spread: five more windows of the same length, after the timed region
+    # (median, p10, p90 of their us/step); and the same steps captured once as
+    # a HIP graph (one rotation of weight sets) and replayed, which shows what
+    # host launch overhead the plain loop carries.
+    spread = None
+    if not args.no_spread:
+        win = []
+        for r in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(steps):
+                step(i)
+            b.record()
+            torch.cuda.synchronize()
+            win.append(a.elapsed_time(b) * 1e3 / steps)
+        win.sort()
+        spread = {"windows": 5, "steps_per_window": steps,
+                  "us_per_step_p10": round(win[0] + 0.4 * (win[1] - win[0]), 3),
+                  "us_per_step_median": round(win[2], 3),
+                  "us_per_step_p90": round(win[3] + 0.6 * (win[4] - win[3]), 3)}
+        spread["graph_us_per_step"] = graph_us_per_step(step, w.sets, steps)
+        log(f"[bench] spread {json.dumps(spread)}")
+
     # per-kernel durations from HIP events recorded by the library on its launch stream
     kernels = {}
     if not args.no_profile:
@@ -362,12 +387,45 @@ def run_one(wname, M, steps, warmup, args):
         "host_wall_ms_per_step": round(wall_ms_per_step, 6),
         "roofline": roofline,
         "read_ceiling": ceiling,
+        "spread": spread,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
     del layers, xs
     torch.cuda.empty_cache()
     return rec
+
+
+def graph_us_per_step(step, period, steps):
+    """Capture `period` consecutive steps (one rotation of the weight sets) in
+    a HIP graph, replay it to cover about `steps` steps, and return the GPU
+    time per step; None if capture fails."""
+    import torch
+    try:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(period):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+    except RuntimeError as e:
+        log(f"[bench] graph capture failed: {e}")
+        return None
+    reps = max(1, steps // period)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (reps * period)
+    del g
+    return round(us, 3)
 
 
 def read_ceiling(buffers, steps):

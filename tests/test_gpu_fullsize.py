@@ -31,27 +31,33 @@ def sample_rows(M, n):
     return sorted(set(int(r) for r in np.linspace(0, M - 1, n)))
 
 
-@pytest.mark.parametrize("wname,M", CASES)
-def test_full_size_parity(wname, M):
+# the last of each decode workload's rotated weight sets as well as the first
+LAST_SET_CASES = [(n, 1, synth.WORKLOADS[n].sets - 1) for n in (
+    "phi3mini_decode_d3072_ff8192", "llama8b_decode_d4096_ff14336",
+    "llama70b_int4_decode_d8192_ff28672")]
+
+
+@pytest.mark.parametrize("wname,M,layer", [(n, M, 0) for n, M in CASES] + LAST_SET_CASES)
+def test_full_size_parity(wname, M, layer):
     w = synth.WORKLOADS[wname]
-    x, g = synth.inputs(w, M, "cuda")
+    x, g = synth.inputs(w, M, "cuda", layer=layer)
     b = synth.bits
     if w.wtype == "int4":
-        q_gu, s_gu, q_d, s_d = synth.layer_int4(w, 0, "cuda")
+        q_gu, s_gu, q_d, s_d = synth.layer_int4(w, layer, "cuda")
         y = F.fmlp_forward(x, g, synth.EPS, q_gu, q_d, s_gu, s_d, ff=w.ff)
         rows = sample_rows(M, 2)
         host = (*oracle.untile_int4(b(q_gu), b(s_gu), 2 * w.ff, w.d),
                 *oracle.untile_int4(b(q_d), b(s_d), w.d, w.ff))
         ref = oracle.forward_int4(b(x)[rows], b(g), synth.EPS, *host)
     else:
-        wg, wu, wd = synth.layer_bf16(w, 0, "cuda")
+        wg, wu, wd = synth.layer_bf16(w, layer, "cuda")
         y = F.fmlp_forward(x, g, synth.EPS, F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
         rows = sample_rows(M, 8 if M <= 32 else 4)
         ref = oracle.forward_unfused(b(x)[rows], b(g), synth.EPS, b(wg), b(wu), b(wd))
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(y.float()))
-    mx, l1 = assert_parity(y[rows], ref, f"{wname} M={M}")
-    print(f"{wname} M={M} rows={rows}: max/rms={mx:.3e} L1={l1:.3e}")
+    mx, l1 = assert_parity(y[rows], ref, f"{wname} M={M} set {layer}")
+    print(f"{wname} M={M} set {layer} rows={rows}: max/rms={mx:.3e} L1={l1:.3e}")
 
 
 @pytest.mark.parametrize("wname,M", [("phi3mini_decode_d3072_ff8192", 1),
