@@ -109,6 +109,9 @@
 #ifndef FMLP_MASK_ACT
 #define FMLP_MASK_ACT 0    // activation loads only in lanes that hold a token
 #endif
+#ifndef FMLP_DEC_LDS_BF16_GU
+#define FMLP_DEC_LDS_BF16_GU 1  // also stage bf16 gate/up activations (small M, no residual)
+#endif
 #ifndef FMLP_DEC_LDS
 #define FMLP_DEC_LDS 1     // stage small-M activations in LDS (0: read them per wave)
 #endif
@@ -1006,7 +1009,8 @@ static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t
                             const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
                             hipStream_t stream) {
   constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
-  constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
+  constexpr bool kStage =
+      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_GU);
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
   const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * S);
@@ -1065,17 +1069,20 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const bool drb = !bdrb && DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
   const int dn_rb = bdrb ? BDRB : drb ? DRB : 1;
   const int splits = drb ? 1 : down_splits(p.d / (16 * dn_rb), p.ff, WK == WK_INT4);
-  // int4 activations staged in LDS for small M, when they fit without
-  // lowering the number of workgroups resident per CU (bytes per workgroup).
-  // Measured on MI355X: 70B-shaped int4 layers at M=1 gain 13 % (gate/up) and
-  // 10 % (down); bf16 layers gain at most 3 % in gate/up and lose up to 14 %
-  // in down, so they keep reading their activations per wave.
+  // Activations staged in LDS for small M, when they fit without lowering
+  // the number of workgroups resident per CU (bytes per workgroup).
+  // Measured on MI355X at M=1: int4 (70B shape) gains 13 % in gate/up and
+  // 10 % in down; bf16 gate/up gains 3-4 % (Phi-3, Llama-8B), while bf16
+  // down loses up to 14 %, so the bf16 down kernel reads its a per wave.
   auto lds_budget = [](int64_t wgs) -> int64_t { return wgs <= 256 ? 96 * 1024 : 32 * 1024; };
   constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2;
   const bool gu_big = big && WK == WK_BF16;
   const int64_t gu_wgs = (2 * p.ff) / (16 * (gu_big ? BGRB : RB));
   const int64_t gu_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * p.d;
-  const bool gl = kStage && p.M <= kLdsMaxM && gu_lds <= lds_budget(gu_wgs);
+  // (bf16 gate/up staging, when enabled, does not cover the residual prologue)
+  constexpr bool kStageGu = FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_GU);
+  const bool gl = kStageGu && (WK == WK_INT4 || !p.res) && p.M <= kLdsMaxM &&
+                  gu_lds <= lds_budget(gu_wgs);
   const int ukd = WK == WK_BF16 ? 32 : 128, nud = (p.ff + ukd - 1) / ukd;
   const int64_t dn_wgs = (p.d / (16 * dn_rb)) * splits;
   const int64_t dn_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * ((nud + splits - 1) / splits) * ukd;

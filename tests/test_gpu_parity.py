@@ -131,7 +131,10 @@ def test_both_paths_at_the_crossover(tiny, M, path):
                                     (512, 1376, 70), (160, 224, 17), (256, 4096, 100),
                                     (288, 2048, 33), (256, 38400, 33),
                                     # >= 768 gate/up workgroups: the 4-wave gate/up launch
-                                    (256, 6144, 1), (96, 6176, 3)])
+                                    (256, 6144, 1), (96, 6176, 3),
+                                    # staged gate/up activations with more chunks than
+                                    # the staging registers hold
+                                    (4096, 1024, 3)])
 def test_odd_shapes(d, ff, M):
     layer = Bf16Layer(d, ff, 20 + d)
     x, g = bf16_inputs(M, d, 400 + M)
