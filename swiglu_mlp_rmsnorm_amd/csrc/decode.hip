@@ -109,6 +109,9 @@
 #ifndef FMLP_MASK_ACT
 #define FMLP_MASK_ACT 0    // activation loads only in lanes that hold a token
 #endif
+#ifndef FMLP_DEC_LDS_BF16_DN
+#define FMLP_DEC_LDS_BF16_DN 0  // also stage the bf16 down kernel's a (small M)
+#endif
 #ifndef FMLP_DEC_LDS_BF16_GU
 #define FMLP_DEC_LDS_BF16_GU 1  // also stage bf16 gate/up activations (small M, no residual)
 #endif
@@ -1048,6 +1051,7 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   constexpr int RB = (NCB == 1) ? GRB : (GRB > 2 ? 2 : GRB);
   constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
   constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
+  constexpr bool kStageDn = FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_DN);
   hipError_t e;
   if constexpr (WK == WK_INT4) {
     launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(512), 0, stream, p.x, p.gamma, p.eps,
@@ -1086,7 +1090,7 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const int ukd = WK == WK_BF16 ? 32 : 128, nud = (p.ff + ukd - 1) / ukd;
   const int64_t dn_wgs = (p.d / (16 * dn_rb)) * splits;
   const int64_t dn_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * ((nud + splits - 1) / splits) * ukd;
-  const bool dl = kStage && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
+  const bool dl = (kStage || FMLP_DEC_LDS_BF16_DN) && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
 
   const int ncnt = splits > 1 ? (int)(p.d / 16) : 0;
   if (gu_big)
@@ -1098,14 +1102,14 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   if (bdrb)
     // (int4 with two token blocks keeps 8 waves: its registers do not fit 16)
     launch_down<WK, NCB, BDRB, (NCB == 1 || WK == WK_INT4) ? FMLP_BIG_DN_S : FMLP_BIG_DN_S2,
-                kStage>(p, ws, splits, dl, dn_lds, stream);
+                kStageDn>(p, ws, splits, dl, dn_lds, stream);
   else if (drb)
-    launch_down<WK, NCB, DRB, (NCB == 2 && WK == WK_INT4) ? 8 : FMLP_DN_S, kStage>(
+    launch_down<WK, NCB, DRB, (NCB == 2 && WK == WK_INT4) ? 8 : FMLP_DN_S, kStageDn>(
         p, ws, splits, dl, dn_lds, stream);
   else if (splits == 1)
-    launch_down<WK, NCB, 1, FMLP_DN_S, kStage>(p, ws, splits, dl, dn_lds, stream);
+    launch_down<WK, NCB, 1, FMLP_DN_S, kStageDn>(p, ws, splits, dl, dn_lds, stream);
   else  // split slices are short: 8 waves each, so that more of them are resident per CU
-    launch_down<WK, NCB, 1, FMLP_DN_SPLIT_S, kStage>(p, ws, splits, dl, dn_lds, stream);
+    launch_down<WK, NCB, 1, FMLP_DN_SPLIT_S, kStageDn>(p, ws, splits, dl, dn_lds, stream);
   return hipGetLastError();
 }
 
