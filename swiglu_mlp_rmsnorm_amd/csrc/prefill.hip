@@ -26,7 +26,8 @@
 #include <type_traits>
 
 #ifndef FMLP_SETPRIO
-#define FMLP_SETPRIO 1  // raise the wave priority over each sub-step's MFMA block (measured +1%)
+#define FMLP_SETPRIO 0  // raise the wave priority over each sub-step's MFMA block (no gain with the
+                        // reads hoisted to the sub-step's top; +1% before)
 #endif
 
 namespace fmlp {
@@ -150,12 +151,12 @@ __global__ __launch_bounds__(256) void k_dequant_f16_tiled(const uint32_t* __res
 // rows 8i + 4*(l/32) + j in register 4i + j, so each lane owns whole
 // gate/up pairs (rows 2p, 2p+1) for the SiLU*mul epilogue.
 //
-// Block tile BN features x BM tokens, 4 waves in a 2 x 2 grid, each owning a
-// (BN/2) x (BM/2) sub-tile; one K step is one 32-column block. Both operands
-// go from memory straight into LDS (global_load_lds, 16 bytes per lane, no
-// register staging and no LDS writes by the waves), each wave instruction
-// one contiguous 1 KB: the weights as their bf16 16 x 32 storage tiles, the
-// activations as their fragments. The
+// Block tile BN features x BM tokens on a WGN x WGM grid of 4 or 8 waves,
+// each owning a (BN/WGN) x (BM/WGM) sub-tile; one K step is one 32-column
+// block. Both operands go from memory straight into LDS (buffer loads with
+// the LDS-DMA bit, 16 bytes per lane, no register staging and no LDS writes
+// by the waves), each wave instruction one contiguous 1 KB: the weights as
+// their bf16 16 x 32 storage tiles, the activations as their fragments. The
 // LDS is a ring of 5 stages (160 KB at 256 x 256), so the loads of step
 // kt+4 are issued while step kt computes: four steps of MFMA work hide the
 // memory latency.
@@ -168,17 +169,18 @@ __global__ __launch_bounds__(256) void k_dequant_f16_tiled(const uint32_t* __res
 // sub-step's MFMAs each wave waits only for step kt+1's loads (vector memory
 // counts retire in issue order, so later steps' loads stay in flight), meets
 // the barrier, and reads step kt+1's first fragments under those MFMAs.
-// Loads and LDS reads are interleaved between the MFMAs (sched_group_barrier)
-// so they issue in the matrix pipe's shadow.
+// Within a sub-step the LDS reads issue first and the conversions are spread
+// between the MFMAs (sched_group_barrier), in the matrix pipe's shadow.
 //
 // Tiles are assigned XCD-major: each of the 8 XCDs takes a contiguous range
 // of tile indices, token tiles fastest, so workgroups sharing a weight band
 // run on the same XCD and share its L2.
-// Epilogues: SiLU*mul to the fp16 tiled activations (gate/up), bf16 y, or
-// an fp32 split-K partial (slice blockIdx.y of [splits, M, N]).
-// Epilogues. The three gate epilogues differ only in the activation, which
-// is a compile-time constant: a runtime choice inlines every activation at
-// each of the unrolled output sites and triples the kernel's code.
+// Epilogues: SiLU*mul (or a GELU form) to the fp16 tiled activations
+// (gate/up), bf16 y, or an fp32 split-K partial (slice blockIdx.y of
+// [splits, M, N]). The three gate epilogues differ only in the activation,
+// which is a compile-time constant: a runtime choice inlines every
+// activation at each of the unrolled output sites and triples the kernel's
+// code.
 enum {
   EPI_SILU_MUL_F16 = 0,
   EPI_STORE_BF16 = 1,
@@ -220,8 +222,24 @@ struct GemmCfg {
   static_assert(3 * LD_PER_T < 64, "vmcnt field");
 };
 
-typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
+
+// Buffer descriptor word 3 for CDNA raw (unswizzled, stride 0) buffers: a
+// 32-bit data format; the extent (num_records) is in bytes.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ int buf_extent(int64_t bytes) {
+  return bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+}
+// One 16-byte-per-lane LDS DMA through a raw buffer descriptor over
+// [base, base + extent): lane l's 16 bytes at byte offset voff + soff land at
+// dst + 16 l. (The descriptor is built here, not in the kernel body: its
+// loop-invariant scalar setup is hoisted by the compiler.)
+__device__ __forceinline__ void buf_load_lds16(const uint16_t* base, int extent, lptr_t dst,
+                                               int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, extent, kBufWord3),
+      dst, 16, voff, soff, 0, 0);
+}
 
 // s_waitcnt immediate for vmcnt(vm) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] |
 // expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]). The builtin, unlike
@@ -262,26 +280,37 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   const int nkb = K >> 5, nrb = N >> 4;
   const int nkt = nkb / (int)gridDim.y, kbeg = (int)blockIdx.y * nkt;
 
+  // Both operands are read through buffer descriptors based at this tile's
+  // first weight row block and first token block (from its K slice start),
+  // so every byte offset fits 32 bits whatever the matrix sizes; a lane's
+  // offset is fixed and each K step adds one scalar offset. Reads past a
+  // descriptor's extent would return zeros rather than fault (all reads
+  // here are in range: row and token blocks are clamped below).
+  //
   // Weight chunk i of a thread: 16-row storage tile rb = W*i + wave of the
   // tile (rows past N clamped), slot = lane; its LDS image sits at rb * 1 KB.
-  const uint16_t* wsrc[C::A_PER_T];
+  const int rb0 = n0 >> 4;
+  const uint16_t* wbase = Wt + ((int64_t)rb0 * nkb + kbeg) * 512;
+  const int wext = buf_extent(((int64_t)nrb * nkb - ((int64_t)rb0 * nkb + kbeg)) * 1024);
+  int woff[C::A_PER_T];
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int rb = C::W * i + wave;
-    const int rbc = (n0 >> 4) + rb < nrb ? (n0 >> 4) + rb : nrb - 1;
-    wsrc[i] = Wt + ((int64_t)rbc * nkb + kbeg) * 512 + lane * 8;
+    const int rbc = rb0 + rb < nrb ? rb : nrb - 1 - rb0;
+    woff[i] = rbc * nkb * 1024 + lane * 16;
   }
   // Activation chunk i: fragment f = W*i + wave of the stage (token block
   // f/2 of the tile, half q = f%2), one contiguous 1 KB fragment of the tiled
   // activations (token blocks past the last one clamped to it).
-  const int ntb = (M + 31) >> 5;
-  const uint16_t* asrc[C::B_PER_T];
+  const int ntb = (M + 31) >> 5, tb0 = m0 >> 5;
+  const uint16_t* abase = Act + ((int64_t)tb0 * nkb + kbeg) * 1024;
+  const int aext = buf_extent(((int64_t)ntb * nkb - ((int64_t)tb0 * nkb + kbeg)) * 2048);
+  int aoff[C::B_PER_T];
 #pragma unroll
   for (int i = 0; i < C::B_PER_T; ++i) {
     const int f = C::W * i + wave;
-    int tb = (m0 >> 5) + (f >> 1);
-    tb = tb < ntb ? tb : ntb - 1;
-    asrc[i] = Act + (((int64_t)tb * nkb + kbeg) * 2 + (f & 1)) * 512 + lane * 8;
+    const int tb = tb0 + (f >> 1) < ntb ? (f >> 1) : ntb - 1 - tb0;
+    aoff[i] = (tb * nkb * 2 + (f & 1)) * 1024 + lane * 16;
   }
   // LDS element offsets of this lane's fragment reads (within a stage): the
   // weight fragment of 32-row block b, half q gathers storage tiles 2b
@@ -300,15 +329,13 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
     uint16_t* base = lds + st * C::STAGE_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(wsrc[i] + kt * 512),
-                                       (lptr_t)(base + (C::W * i + wave) * 512), 16, 0, 0);
+      buf_load_lds16(wbase, wext, (lptr_t)(base + (C::W * i + wave) * 512), woff[i], kt * 1024);
   };
   auto load_b = [&](int kt, int st) __attribute__((always_inline)) {
     uint16_t* base = lds + st * C::STAGE_ELEMS + C::A_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(asrc[i] + kt * 1024),
-                                       (lptr_t)(base + (C::W * i + wave) * 512), 16, 0, 0);
+      buf_load_lds16(abase, aext, (lptr_t)(base + (C::W * i + wave) * 512), aoff[i], kt * 2048);
   };
   auto load_step = [&](int kt, int st) __attribute__((always_inline)) {
     load_a(kt, st);
@@ -316,16 +343,30 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   };
 
   u32x4 fa[2][C::WNB], fb[2][C::WMB];
-  auto frag_load = [&](int buf, int st, int q) __attribute__((always_inline)) {
+  auto frag_load_a = [&](int buf, int st, int q) __attribute__((always_inline)) {
     const uint16_t* base = lds + st * C::STAGE_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::WNB; ++i)
       fa[buf][i] = *reinterpret_cast<const u32x4*>(
           &base[a_rd + (wn * C::WNB + i) * 1024 + q * 256]);
+  };
+  auto frag_load_b = [&](int buf, int st, int q) __attribute__((always_inline)) {
+    const uint16_t* base = lds + st * C::STAGE_ELEMS;
 #pragma unroll
     for (int j = 0; j < C::WMB; ++j)
       fb[buf][j] = *reinterpret_cast<const u32x4*>(
           &base[b_rd + ((wm * C::WMB + j) * 2 + q) * 512]);
+  };
+  auto frag_load = [&](int buf, int st, int q) __attribute__((always_inline)) {
+    frag_load_a(buf, st, q);
+    frag_load_b(buf, st, q);
+  };
+  // the same reads, weights strictly first, all issued before what follows
+  auto frag_load_ordered = [&](int buf, int st, int q) __attribute__((always_inline)) {
+    frag_load_a(buf, st, q);
+    __builtin_amdgcn_sched_barrier(0);
+    frag_load_b(buf, st, q);
+    __builtin_amdgcn_sched_barrier(0);
   };
   // weight fragments bf16 -> fp16 in place (after their LDS reads land)
   auto convert = [&](int buf) __attribute__((always_inline)) {
@@ -340,21 +381,19 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
 #pragma unroll
       for (int j = 0; j < C::WMB; ++j) acc[i][j] = mfma32_f16(fa[buf][i], fb[buf][j], acc[i][j]);
   };
-  // Interleave within one sub-step: the first MFMAs are each followed by a
-  // fragment read of the other register set, the later ones by the
-  // conversions of those fragments, and the NL loads are spread evenly over
-  // the sub-step, so everything issues in the matrix pipe's shadow and the
-  // four waves of a CU do not hand the address unit their loads in bursts.
-  auto interleave = [&](auto n_vmem_c) __attribute__((always_inline)) {
-    constexpr int NL = decltype(n_vmem_c)::value, NR = C::WNB + C::WMB;
-    constexpr int NMF = C::WNB * C::WMB, NV = AF16 ? 0 : C::WNB * 12, HALF = NMF / 2;
-    constexpr int LSTRIDE = NL > 0 ? (NMF / NL > 0 ? NMF / NL : 1) : NMF;
+  // Schedule of one sub-step: all fragment reads of the other register set
+  // issue at its top (weights first, in program order), then the MFMAs, with
+  // the conversions of the new weight fragments spread over the second half.
+  // A conversion then waits only for its own weight read (the LDS DMA is a
+  // buffer load, counted on vmcnt alone, so the LDS waits stay exact), issued
+  // half a sub-step earlier. (Measured 1.5-4% faster than spreading the reads
+  // over the MFMAs.)
+  auto interleave = [&]() __attribute__((always_inline)) {
+    constexpr int NMF = C::WNB * C::WMB;
+    constexpr int NV = AF16 ? 0 : C::WNB * 12, HALF = NMF / 2;
 #pragma unroll
     for (int g = 0; g < NMF; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // MFMA
-      if (g < NR) __builtin_amdgcn_sched_group_barrier(0x0100, 1, 0);   // DS read
-      if (NL > 0 && g % LSTRIDE == 0 && g / LSTRIDE < NL)
-        __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);             // VMEM read
       if (NV > 0 && g >= HALF)
         __builtin_amdgcn_sched_group_barrier(0x0002, (NV + HALF - 1) / HALF, 0);  // VALU
     }
@@ -367,6 +406,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   __builtin_amdgcn_s_barrier();
   frag_load(0, 0, 0);
   convert(0);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
 
   // steady state: step kt computes from stage kt % 5 while step kt+4 loads
   // into stage (kt+4) % 5, which step kt-1 released at its barrier
@@ -376,29 +416,28 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   int kt = 0, st = 0;
   for (; kt + 4 < nkt; ++kt) {
     const int st1 = st == 4 ? 0 : st + 1, st4 = st == 0 ? 4 : st - 1;
-#ifndef FMLP_EXP_NOLOAD
     load_a(kt + 4, st4);
-#endif
     if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    frag_load(1, st, 1);
+    frag_load_ordered(1, st, 1);
     mma(0);
     convert(1);
-    interleave(std::integral_constant<int, C::A_PER_T>{});
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T + C::A_PER_T));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-#ifndef FMLP_EXP_NOLOAD
     load_b(kt + 4, st4);
-#endif
     if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(1);
-    frag_load(0, st1, 0);
+    frag_load_ordered(0, st1, 0);
     mma(1);
     convert(0);
-    interleave(std::integral_constant<int, C::B_PER_T>{});
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    // (the activation reads were issued a whole sub-step ago: a free wait
+    // that leaves the next iteration's first MFMAs nothing to wait for)
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     st = st1;
   }
   // the last (up to 4) steps: nothing left to load
@@ -493,6 +532,15 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
   return hipGetLastError();
 }
 
+#ifndef FMLP_DOWN_W4
+#define FMLP_DOWN_W4 1  // down GEMM's 256 x 256 tile on 4 waves (128 x 128 each)
+#endif
+#ifndef FMLP_DN_WGN
+#define FMLP_DN_WGN 2  // wave grid of the down GEMM's 256 x 256 tile on 4 waves
+#endif
+#ifndef FMLP_DN_WGM
+#define FMLP_DN_WGM 2
+#endif
 #ifndef FMLP_S0_WGN
 #define FMLP_S0_WGN 4  // wave grid of the 256 x 256 tile
 #endif
@@ -548,9 +596,13 @@ static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const u
   const int n_main = N - g.tail_rows;
   hipError_t e = hipSuccess;
   if (n_main > 0) {
+    // the down GEMM runs the 256 x 256 tile on 4 waves, the gate/up GEMM on
+    // FMLP_S0_WGN x FMLP_S0_WGM (measured best for each)
+    constexpr bool w4 = !epi_gate(EPI) && FMLP_DOWN_W4;
+    constexpr int s0n = w4 ? FMLP_DN_WGN : FMLP_S0_WGN, s0m = w4 ? FMLP_DN_WGM : FMLP_S0_WGM;
     if (g.shape == 0)
-      e = launch_gemm_t<8, 8, FMLP_S0_WGN, FMLP_S0_WGM, EPI, AF16>(W, Act, out, M, N, K, g.splits,
-                                                                  stream, 0, n_main);
+      e = launch_gemm_t<8, 8, s0n, s0m, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
+                                                  n_main);
     else if (g.shape == 1)
       e = launch_gemm_t<8, 4, 4, 1, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
     else
