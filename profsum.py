@@ -72,6 +72,10 @@ def pmc(args):
     # counters are KiB per dispatch; the copy moves copy_bytes each way. A
     # kernel kind may dispatch more than once per forward step: traffic is
     # summed over the run's dispatches and divided by its steps.
+    for n, name in ((len(k_f), "FETCH_SIZE"), (len(k_w), "WRITE_SIZE")):
+        if n % args.steps:
+            raise SystemExit(f"{name}: {n} dispatches of /{args.match}/ is not a multiple of "
+                             f"the run's {args.steps} steps (a run with extra timing windows?)")
     fetch_scale = args.copy_bytes / (copy_f * 1024.0)
     write_scale = args.copy_bytes / (copy_w * 1024.0)
     fetch_b = sum(k_f) * 1024.0 * fetch_scale / args.steps
