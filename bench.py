@@ -79,24 +79,26 @@ def step_bytes(M, d, ff, wtype):
     return gu + dn + M * d * 2 + d * 2 + M * d * 2
 
 
-def kernel_bytes(kernel, M, d, ff, wtype):
+def kernel_bytes(kernel, M, d, ff, wtype, f16=None):
     """Algorithmic bytes of one launch of a decode kernel: its weights
     (+ scales), its activation inputs and its outputs. bf16 path: gate/up
     reads x and gamma and writes the SiLU*mul product as a bf16 hi + lo pair
-    (4 bytes per element), which down reads back. int4 path: gate/up reads
-    the prepared fp16 n, the product is fp16 (2 bytes per element).
+    (4 bytes per element), which down reads back. int4 path, and the bf16
+    path at larger M (f16: a prep kernel ran): gate/up reads the prepared
+    fp16 n, the product is fp16 (2 bytes per element).
     Single-pass decode: one kernel reads both matrices, x and gamma and
     writes fp32 partial sums per 32-feature slice of ff, which the reduce
     kernel reads back to write y."""
     gu, dn = weight_bytes(d, ff, wtype)
-    a_elem = 2 if wtype == "int4" else 4
+    f16 = wtype == "int4" if f16 is None else f16
+    a_elem = 2 if f16 else 4
     partials = (ff // 32) * M * d * 4  # single-pass decode: fp32 per 32-feature slice
     if kernel == "decode_fused_bf16":
         return gu + dn + M * d * 2 + d * 2 + partials
     if kernel == "partial_reduce":
         return partials + M * d * 2
     if "gateup" in kernel:
-        act_in = M * d * 2 + (0 if wtype == "int4" else d * 2)
+        act_in = M * d * 2 + (0 if f16 else d * 2)
         return gu + act_in + M * ff * a_elem
     if kernel == "act_prep":
         return M * d * 2 + d * 2 + M * d * 2
@@ -319,7 +321,9 @@ def run_one(wname, M, steps, warmup, args):
         unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
     elif path == "decode":
         dom = "decode_gateup_int4" if w.wtype == "int4" else "decode_gateup_bf16"
-        dom_units = kernel_bytes(dom, M, d, ff, w.wtype)
+        # fp16 activations: int4, or a bf16 step that ran the prep kernel
+        f16 = w.wtype == "int4" or "act_prep" in kernels
+        dom_units = kernel_bytes(dom, M, d, ff, w.wtype, f16)
         unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
     else:
         dom = "gemm_gateup_silu_f16"
@@ -339,7 +343,9 @@ def run_one(wname, M, steps, warmup, args):
     for name, k in kernels.items():
         t = k["us_per_step"]
         if name.startswith("decode") or name in ("act_prep", "partial_reduce"):
-            k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype) / (t * 1e3), 1)
+            k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype,
+                                               w.wtype == "int4" or "act_prep" in kernels)
+                                  / (t * 1e3), 1)
         elif name == "gemm_gateup_silu_f16":
             k["tflop_per_s"] = round(2.0 * M * 2 * ff * d / (t * 1e6), 1)
         elif name == "gemm_down_f16":

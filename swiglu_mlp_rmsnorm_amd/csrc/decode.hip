@@ -1,9 +1,11 @@
-// Decode path (M <= 32 tokens): two kernels per forward (three for int4).
+// Decode path (M <= 32 tokens): two kernels per forward (three for int4,
+// and for bf16 weights at M > 16).
 //
-//   0. (int4 only) act prep: r = 1/sqrt(mean(x^2) + eps) per token and the
-//      normalised input n = gamma * x * r as fp16 in the int4 operand order
-//      (FastTPS review, section 3, Figure 4 part1). On the bf16 path the
-//      RMSNorm is folded into step 1 instead.
+//   0. (int4; bf16 at M > 16) act prep: r = 1/sqrt(mean(x^2) + eps) per token
+//      and the normalised input n = gamma * x * r as fp16, in the int4
+//      operand order or in natural order (FastTPS review, section 3, Figure 4
+//      part1). On the bf16 path at M <= 16 the RMSNorm is folded into step 1
+//      instead.
 //   1. gate/up: z = W_gu n over the interleaved rows, then a = SiLU(z_gate) *
 //      z_up on each (2i, 2i+1) pair in registers (Figure 4 part2; llama.cpp
 //      PR digest: the GLU is applied in the same pass as the gate/up matmul).
@@ -25,7 +27,11 @@
 // bf16 weights: the activation is an exact-to-2^-17 bf16 hi + lo pair (two
 // bf16 MFMAs per tile), so the normalised input and the SiLU*mul
 // intermediate keep fp32-like precision (rounding either to bf16 alone
-// breaks the accuracy bar at the larger shapes).
+// breaks the accuracy bar at the larger shapes). At M > 16 (two token blocks)
+// the activations are fp16 instead, as on the prefill path: one f16 MFMA per
+// tile against the weight tile converted to fp16 in registers (exact in the
+// fp16 normal range), and half the activation bytes per workgroup, which at
+// that M match the weight bytes.
 //
 // int4 weights: one fp16 MFMA per group. A word holds the 8 codes a lane
 // needs; with u = word ^ 0x88888888 each nibble is q+8, and
@@ -118,13 +124,22 @@
 #ifndef FMLP_DEC_LDS
 #define FMLP_DEC_LDS 1     // stage small-M activations in LDS (0: read them per wave)
 #endif
+#ifndef FMLP_H16_MIN_M
+#define FMLP_H16_MIN_M 17  // bf16 weights: from this M on, fp16 activations (WK_BF16H);
+                           // measured: -10% at Llama-8B M=32, no gain at M=16 (the prep
+                           // launch costs what the kernels save), a loss at M=8
+#endif
 #ifndef FMLP_FU_DYN_LDS
 #define FMLP_FU_DYN_LDS 0  // extra (unused) LDS per single-pass workgroup, bytes
 #endif
 
 namespace fmlp {
 
-enum { WK_BF16 = 0, WK_INT4 = 1 };
+// Weight kinds: bf16 weights with the bf16 hi + lo activation pair; int4
+// weights; bf16 weights with fp16 activations (several tokens: one MFMA per
+// tile instead of two and half the activation bytes, the weight tile
+// converted to fp16 in registers).
+enum { WK_BF16 = 0, WK_INT4 = 1, WK_BF16H = 2 };
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -225,9 +240,24 @@ __device__ __forceinline__ u32x4 act_q4_chunk(u32x4 v, u32x4 g, float r) {
   return o;
 }
 
+// The same in natural order (no slot permutation, no 1/16 slots): the fp16
+// activations of the bf16-weight several-token path.
+__device__ __forceinline__ u32x4 act_f16_chunk(u32x4 v, u32x4 g, float r) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const _Float16 lo = (_Float16)(bf16_lo(v[j]) * bf16_lo(g[j]) * r);
+    const _Float16 hi = (_Float16)(bf16_hi(v[j]) * bf16_hi(g[j]) * r);
+    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  return o;
+}
+
 // With res, the row normalised is the residual stream h = bf16_rne(x + res),
-// which is also stored to hout.
-__global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict__ x,
+// which is also stored to hout. Q4: the int4 slot order, else natural order.
+template <bool Q4>
+__global__ __launch_bounds__(512) void k_act_prep(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma,
                                                      float eps, uint16_t* __restrict__ n0, int d,
                                                      const uint16_t* __restrict__ res,
@@ -279,10 +309,13 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
 #pragma unroll
   for (int i = 0; i < kActPrepChunks; ++i) {
     const int c = tid + i * 512;
-    if (c < chunks) st16(n0 + m * d + c * 8, act_q4_chunk(v[i], g[i], r));
+    if (c < chunks)
+      st16(n0 + m * d + c * 8, Q4 ? act_q4_chunk(v[i], g[i], r) : act_f16_chunk(v[i], g[i], r));
   }
-  for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512)
-    st16(n0 + m * d + c * 8, act_q4_chunk(row(c), ld16(gamma + c * 8), r));
+  for (int c = tid + kActPrepChunks * 512; c < chunks; c += 512) {
+    const u32x4 xv = row(c), gv = ld16(gamma + c * 8);
+    st16(n0 + m * d + c * 8, Q4 ? act_q4_chunk(xv, gv, r) : act_f16_chunk(xv, gv, r));
+  }
 }
 
 // ------------------------------------------------------------ GEMV core
@@ -297,6 +330,8 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
 //   ACT_Q4_LDS : as ACT_Q4, act0 staged in LDS by the workgroup
 //   ACT_XR     : as ACT_X on the residual stream h = bf16_rne(x + res) (res
 //                [M, K] like x); h is also stored to hout when that is given
+//   ACT_F16    : bf16 weights, each tile converted to fp16 in registers;
+//                act0 = fp16 [M, K], natural order; one f16 MFMA per tile
 // Global activations are read into the ring with the weights. Staged ones
 // are [M, astride] rows whose first element is k = kbase; they are read
 // from LDS as they are used. stage_load() issues the workgroup's loads of
@@ -307,7 +342,7 @@ __global__ __launch_bounds__(512) void k_act_prep_q4(const uint16_t* __restrict_
 // 16 rows x 4 groups) + scales. The K units u0 .. u0+ucnt-1 are covered;
 // each wave walks units u0+wave, u0+wave+S, ...
 // with a P-deep ring of weight tiles (and global activation chunks) in flight.
-enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5 };
+enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5, ACT_F16 = 6 };
 
 template <int MODE, int NCB, int RB, int S, int P, class StageLoad, class StageStore>
 __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
@@ -339,7 +374,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr bool kX = MODE == ACT_X || MODE == ACT_XR;  // activations from x (and res)
-  if constexpr (kX || MODE == ACT_HL || MODE == ACT_HL_LDS) {
+  if constexpr (kX || MODE == ACT_HL || MODE == ACT_HL_LDS || MODE == ACT_F16) {
     // unit = one 32-column group
     const uint16_t* wt = static_cast<const uint16_t*>(w) + lane * 8;
     const int nit = wave < ucnt ? (ucnt - wave + S - 1) / S : 0;
@@ -413,30 +448,39 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
             }
           }
           if (it + P < nit) issue(p, it + P);
+          if constexpr (MODE == ACT_F16) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) {
-            if (kX) {
-              // h holds x (l the residual); build the hi/lo pair of gamma * x in place
-              u32x4 xv = h[cb];
-              if (MODE == ACT_XR) {
-                xv = add_bf16x8(xv, l[cb]);
-                if (hout != nullptr && tok[cb]) st16(hout + aoff[cb] + kb * 32, xv);
+            for (int rb = 0; rb < RB; ++rb) wv[rb] = bf16x8_to_f16x8(wv[rb]);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+              for (int rb = 0; rb < RB; ++rb) acc[rb][cb] = mfma_f16(h[cb], wv[rb], acc[rb][cb]);
+          } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+              if (kX) {
+                // h holds x (l the residual); build the hi/lo pair of gamma * x in place
+                u32x4 xv = h[cb];
+                if (MODE == ACT_XR) {
+                  xv = add_bf16x8(xv, l[cb]);
+                  if (hout != nullptr && tok[cb]) st16(hout + aoff[cb] + kb * 32, xv);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  const float x0 = bf16_lo(xv[j]), x1 = bf16_hi(xv[j]);
+                  ss[cb] = fmaf(x0, x0, ss[cb]);
+                  ss[cb] = fmaf(x1, x1, ss[cb]);
+                  uint32_t hh, ll;
+                  split_bf16_pair(x0 * bf16_lo(gv[j]), x1 * bf16_hi(gv[j]), hh, ll);
+                  h[cb][j] = hh;
+                  l[cb][j] = ll;
+                }
               }
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float x0 = bf16_lo(xv[j]), x1 = bf16_hi(xv[j]);
-                ss[cb] = fmaf(x0, x0, ss[cb]);
-                ss[cb] = fmaf(x1, x1, ss[cb]);
-                uint32_t hh, ll;
-                split_bf16_pair(x0 * bf16_lo(gv[j]), x1 * bf16_hi(gv[j]), hh, ll);
-                h[cb][j] = hh;
-                l[cb][j] = ll;
+              for (int rb = 0; rb < RB; ++rb) {
+                acc[rb][cb] = mfma_bf16(h[cb], wv[rb], acc[rb][cb]);
+                acc[rb][cb] = mfma_bf16(l[cb], wv[rb], acc[rb][cb]);
               }
-            }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-              acc[rb][cb] = mfma_bf16(h[cb], wv[rb], acc[rb][cb]);
-              acc[rb][cb] = mfma_bf16(l[cb], wv[rb], acc[rb][cb]);
             }
           }
         }
@@ -550,7 +594,9 @@ __device__ __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RB][NCB]) {
 // r = 1/sqrt(mean(x^2) + eps) scales z before SiLU*mul (z * r = W (gamma x r)).
 // Writes a = a0 + a1 (bf16 hi/lo, natural order, [M, ff]).
 // int4: activations are the prepared fp16 n (ACT_Q4); writes a0 = fp16 a in
-// the int4 slot order, [M, ff].
+// the int4 slot order, [M, ff]. bf16 weights with fp16 activations
+// (WK_BF16H): the prepared fp16 n in natural order (ACT_F16); writes a0 =
+// fp16 a, [M, ff].
 // LDS: the workgroup first stages its activations in LDS (dynamic shared
 // memory): gamma * x as the bf16 hi + lo pair with the per-token sums of x^2
 // (bf16), or a copy of n (int4); for small M, where the per-wave activation
@@ -579,7 +625,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
   f32x4 acc[RB][NCB];
   float ss[NCB];
-  const int units = WK == WK_BF16 ? d >> 5 : (d + 127) >> 7;
+  const int units = WK == WK_INT4 ? (d + 127) >> 7 : d >> 5;
   if constexpr (LDS) {
     uint16_t* lhi = stage_lds;
     uint16_t* llo = stage_lds + (int64_t)M * d;
@@ -650,9 +696,9 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
         w, sc, lhi, llo, rb0, d, M, 0, units, acc, ss, d, 0, stage_load, stage_store);
     stash<RB, NCB>(red, acc);
   } else {
-    gemv_core<WK == WK_BF16 ? (RES ? ACT_XR : ACT_X) : ACT_Q4, NCB, RB, S, P>(
-        w, sc, act0, act1, rb0, d, M, 0, units, acc, ss, d, 0, [] {}, [] {}, res,
-        blockIdx.x == 0 ? hout : nullptr);
+    gemv_core<WK == WK_BF16 ? (RES ? ACT_XR : ACT_X) : WK == WK_BF16H ? ACT_F16 : ACT_Q4, NCB,
+              RB, S, P>(w, sc, act0, act1, rb0, d, M, 0, units, acc, ss, d, 0, [] {}, [] {}, res,
+                        blockIdx.x == 0 ? hout : nullptr);
     stash<RB, NCB>(red, acc);
     if (WK == WK_BF16) {
       // lanes col, col+16, col+32, col+48 hold the same token
@@ -689,6 +735,8 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
       const uint16_t h = bf16_rne(av);
       a0[(int64_t)t * ff + i] = h;
       a1[(int64_t)t * ff + i] = bf16_rne(av - __uint_as_float((uint32_t)h << 16));
+    } else if (WK == WK_BF16H) {
+      a0[(int64_t)t * ff + i] = __builtin_bit_cast(uint16_t, (_Float16)act_mul(act, g, u));
     } else {
       const float av = act_mul(act, g, u);
       const int mm = i & 7;
@@ -719,7 +767,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
   extern __shared__ __align__(16) uint16_t stage_lds[];
   const int64_t rb0 = (int64_t)blockIdx.x * RB;
   const int splits = gridDim.y, ks = blockIdx.y;
-  constexpr int UK = WK == WK_BF16 ? 32 : 128;  // K per unit
+  constexpr int UK = WK == WK_INT4 ? 128 : 32;  // K per unit
   const int nu = (ff + UK - 1) / UK;            // K units
   const int per = (nu + splits - 1) / splits;
   const int u0 = ks * per, ucnt = nu - u0 < per ? nu - u0 : per;
@@ -763,7 +811,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
         w, sc, lhi, llo, rb0, ff, M, u0, ucnt > 0 ? ucnt : 0, acc, ss, astride, kbeg, stage_load,
         stage_store);
   } else {
-    gemv_core<WK == WK_BF16 ? ACT_HL : ACT_Q4, NCB, RB, S, P>(
+    gemv_core<WK == WK_BF16 ? ACT_HL : WK == WK_BF16H ? ACT_F16 : ACT_Q4, NCB, RB, S, P>(
         w, sc, a0, a1, rb0, ff, M, u0, ucnt > 0 ? ucnt : 0, acc, ss, ff, 0, [] {}, [] {});
   }
   stash<RB, NCB>(red, acc);
@@ -1013,7 +1061,7 @@ static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t
                             hipStream_t stream) {
   constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
   constexpr bool kStage =
-      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_GU);
+      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_GU));
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
   const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * S);
@@ -1038,7 +1086,7 @@ template <int WK, int NCB, int RB>
 static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
                           const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
                           hipStream_t stream) {
-  if (WK == WK_BF16 && NCB == 1 && (2 * p.ff) / (16 * RB) >= FMLP_GU_MANY_WGS)
+  if (WK != WK_INT4 && NCB == 1 && (2 * p.ff) / (16 * RB) >= FMLP_GU_MANY_WGS)
     launch_gateup_s<WK, NCB, RB, FMLP_GU_S_MANY>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
   else
     launch_gateup_s<WK, NCB, RB, FMLP_GU_S>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
@@ -1051,14 +1099,15 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   constexpr int RB = (NCB == 1) ? GRB : (GRB > 2 ? 2 : GRB);
   constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
   constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
-  constexpr bool kStageDn = FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_DN);
+  constexpr bool kStageDn =
+      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_DN));
   hipError_t e;
-  if constexpr (WK == WK_INT4) {
-    launch_kernel(KK_ACT_PREP, k_act_prep_q4, dim3(p.M), dim3(512), 0, stream, p.x, p.gamma, p.eps,
-                  ws.n0, p.d, p.res, p.hout);
+  if constexpr (WK != WK_BF16) {
+    launch_kernel(KK_ACT_PREP, k_act_prep<WK == WK_INT4>, dim3(p.M), dim3(512), 0, stream, p.x,
+                  p.gamma, p.eps, ws.n0, p.d, p.res, p.hout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // bf16 reads x and gamma directly; int4 reads the prepared fp16 n
+  // bf16 reads x and gamma directly; the others read the prepared fp16 n
   const uint16_t* act0 = WK == WK_BF16 ? p.x : ws.n0;
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
   // Larger M: every K unit's activation loads (M tokens per wave) cost as
@@ -1080,21 +1129,22 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // down loses up to 14 %, so the bf16 down kernel reads its a per wave.
   auto lds_budget = [](int64_t wgs) -> int64_t { return wgs <= 256 ? 96 * 1024 : 32 * 1024; };
   constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2;
-  const bool gu_big = big && WK == WK_BF16;
+  const bool gu_big = big && WK != WK_INT4;
   const int64_t gu_wgs = (2 * p.ff) / (16 * (gu_big ? BGRB : RB));
   const int64_t gu_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * p.d;
   // (bf16 gate/up staging, when enabled, does not cover the residual prologue)
-  constexpr bool kStageGu = FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || FMLP_DEC_LDS_BF16_GU);
+  constexpr bool kStageGu =
+      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_GU));
   const bool gl = kStageGu && (WK == WK_INT4 || !p.res) && p.M <= kLdsMaxM &&
                   gu_lds <= lds_budget(gu_wgs);
-  const int ukd = WK == WK_BF16 ? 32 : 128, nud = (p.ff + ukd - 1) / ukd;
+  const int ukd = WK == WK_INT4 ? 128 : 32, nud = (p.ff + ukd - 1) / ukd;
   const int64_t dn_wgs = (p.d / (16 * dn_rb)) * splits;
   const int64_t dn_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * ((nud + splits - 1) / splits) * ukd;
   const bool dl = (kStage || FMLP_DEC_LDS_BF16_DN) && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
 
   const int ncnt = splits > 1 ? (int)(p.d / 16) : 0;
   if (gu_big)
-    launch_gateup<WK, NCB, WK == WK_BF16 ? BGRB : RB>(p, ws, act0, act1, ncnt, gl, gu_lds,
+    launch_gateup<WK, NCB, WK != WK_INT4 ? BGRB : RB>(p, ws, act0, act1, ncnt, gl, gu_lds,
                                                       stream);
   else
     launch_gateup<WK, NCB, RB>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
@@ -1117,6 +1167,9 @@ hipError_t launch_decode(const Problem& p, hipStream_t stream) {
   if (p.wtype == 1)
     return p.M <= 16 ? launch_decode_t<WK_INT4, 1>(p, stream)
                      : launch_decode_t<WK_INT4, 2>(p, stream);
+  if (p.M >= FMLP_H16_MIN_M)
+    return p.M <= 16 ? launch_decode_t<WK_BF16H, 1>(p, stream)
+                     : launch_decode_t<WK_BF16H, 2>(p, stream);
   return p.M <= 16 ? launch_decode_t<WK_BF16, 1>(p, stream) : launch_decode_t<WK_BF16, 2>(p, stream);
 }
 

@@ -64,6 +64,12 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   const fp16x2_t h = __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w));
   return __builtin_bit_cast(uint32_t, h);
 }
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 h;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(v[j]);
+  return h;
+}
 
 // ---- MFMA wrappers (v_mfma_f32_16x16x32_{bf16,f16}) ------------------------
 // Operand layout (wave64): lane l supplies row (l % 16) of A and column

@@ -247,13 +247,6 @@ __device__ __forceinline__ void buf_load_lds16(const uint16_t* base, int extent,
 // no redundant waits.
 constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | 0x70 | ((vm >> 4) << 14); }
 
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
-  u32x4 h;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) h[j] = bf16x2_to_f16x2(v[j]);
-  return h;
-}
-
 // AF16: the weight tiles already hold fp16 (dequantised int4), no conversion.
 template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
 __global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
