@@ -73,6 +73,9 @@
 #ifndef FMLP_Q4_P
 #define FMLP_Q4_P 1   // int4 ring depth (super-tiles of 4 groups)
 #endif
+#ifndef FMLP_Q4_DN_P
+#define FMLP_Q4_DN_P FMLP_Q4_P  // int4 down ring depth
+#endif
 #ifndef FMLP_Q4_GU_RB
 #define FMLP_Q4_GU_RB 2  // int4 gate/up row blocks per workgroup
 #endif
@@ -1043,7 +1046,7 @@ hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
 template <int WK, int NCB, int DRB, int S, bool STAGE>
 static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool lds,
                         int64_t lds_bytes, hipStream_t stream) {
-  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_DN_P;
+  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_DN_P : FMLP_DN_P;
   const int kind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
   const dim3 grid(p.d / (16 * DRB), splits), block(64 * S);
   if (STAGE && lds)
