@@ -43,7 +43,7 @@ static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // padding slots are never read into a stored output.
 __device__ __forceinline__ int64_t act_tile_off(int t, int k, int K) {
   const int tb = t >> 5, kb = k >> 5, q = (k >> 4) & 1, slot = ((k >> 3) & 1) * 32 + (t & 31);
-  return ((int64_t)(tb * (K >> 5) + kb) * 2 + q) * 512 + slot * 8 + (k & 7);
+  return (((int64_t)tb * (K >> 5) + kb) * 2 + q) * 512 + slot * 8 + (k & 7);
 }
 
 static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
