@@ -217,10 +217,11 @@ constexpr uint32_t kNegOffA = 0xE408E408u, kNegOffB = 0xE480E480u;
 // order, and whether that slot carries the value divided by 16.
 __device__ __forceinline__ int q4_slot(int m) { return (m & 1) ? 2 + ((m >> 1) & 1) * 4 + (m >> 2) : (m >> 1 & 1) * 4 + (m >> 2); }
 
-// ------------------------------------------------------------ act prep (int4)
-// One 512-thread workgroup per token: r = 1/sqrt(mean(x^2) + eps), then
-// n = x * gamma * r stored as fp16 [M, d] in the int4 slot order, the slots
-// of odd elements carrying n/16. Each thread issues all its x and gamma
+// ------------------------------------------------------------ act prep
+// (int4; bf16 weights at M > 16.) One 512-thread workgroup per token:
+// r = 1/sqrt(mean(x^2) + eps), then n = x * gamma * r stored as fp16 [M, d],
+// either in the int4 slot order with the slots of odd elements carrying
+// n/16, or in natural order. Each thread issues all its x and gamma
 // loads at once and keeps x in registers between the two steps (d up to
 // kActPrepChunks * 8 * 512; larger d takes a second pass over x).
 constexpr int kActPrepChunks = 4;
