@@ -56,15 +56,29 @@ __global__ __launch_bounds__(256) void k_rms_scale(const uint16_t* __restrict__ 
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (t >= M) return;
   const uint16_t* xr = x + (int64_t)t * d;
+  const uint16_t* rr = res ? res + (int64_t)t * d : nullptr;
+  const int nch = d >> 3;
+  // kU chunks per lane in flight at once (one load, then its wait, per
+  // chunk would serialise the row's memory latency)
+  constexpr int kU = 8;
   float ss = 0.f;
-  for (int c = lane; c < (d >> 3); c += 64) {
-    u32x4 v = ld16(xr + c * 8);
-    if (res) v = add_bf16x8(v, ld16(res + (int64_t)t * d + c * 8));  // residual stream
+  for (int c0 = lane; c0 < nch; c0 += 64 * kU) {
+    u32x4 v[kU], rv[kU];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = bf16_lo(v[j]), hi = bf16_hi(v[j]);
-      ss = fmaf(lo, lo, ss);
-      ss = fmaf(hi, hi, ss);
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * 64;
+      v[u] = c < nch ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+      if (rr) rv[u] = c < nch ? ld16(rr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const u32x4 w = rr ? add_bf16x8(v[u], rv[u]) : v[u];  // residual stream
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
     }
   }
 #pragma unroll
