@@ -846,10 +846,17 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
   for (int o = threadIdx.x; o < RB * 16 * M; o += 64 * S) {
     const int rl = o % (RB * 16), t = o / (RB * 16);
     const int64_t yi = (int64_t)t * d + rb0 * 16 + rl;
+    // all slices' loads in flight before the first add (one load and its
+    // wait per slice would chain their latencies): unconditional, slices past
+    // the last re-read it and are masked out; summed in slice order
+    float pv[kMaxSplit];
+#pragma unroll
+    for (int k = 0; k < kMaxSplit; ++k)
+      pv[k] = __hip_atomic_load(part + (int64_t)(k < splits ? k : splits - 1) * M * d + yi,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float sum = 0.f;
-    for (int k = 0; k < splits; ++k)
-      sum += __hip_atomic_load(part + (int64_t)k * M * d + yi, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < kMaxSplit; ++k) sum += k < splits ? pv[k] : 0.f;
     y[yi] = bf16_rne(sum);
   }
 }
