@@ -402,7 +402,8 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   auto interleave = [&](auto nl_c) __attribute__((always_inline)) {
     constexpr int NMF = C::WNB * C::WMB;
     constexpr int NV = AF16 ? 0 : C::WNB * 12, HALF = NMF / 2;
-    constexpr int NL = kSpread ? decltype(nl_c)::value : 0, LS = NL > 0 ? NMF / NL : NMF;
+    constexpr int NL = kSpread ? decltype(nl_c)::value : 0;
+    constexpr int LS = NMF / (NL > 0 ? NL : 1) > 0 ? NMF / (NL > 0 ? NL : 1) : 1;  // MFMAs per load
 #pragma unroll
     for (int g = 0; g < NMF; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);               // MFMA

@@ -25,8 +25,8 @@ std::vector<Record> g_records;
 
 void clear_locked() {
   for (Record& r : g_records) {
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);  // best-effort cleanup
+    (void)hipEventDestroy(r.stop);
   }
   g_records.clear();
 }
@@ -38,7 +38,7 @@ bool profiling_enabled() { return g_on.load(std::memory_order_relaxed); }
 bool profile_events(hipEvent_t* start, hipEvent_t* stop) {
   if (hipEventCreate(start) != hipSuccess) return false;
   if (hipEventCreate(stop) != hipSuccess) {
-    hipEventDestroy(*start);
+    (void)hipEventDestroy(*start);
     return false;
   }
   return true;
