@@ -361,7 +361,6 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
   constexpr bool kLds = MODE == ACT_HL_LDS || MODE == ACT_Q4_LDS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int jmax = M >= 4 ? 4 : M;
   const int nkb = K >> 5;
   int64_t aoff[NCB];
   bool tok[NCB];
@@ -439,16 +438,17 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) wv[rb] = wb[p][rb];
           const u32x4 gv = gb[p];
+          // (lanes of absent tokens read token 0's activations: MFMA rows
+          // are independent, so they only fill accumulator rows that are
+          // never reduced into a stored output; no masking needed)
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             if constexpr (kLds) {
-              h[cb] = tok[cb] ? *reinterpret_cast<const u32x4*>(act0 + aoff[cb] + kb * 32)
-                              : u32x4{0u, 0u, 0u, 0u};
-              l[cb] = tok[cb] ? *reinterpret_cast<const u32x4*>(act1 + aoff[cb] + kb * 32)
-                              : u32x4{0u, 0u, 0u, 0u};
+              h[cb] = *reinterpret_cast<const u32x4*>(act0 + aoff[cb] + kb * 32);
+              l[cb] = *reinterpret_cast<const u32x4*>(act1 + aoff[cb] + kb * 32);
             } else {
-              h[cb] = tok[cb] ? hb[p][cb] : u32x4{0u, 0u, 0u, 0u};
-              l[cb] = tok[cb] ? lb[p][cb] : u32x4{0u, 0u, 0u, 0u};
+              h[cb] = hb[p][cb];
+              l[cb] = lb[p][cb];
             }
           }
           if (it + P < nit) issue(p, it + P);
@@ -549,11 +549,11 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
             const int kb = q * 4 + j < nkb ? q * 4 + j : nkb - 1;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
+              // (absent tokens: as in the bf16 branch, no masking needed)
               if constexpr (kLds)
-                av[j][cb] = tok[cb] ? *reinterpret_cast<const u32x4*>(act0 + aoff[cb] + kb * 32)
-                                    : u32x4{0u, 0u, 0u, 0u};
+                av[j][cb] = *reinterpret_cast<const u32x4*>(act0 + aoff[cb] + kb * 32);
               else
-                av[j][cb] = tok[cb] ? ab[p][j][cb] : u32x4{0u, 0u, 0u, 0u};
+                av[j][cb] = ab[p][j][cb];
             }
           }
           if (it + P < nit) issue(p, it + P);
@@ -570,7 +570,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                     _Float16, (uint16_t)(sv[rb] >> (16 * j)));
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  if (e < jmax) acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
+                  acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
               }
             }
           }
