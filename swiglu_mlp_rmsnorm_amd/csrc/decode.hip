@@ -199,13 +199,16 @@ static DecodeWs decode_ws(const Problem& p) {
 // ------------------------------------------------------------ int4 helpers
 
 // 8 codes -> fp16 operand words (see the file comment for the slot order).
+// (w ^ 0x88888888) & m | 0x64006400 equals (w & m) ^ (0x64006400 | (0x88888888
+// & m)), the nibble field and the fp16 exponent bits being disjoint: one
+// 3-input bit operation per word pair.
 __device__ __forceinline__ u32x4 int4_to_f16_magic(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u, u8 = u >> 8;
+  const uint32_t w8 = w >> 8;
   u32x4 r;
-  r[0] = (u & 0x000F000Fu) | 0x64006400u;
-  r[1] = (u & 0x00F000F0u) | 0x64006400u;
-  r[2] = (u8 & 0x000F000Fu) | 0x64006400u;
-  r[3] = (u8 & 0x00F000F0u) | 0x64006400u;
+  r[0] = (w & 0x000F000Fu) ^ 0x64086408u;
+  r[1] = (w & 0x00F000F0u) ^ 0x64806480u;
+  r[2] = (w8 & 0x000F000Fu) ^ 0x64086408u;
+  r[3] = (w8 & 0x00F000F0u) ^ 0x64806480u;
   return r;
 }
 
@@ -569,8 +572,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                 const float s = (float)__builtin_bit_cast(
                     _Float16, (uint16_t)(sv[rb] >> (16 * j)));
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
+                for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
               }
             }
           }
