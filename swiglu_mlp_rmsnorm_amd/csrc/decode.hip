@@ -351,7 +351,10 @@ __global__ __launch_bounds__(512) void k_act_prep(const uint16_t* __restrict__ x
 // with a P-deep ring of weight tiles (and global activation chunks) in flight.
 enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5, ACT_F16 = 6 };
 
-template <int MODE, int NCB, int RB, int S, int P, class StageLoad, class StageStore>
+// EMAX: accumulator rows per lane that can hold a token (int4 scale FMAs;
+// 1 when M = 1).
+template <int MODE, int NCB, int RB, int S, int P, int EMAX = 4, class StageLoad,
+          class StageStore>
 __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                                           const uint16_t* __restrict__ sc,
                                           const uint16_t* __restrict__ act0,
@@ -572,7 +575,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                 const float s = (float)__builtin_bit_cast(
                     _Float16, (uint16_t)(sv[rb] >> (16 * j)));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
+                for (int e = 0; e < EMAX; ++e) acc[rb][cb][e] = fmaf(s, dq[e], acc[rb][cb][e]);
               }
             }
           }
@@ -615,7 +618,7 @@ constexpr int kStageRegsDown = 4;     // the same for the down kernel
 
 // RES (bf16): the activations are the residual stream h = bf16_rne(x + res);
 // workgroup 0 stores h to hout. act: the gate activation.
-template <int WK, int NCB, int RB, int S, int P, bool LDS, bool RES>
+template <int WK, int NCB, int RB, int S, int P, bool LDS, bool RES, int EMAX = 4>
 __global__ __launch_bounds__(64 * S) void k_decode_gateup(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ act0,
     const uint16_t* __restrict__ act1, float eps, uint16_t* __restrict__ a0,
@@ -698,7 +701,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
         }
       }
     };
-    gemv_core<WK == WK_BF16 ? ACT_HL_LDS : ACT_Q4_LDS, NCB, RB, S, P>(
+    gemv_core<WK == WK_BF16 ? ACT_HL_LDS : ACT_Q4_LDS, NCB, RB, S, P, EMAX>(
         w, sc, lhi, llo, rb0, d, M, 0, units, acc, ss, d, 0, stage_load, stage_store);
     stash<RB, NCB>(red, acc);
   } else {
@@ -763,7 +766,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
 // the result does not depend on arrival order. No workgroup waits for
 // another.
 // LDS: the workgroup stages its K range of a in LDS first (small M).
-template <int WK, int NCB, int RB, int S, int P, bool LDS>
+template <int WK, int NCB, int RB, int S, int P, bool LDS, int EMAX = 4>
 __global__ __launch_bounds__(64 * S) void k_decode_down(
     const void* __restrict__ w, const uint16_t* __restrict__ sc, const uint16_t* __restrict__ a0,
     const uint16_t* __restrict__ a1, uint16_t* __restrict__ y, int M, int d, int ff,
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
         if constexpr (WK == WK_BF16) *reinterpret_cast<u32x4*>(llo + dst(c)) = ld16(a1 + src(c));
       }
     };
-    gemv_core<WK == WK_BF16 ? ACT_HL_LDS : ACT_Q4_LDS, NCB, RB, S, P>(
+    gemv_core<WK == WK_BF16 ? ACT_HL_LDS : ACT_Q4_LDS, NCB, RB, S, P, EMAX>(
         w, sc, lhi, llo, rb0, ff, M, u0, ucnt > 0 ? ucnt : 0, acc, ss, astride, kbeg, stage_load,
         stage_store);
   } else {
@@ -1059,7 +1062,11 @@ static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool l
   constexpr int DP = WK == WK_INT4 ? FMLP_Q4_DN_P : FMLP_DN_P;
   const int kind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
   const dim3 grid(p.d / (16 * DRB), splits), block(64 * S);
-  if (STAGE && lds)
+  if (STAGE && lds && WK == WK_INT4 && p.M == 1)  // one accumulator row holds the token
+    launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, STAGE, 1>, grid, block,
+                  (uint32_t)lds_bytes, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d,
+                  p.ff, ws.part, ws.cnt);
+  else if (STAGE && lds)
     launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, STAGE>, grid, block,
                   (uint32_t)lds_bytes, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d,
                   p.ff, ws.part, ws.cnt);
@@ -1083,7 +1090,9 @@ static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t
                   ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt, p.act, p.res, p.hout);
   };
   // the int4 path has added the residual in its prep kernel already
-  if (kStage && lds)
+  if (kStage && lds && WK == WK_INT4 && p.M == 1)  // one accumulator row holds the token
+    go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false, 1>, (uint32_t)lds_bytes);
+  else if (kStage && lds)
     go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false>, (uint32_t)lds_bytes);
   else if (WK == WK_BF16 && p.res)
     go(k_decode_gateup<WK, NCB, RB, S, GP, false, WK == WK_BF16>, 0);
