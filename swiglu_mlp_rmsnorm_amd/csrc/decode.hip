@@ -1062,8 +1062,10 @@ static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool l
   constexpr int DP = WK == WK_INT4 ? FMLP_Q4_DN_P : FMLP_DN_P;
   const int kind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
   const dim3 grid(p.d / (16 * DRB), splits), block(64 * S);
-  if (STAGE && lds && WK == WK_INT4 && p.M == 1)  // one accumulator row holds the token
-    launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, STAGE, 1>, grid, block,
+  // int4 at M = 1: one accumulator row per lane holds the token
+  constexpr int kEmax1 = WK == WK_INT4 ? 1 : 4;
+  if (STAGE && lds && WK == WK_INT4 && p.M == 1)
+    launch_kernel(kind, k_decode_down<WK, NCB, DRB, S, DP, STAGE, kEmax1>, grid, block,
                   (uint32_t)lds_bytes, stream, p.w_down, p.s_down, ws.a0, ws.a1, p.y, p.M, p.d,
                   p.ff, ws.part, ws.cnt);
   else if (STAGE && lds)
@@ -1090,8 +1092,10 @@ static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t
                   ws.a1, p.M, p.d, p.ff, ws.cnt, ncnt, p.act, p.res, p.hout);
   };
   // the int4 path has added the residual in its prep kernel already
-  if (kStage && lds && WK == WK_INT4 && p.M == 1)  // one accumulator row holds the token
-    go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false, 1>, (uint32_t)lds_bytes);
+  // int4 at M = 1: one accumulator row per lane holds the token
+  constexpr int kEmax1 = WK == WK_INT4 ? 1 : 4;
+  if (kStage && lds && WK == WK_INT4 && p.M == 1)
+    go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false, kEmax1>, (uint32_t)lds_bytes);
   else if (kStage && lds)
     go(k_decode_gateup<WK, NCB, RB, S, GP, kStage, false>, (uint32_t)lds_bytes);
   else if (WK == WK_BF16 && p.res)
