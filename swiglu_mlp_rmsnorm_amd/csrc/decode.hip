@@ -457,7 +457,6 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
               l[cb] = lb[p][cb];
             }
           }
-          if (it + P < nit) issue(p, it + P);
           if constexpr (MODE == ACT_F16) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) wv[rb] = bf16x8_to_f16x8(wv[rb]);
@@ -493,6 +492,10 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
               }
             }
           }
+          // the slot's next tile is issued once this one has been consumed,
+          // so its registers are reused in place rather than copied out
+          // (measured 0.5-2% faster than issuing before the MFMAs)
+          if (it + P < nit) issue(p, it + P);
         }
       }
     }
@@ -562,7 +565,10 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
                 av[j][cb] = ab[p][j][cb];
             }
           }
-          if (it + P < nit) issue(p, it + P);
+          // (unstaged activations: the next tile is issued after this one is
+          // consumed, as in the bf16 branch; measured: down 6% faster at
+          // M = 16, while the staged kernels at M <= 4 keep the early issue)
+          if (kLds && it + P < nit) issue(p, it + P);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (q * 4 + j >= nkb) break;
@@ -579,6 +585,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
               }
             }
           }
+          if (!kLds && it + P < nit) issue(p, it + P);
         }
       }
     }
