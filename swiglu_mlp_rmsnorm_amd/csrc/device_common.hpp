@@ -85,17 +85,24 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// SiLU(t) * u in fp32, SiLU(t) = t / (1 + e^-t). For t -> -inf the quotient
-// tends to -0 without producing NaN.
-__device__ __forceinline__ float silu_mul(float t, float u) {
-  return t / (1.0f + expf(-t)) * u;
+// sigma(z) = 1 / (1 + e^-z) with the hardware exponential and reciprocal
+// (about 1 ulp each; the results are rounded to fp16 or bf16 afterwards).
+// Limits: 0 for z -> -inf (e^-z = inf), 1 for z -> +inf.
+__device__ __forceinline__ float fast_sigmoid(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// SiLU(t) * u in fp32, SiLU(t) = t sigma(t). For finite t -> -inf it tends
+// to -0 (sigma underflows to 0) without producing NaN.
+__device__ __forceinline__ float silu_mul(float t, float u) { return t * fast_sigmoid(t) * u; }
+
 // Gate activations (enum fmlp_activation): 0 SiLU; 1 GELU, tanh form
-// 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))); 2 GELU, erf form
+// 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))), evaluated through the
+// identity 0.5 (1 + tanh y) = sigma(2 y); 2 GELU, erf form
 // 0.5 t (1 + erf(t / sqrt 2)). Both GELU forms tend to -0 for t -> -inf.
 __device__ __forceinline__ float act_mul(int act, float t, float u) {
-  if (act == 1) return 0.5f * t * (1.0f + tanhf(0.7978845608028654f * (t + 0.044715f * t * t * t))) * u;
+  if (act == 1)
+    return t * fast_sigmoid(1.5957691216057308f * (t + 0.044715f * t * t * t)) * u;
   if (act == 2) return 0.5f * t * (1.0f + erff(t * 0.7071067811865476f)) * u;
   return silu_mul(t, u);
 }
