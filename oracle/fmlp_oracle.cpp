@@ -30,6 +30,12 @@
 //       the pages give no GELU formula, so both usual forms are offered:
 //       erf form t * Phi(t) = 0.5 t (1 + erf(t / sqrt 2)), and tanh form
 //       0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3)));
+//     fp16 weight storage: a bf16 weight becomes the fp16 value of largest
+//       magnitude not above its own, with its sign (truncation toward zero).
+//       Every bf16 value in the fp16 normal range [2^-14, 65504] is exact in
+//       fp16 (8 significant bits of 11); only the subnormal range rounds, and
+//       non-finite values or magnitudes above 65504 are range errors. The
+//       forward then reads those fp16 values as the weights;
 //     residual prologue: with a residual input r (the previous sublayer's
 //       output), the residual stream h = bf16_rne(x + r) is formed, written
 //       out, and normalised in place of x (the residual add fused with the
@@ -339,18 +345,48 @@ void oracle_dequant_int4(const uint8_t* q, const uint16_t* scales,
                        (float)int4_at(q + r * (K / 2), k);
 }
 
+// bf16 -> fp16 by truncation toward zero, over n elements (bit patterns),
+// written from the binary16 format: the magnitude in units of the fp16 spacing
+// at its binade (2^-24 below 2^-14), rounded down, fields rebuilt, sign kept.
+// Returns how many elements are not finite or exceed 65504 in magnitude;
+// their outputs are set to 0.
+int64_t oracle_bf16_to_f16_trunc(const uint16_t* w, int64_t n, uint16_t* out) {
+  int64_t bad = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = bf16_value(w[i]);
+    const double a = std::fabs(v);
+    if (!std::isfinite(v) || a > 65504.0) {
+      ++bad;
+      out[i] = 0;
+      continue;
+    }
+    uint16_t bits;
+    if (a < std::ldexp(1.0, -14)) {
+      bits = (uint16_t)std::floor(std::ldexp(a, 24));  // subnormal: unit 2^-24
+    } else {
+      int e2;
+      std::frexp(a, &e2);                                        // a in [2^(e2-1), 2^e2)
+      const double mant = std::floor(std::ldexp(a, 11 - e2));  // in [1024, 2047]
+      bits = (uint16_t)(((e2 - 1 + 15) << 10) | ((int)mant - 1024));
+    }
+    out[i] = (uint16_t)((w[i] & 0x8000u) | bits);
+  }
+  return bad;
+}
+
 // ---------------------------------------------------------------- forward
 
 // Weight access: one callback-free struct per storage kind keeps the three
 // forward variants on the same arithmetic.
 struct WeightView {
-  int kind;                 // 0 bf16, 1 int4 group-32
-  const uint16_t* bf;       // bf16 [rows, K]
+  int kind;                 // 0 bf16, 1 int4 group-32, 2 fp16
+  const uint16_t* bf;       // bf16 (kind 0) or fp16 (kind 2) [rows, K]
   const uint8_t* q;         // int4 [rows, K/2]
   const uint16_t* s;        // fp16 [rows, K/32]
   int64_t K;
   double at(int64_t row, int64_t k) const {
     if (kind == 0) return bf16_value(bf[row * K + k]);
+    if (kind == 2) return f16_value(bf[row * K + k]);
     return f16_value(s[row * (K / 32) + k / 32]) *
            (double)int4_at(q + row * (K / 2), k);
   }
@@ -445,6 +481,18 @@ void oracle_forward_int4(const uint16_t* x, const uint16_t* gamma, double eps,
                          int64_t M, int64_t d, int64_t ff, double* y) {
   oracle_forward_int4_ex(x, nullptr, nullptr, gamma, eps, 0, q_gu, s_gu, q_down, s_down, M, d,
                          ff, y);
+}
+
+// Eq(1) with fp16 weights: the interleaved w_gu [2ff, d] and w_down [d, ff]
+// hold fp16 values (oracle_bf16_to_f16_trunc of the bf16 matrices), widened
+// exactly to double; activation and residual prologue as in
+// oracle_forward_unfused_ex.
+void oracle_forward_f16_ex(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
+                           const uint16_t* gamma, double eps, int act, const uint16_t* w_gu,
+                           const uint16_t* w_down, int64_t M, int64_t d, int64_t ff, double* y) {
+  WeightView gu{2, w_gu, nullptr, nullptr, d};
+  WeightView dn{2, w_down, nullptr, nullptr, ff};
+  forward_core(x, res, h_out, gamma, eps, act, gu, 0, 2, gu, 1, 2, dn, M, d, ff, y);
 }
 
 // Threads the parallel loops above will use.

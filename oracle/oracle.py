@@ -72,6 +72,9 @@ def _load():
             "oracle_forward_bf16": (None, [P, P, D, P, P, I64, I64, I64, P]),
             "oracle_forward_int4": (None, [P, P, D, P, P, P, P, I64, I64, I64, P]),
             "oracle_omp_threads": (ctypes.c_int, []),
+            "oracle_bf16_to_f16_trunc": (I64, [P, I64, P]),
+            "oracle_forward_f16_ex": (None, [P, P, P, P, D, ctypes.c_int, P, P, I64, I64, I64,
+                                             P]),
             "oracle_tile_bf16": (None, [P, I64, I64, P]),
             "oracle_untile_bf16": (None, [P, I64, I64, P]),
             "oracle_int4_tiled_code_bytes": (I64, [I64, I64]),
@@ -261,6 +264,32 @@ def forward_int4_ex(x, gamma, eps, q_gu, s_gu, q_down, s_down, act=ACT_SILU, res
     _load().oracle_forward_int4_ex(_p(x), None if res is None else _p(res),
                                    None if h is None else _p(h), _p(gamma), eps, act,
                                    _p(q_gu), _p(s_gu), _p(q_down), _p(s_down), M, d, ff, _p(y))
+    return y, h
+
+
+def bf16_to_f16_trunc(w: np.ndarray):
+    """bf16 -> fp16 bits, truncation toward zero (exact in the fp16 normal
+    range); returns (out, number of non-finite or > 65504 elements)."""
+    w = _c(w, np.uint16)
+    out = np.empty(w.shape, np.uint16)
+    bad = _load().oracle_bf16_to_f16_trunc(_p(w), w.size, _p(out))
+    return out, int(bad)
+
+
+def forward_f16_ex(x, gamma, eps, w_gu, w_down, act=ACT_SILU, residual=None):
+    """Eq(1) with fp16 weights (interleaved w_gu [2ff, d], w_down [d, ff],
+    fp16 bits), gate activation `act` and the optional residual prologue;
+    returns (y fp64 [M, d], h bf16 bits [M, d] or None)."""
+    x, gamma = _c(x, np.uint16), _c(gamma, np.uint16)
+    w_gu, w_down = _c(w_gu, np.uint16), _c(w_down, np.uint16)
+    M, d = x.shape
+    ff = w_gu.shape[0] // 2
+    y = np.empty((M, d), np.float64)
+    res = None if residual is None else _c(residual, np.uint16)
+    h = None if residual is None else np.empty((M, d), np.uint16)
+    _load().oracle_forward_f16_ex(_p(x), None if res is None else _p(res),
+                                  None if h is None else _p(h), _p(gamma), eps, act,
+                                  _p(w_gu), _p(w_down), M, d, ff, _p(y))
     return y, h
 
 

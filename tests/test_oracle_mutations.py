@@ -28,6 +28,11 @@ MUTATIONS = {
     "gelu_forms_swapped": ("if (act == 1) return oracle_gelu_tanh(t);", "if (act == 1) return oracle_gelu_erf(t);"),
     "bf16_round_toward_zero": ("std::nearbyint(std::ldexp(a, 8 - e2))", "std::trunc(std::ldexp(a, 8 - e2))"),
     "residual_not_normalised": ("      xm = h;\n", "      (void)xm;\n"),
+    "f16_subnormal_rounds_nearest": ("std::floor(std::ldexp(a, 24))", "std::nearbyint(std::ldexp(a, 24))"),
+    "f16_sign_dropped": ("out[i] = (uint16_t)((w[i] & 0x8000u) | bits);", "out[i] = bits;"),
+    "f16_exponent_bias": ("(((e2 - 1 + 15) << 10)", "(((e2 - 1 + 16) << 10)"),
+    "f16_range_one_binade_high": ("a > 65504.0", "a > 65536.0"),
+    "f16_weights_read_as_bf16": ("if (kind == 2) return f16_value(", "if (kind == 2) return bf16_value("),
 }
 
 

@@ -508,3 +508,102 @@ def test_int4_forward_ex_matches_torch_composition():
                                   residual=res)
     np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
     assert np.array_equal(h, hb.view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------ fp16 weight storage
+# bf16 -> fp16 by truncation toward zero. Expected patterns worked out by hand
+# from the two formats: bf16 = sign | 8-bit exponent (bias 127) | 7 bits;
+# fp16 = sign | 5-bit exponent (bias 15) | 10 bits, subnormal unit 2^-24.
+F16_TRUNC_HAND = [
+    (0x3F80, 0x3C00),  # 1.0
+    (0xC000, 0xC000),  # -2.0
+    (0x477F, 0x7BF8),  # 65280 = 2^15 * (1 + 1016/1024), largest bf16 below 65504
+    (0x3880, 0x0400),  # 2^-14, smallest fp16 normal
+    (0x3800, 0x0200),  # 2^-15 = 512 * 2^-24, exact subnormal
+    (0x3380, 0x0001),  # 2^-24, smallest fp16 subnormal
+    (0x33C0, 0x0001),  # 1.5 * 2^-24 truncates to 2^-24 (nearest-even would give 2 units)
+    (0x3300, 0x0000),  # 2^-25 truncates to +0
+    (0xB300, 0x8000),  # -2^-25 truncates to -0
+    (0x35E0, 0x001C),  # 1.75 * 2^-20 = 28 units of 2^-24
+    (0x8000, 0x8000),  # -0
+]
+F16_TRUNC_RANGE = [0x4780, 0xC780, 0x7F80, 0xFF80, 0x7FC0, 0x7F7F]  # 65536, -65536, +-inf, NaN, max bf16
+
+
+def test_f16_trunc_hand_values():
+    w = np.array([b for b, _ in F16_TRUNC_HAND], np.uint16)
+    out, bad = oracle.bf16_to_f16_trunc(w)
+    assert bad == 0
+    assert [int(v) for v in out] == [h for _, h in F16_TRUNC_HAND]
+    for b in F16_TRUNC_RANGE:
+        _, bad = oracle.bf16_to_f16_trunc(np.array([0x3F80, b], np.uint16))
+        assert bad == 1, hex(b)
+
+
+def test_f16_trunc_every_pattern():
+    # every bf16 pattern: exact in the fp16 normal range, the largest fp16
+    # magnitude not above |v| below it (sign kept), range errors exactly for
+    # non-finite values and magnitudes above 65504; fp16 decoded by numpy
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_values(bits)
+    out, bad = oracle.bf16_to_f16_trunc(bits)
+    err = ~np.isfinite(v) | (np.abs(v) > 65504.0)
+    assert bad == int(err.sum())
+    assert not out[err].any()
+    ok = ~err
+    h = out[ok].view(np.float16)
+    hv, a = h.astype(np.float64), np.abs(v[ok])
+    assert np.array_equal(out[ok] >> 15, bits[ok] >> 15)
+    normal = a >= 2.0 ** -14
+    assert np.array_equal(np.abs(hv[normal]), a[normal])
+    up = np.nextafter(np.abs(h), np.float16(np.inf)).astype(np.float64)
+    assert np.all(np.abs(hv) <= a) and np.all(a < up)
+
+
+def _f16_layer(M, d, ff, seed):
+    x, g, wg, wu, wd = _rand_layer(M, d, ff, seed)
+    wgu = oracle.pack_interleaved(wg, wu)
+    # a few weights in the fp16 subnormal range, where the conversion rounds
+    tiny = bf16_bits(np.array([3.1e-7, -4.7e-6, 2.9e-5, -6.0e-5], np.float32))
+    wgu.reshape(-1)[[3, 70, 1000, 5001]] = tiny
+    wd.reshape(-1)[[5, 77, 900]] = tiny[:3]
+    return x, g, wgu, wd
+
+
+@pytest.mark.parametrize("act,approx,with_res", [(oracle.ACT_SILU, None, False),
+                                                 (oracle.ACT_GELU_TANH, "tanh", True)])
+def test_f16_forward_matches_torch_composition(act, approx, with_res):
+    M, d, ff = 3, 128, 160
+    x, g, wgu, wd = _f16_layer(M, d, ff, 850)
+    hgu, bad1 = oracle.bf16_to_f16_trunc(wgu)
+    hd, bad2 = oracle.bf16_to_f16_trunc(wd)
+    assert bad1 == 0 and bad2 == 0
+    res = rand_bf16((M, d), 2.0, 851) if with_res else None
+    X = torch.from_numpy(bf16_values(x))
+    if with_res:
+        hb = (X.float() + torch.from_numpy(bf16_values(res)).float()).to(torch.bfloat16)
+        X = hb.double()
+    WGU = torch.from_numpy(hgu.view(np.float16).astype(np.float64))
+    WD = torch.from_numpy(hd.view(np.float16).astype(np.float64))
+    n = F.rms_norm(X, (d,), torch.from_numpy(bf16_values(g)), 1e-5)
+    z = n @ WGU[0::2].T
+    gate = F.silu(z) if approx is None else F.gelu(z, approximate=approx)
+    ref = ((gate * (n @ WGU[1::2].T)) @ WD.T).numpy()
+    y, h = oracle.forward_f16_ex(x, g, 1e-5, hgu, hd, act=act, residual=res)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+    if with_res:
+        assert np.array_equal(h, hb.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_f16_forward_equals_bf16_forward_when_exact():
+    # weights inside the fp16 normal range convert exactly, so the fp16 forward
+    # reads the same values as the bf16 one and gives the same doubles
+    x, g, wg, wu, wd = _rand_layer(2, 64, 96, 860)
+    wgu = oracle.pack_interleaved(wg, wu)
+    tiny = lambda w: np.abs(bf16_values(w)) < 2.0 ** -14
+    wgu[tiny(wgu)] = wgu[tiny(wgu)] & 0x8000  # signed zeros
+    wd[tiny(wd)] = wd[tiny(wd)] & 0x8000
+    hgu, _ = oracle.bf16_to_f16_trunc(wgu)
+    hd, _ = oracle.bf16_to_f16_trunc(wd)
+    y16, _ = oracle.forward_f16_ex(x, g, 1e-5, hgu, hd)
+    assert np.array_equal(y16, oracle.forward_bf16(x, g, 1e-5, wgu, wd))
