@@ -51,14 +51,15 @@ enum fmlp_status {
   FMLP_ERR_UNSUPPORTED_SHAPE = -2, /* d/ff/M outside the limits above */
   FMLP_ERR_ALIGNMENT = -3,         /* a pointer is not 16-byte aligned */
   FMLP_ERR_WORKSPACE = -4,         /* workspace smaller than fmlp_workspace_size */
-  FMLP_ERR_RANGE = -5,             /* int4 scale not a finite fp16 */
+  FMLP_ERR_RANGE = -5,             /* int4 scale or fp16 weight out of fp16 range */
   FMLP_ERR_HIP = -6,               /* a HIP runtime call or launch failed */
   FMLP_ERR_DEVICE = -7             /* current device is not gfx950 */
 };
 
 enum fmlp_wtype {
   FMLP_W_BF16 = 0,     /* bf16 weights */
-  FMLP_W_INT4_G32 = 1  /* int4 codes + fp16 scales, groups of 32 along K */
+  FMLP_W_INT4_G32 = 1, /* int4 codes + fp16 scales, groups of 32 along K */
+  FMLP_W_F16 = 2       /* fp16 weights (fmlp_convert_f16 of the bf16 tiles) */
 };
 
 enum fmlp_path {
@@ -137,6 +138,24 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
                        void* scales, void* stream);
 
 /*
+ * Convert bf16 weights to fp16 for the FMLP_W_F16 weight type: element i of
+ * out is the fp16 value of largest magnitude not above that of w[i], with its
+ * sign (truncation toward zero). Every bf16 value in the fp16 normal range
+ * [2^-14, 65504] is exact in fp16, so only magnitudes below 2^-14 round,
+ * exactly as the MFMA prefill path rounds bf16 weights before its fp16
+ * products; a forward on the converted weights therefore takes the same
+ * values as one on the bf16 weights there. Element-wise, so it applies to
+ * the tiled matrices (fmlp_pack_interleaved, fmlp_pack_matrix) as to any
+ * other layout. A storage option: the prefill GEMMs' fp16 products then
+ * read the weights as they are, with no conversion in the inner loop.
+ *   w    : bf16 [n], read only.     out : fp16 [n]; must not overlap w.
+ *   n    : element count, a positive multiple of 8.
+ * Synchronises `stream`. Returns FMLP_ERR_RANGE if some w[i] is not finite
+ * or exceeds 65504 in magnitude (out then undefined).
+ */
+int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream);
+
+/*
  * Expand tiled int4 to row-major fp32 [rows, K]: out[r,k] = float(s[r,k/32])
  * * q[r,k], exact in fp32. A test hook for the in-register expansion the
  * int4 forward kernels perform; not used by fmlp_forward.
@@ -166,6 +185,11 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *                             prefill first expands both matrices to fp16
  *                             tiles in the workspace (s*q rounded once to
  *                             fp16), so its workspace holds 6*ff*d bytes more
+ *                FMLP_W_F16: w_gu and w_down as for FMLP_W_BF16, converted
+ *                             by fmlp_convert_f16; scales ignored. Decode
+ *                             takes fp16 n and a at every M (one RMSNorm
+ *                             launch before gate/up); prefill runs its fp16
+ *                             products on them directly
  *   y          : bf16 [M, d], written (round to nearest even); must not
  *                overlap any other buffer.
  *   workspace  : device scratch of at least fmlp_workspace_size(M,d,ff,wtype)
@@ -173,11 +197,11 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *   M == 0 is a no-op returning FMLP_OK (x and y may then be NULL).
  * Accumulation is fp32. The normalised input and the SiLU*mul intermediate
  * are kept as bf16 hi + lo pairs (about 2^-17 relative) on the bf16 decode
- * path, and as fp16 on the int4 decode path and the MFMA prefill path
- * (|values| must stay below 65504 there; the prefill path also converts the
- * weights, or s*q, to fp16, so the same bound holds for them). Not bitwise identical across
- * paths; deterministic for a given path and shape. Concurrent calls must
- * not share a workspace.
+ * path up to 16 tokens, and as fp16 on every other path (|values| must stay
+ * below 65504 there; the prefill path also converts bf16 weights, or s*q,
+ * to fp16 the way fmlp_convert_f16 does, so the same bound holds for them).
+ * Not bitwise identical across paths; deterministic for a given path and
+ * shape. Concurrent calls must not share a workspace.
  */
 int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
                  const void* w_gu, const void* gu_scales, const void* w_down,
@@ -189,7 +213,7 @@ int fmlp_forward(const void* x, const void* gamma, float eps, int32_t wtype,
  * fmlp_forward with the kernel path chosen by the caller (enum fmlp_path);
  * used to test both paths at the same shapes, for either weight type.
  * FMLP_PATH_DECODE with M > 32, and FMLP_PATH_SINGLE_PASS with M > 8 or
- * int4 weights, return FMLP_ERR_UNSUPPORTED_SHAPE.
+ * weights other than bf16, return FMLP_ERR_UNSUPPORTED_SHAPE.
  */
 int fmlp_forward_path(const void* x, const void* gamma, float eps,
                       int32_t wtype, const void* w_gu, const void* gu_scales,

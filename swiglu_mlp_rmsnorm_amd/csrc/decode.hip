@@ -142,7 +142,9 @@ namespace fmlp {
 // weights; bf16 weights with fp16 activations (several tokens: one MFMA per
 // tile instead of two and half the activation bytes, the weight tile
 // converted to fp16 in registers).
-enum { WK_BF16 = 0, WK_INT4 = 1, WK_BF16H = 2 };
+enum { WK_BF16 = 0, WK_INT4 = 1, WK_BF16H = 2, WK_F16 = 3 };
+// bf16 or fp16 weights read with fp16 activations
+constexpr bool wk_h16(int wk) { return wk == WK_BF16H || wk == WK_F16; }
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -339,6 +341,7 @@ __global__ __launch_bounds__(512) void k_act_prep(const uint16_t* __restrict__ x
 //                [M, K] like x); h is also stored to hout when that is given
 //   ACT_F16    : bf16 weights, each tile converted to fp16 in registers;
 //                act0 = fp16 [M, K], natural order; one f16 MFMA per tile
+//   ACT_F16W   : as ACT_F16 on fp16 weights (no conversion)
 // Global activations are read into the ring with the weights. Staged ones
 // are [M, astride] rows whose first element is k = kbase; they are read
 // from LDS as they are used. stage_load() issues the workgroup's loads of
@@ -349,7 +352,10 @@ __global__ __launch_bounds__(512) void k_act_prep(const uint16_t* __restrict__ x
 // 16 rows x 4 groups) + scales. The K units u0 .. u0+ucnt-1 are covered;
 // each wave walks units u0+wave, u0+wave+S, ...
 // with a P-deep ring of weight tiles (and global activation chunks) in flight.
-enum { ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5, ACT_F16 = 6 };
+enum {
+  ACT_X = 0, ACT_HL = 1, ACT_Q4 = 2, ACT_HL_LDS = 3, ACT_Q4_LDS = 4, ACT_XR = 5, ACT_F16 = 6,
+  ACT_F16W = 7
+};
 
 // EMAX: accumulator rows per lane that can hold a token (int4 scale FMAs;
 // 1 when M = 1).
@@ -383,7 +389,8 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
     for (int cb = 0; cb < NCB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr bool kX = MODE == ACT_X || MODE == ACT_XR;  // activations from x (and res)
-  if constexpr (kX || MODE == ACT_HL || MODE == ACT_HL_LDS || MODE == ACT_F16) {
+  if constexpr (kX || MODE == ACT_HL || MODE == ACT_HL_LDS || MODE == ACT_F16 ||
+                MODE == ACT_F16W) {
     // unit = one 32-column group
     const uint16_t* wt = static_cast<const uint16_t*>(w) + lane * 8;
     const int nit = wave < ucnt ? (ucnt - wave + S - 1) / S : 0;
@@ -457,9 +464,11 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
               l[cb] = lb[p][cb];
             }
           }
-          if constexpr (MODE == ACT_F16) {
+          if constexpr (MODE == ACT_F16 || MODE == ACT_F16W) {
+            if constexpr (MODE == ACT_F16) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) wv[rb] = bf16x8_to_f16x8(wv[rb]);
+              for (int rb = 0; rb < RB; ++rb) wv[rb] = bf16x8_to_f16x8(wv[rb]);
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -611,8 +620,8 @@ __device__ __forceinline__ void stash(f32x4* red, const f32x4 (&acc)[RB][NCB]) {
 // Writes a = a0 + a1 (bf16 hi/lo, natural order, [M, ff]).
 // int4: activations are the prepared fp16 n (ACT_Q4); writes a0 = fp16 a in
 // the int4 slot order, [M, ff]. bf16 weights with fp16 activations
-// (WK_BF16H): the prepared fp16 n in natural order (ACT_F16); writes a0 =
-// fp16 a, [M, ff].
+// (WK_BF16H), or fp16 weights (WK_F16): the prepared fp16 n in natural order
+// (ACT_F16, ACT_F16W); writes a0 = fp16 a, [M, ff].
 // LDS: the workgroup first stages its activations in LDS (dynamic shared
 // memory): gamma * x as the bf16 hi + lo pair with the per-token sums of x^2
 // (bf16), or a copy of n (int4); for small M, where the per-wave activation
@@ -712,7 +721,11 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
         w, sc, lhi, llo, rb0, d, M, 0, units, acc, ss, d, 0, stage_load, stage_store);
     stash<RB, NCB>(red, acc);
   } else {
-    gemv_core<WK == WK_BF16 ? (RES ? ACT_XR : ACT_X) : WK == WK_BF16H ? ACT_F16 : ACT_Q4, NCB,
+    gemv_core<WK == WK_BF16    ? (RES ? ACT_XR : ACT_X)
+              : WK == WK_BF16H ? ACT_F16
+              : WK == WK_F16   ? ACT_F16W
+                               : ACT_Q4,
+              NCB,
               RB, S, P>(w, sc, act0, act1, rb0, d, M, 0, units, acc, ss, d, 0, [] {}, [] {}, res,
                         blockIdx.x == 0 ? hout : nullptr);
     stash<RB, NCB>(red, acc);
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(64 * S) void k_decode_gateup(
       const uint16_t h = bf16_rne(av);
       a0[(int64_t)t * ff + i] = h;
       a1[(int64_t)t * ff + i] = bf16_rne(av - __uint_as_float((uint32_t)h << 16));
-    } else if (WK == WK_BF16H) {
+    } else if (wk_h16(WK)) {
       a0[(int64_t)t * ff + i] = __builtin_bit_cast(uint16_t, (_Float16)act_mul(act, g, u));
     } else {
       const float av = act_mul(act, g, u);
@@ -827,7 +840,11 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
         w, sc, lhi, llo, rb0, ff, M, u0, ucnt > 0 ? ucnt : 0, acc, ss, astride, kbeg, stage_load,
         stage_store);
   } else {
-    gemv_core<WK == WK_BF16 ? ACT_HL : WK == WK_BF16H ? ACT_F16 : ACT_Q4, NCB, RB, S, P>(
+    gemv_core<WK == WK_BF16    ? ACT_HL
+              : WK == WK_BF16H ? ACT_F16
+              : WK == WK_F16   ? ACT_F16W
+                               : ACT_Q4,
+              NCB, RB, S, P>(
         w, sc, a0, a1, rb0, ff, M, u0, ucnt > 0 ? ucnt : 0, acc, ss, ff, 0, [] {}, [] {});
   }
   stash<RB, NCB>(red, acc);
@@ -1200,6 +1217,9 @@ hipError_t launch_decode(const Problem& p, hipStream_t stream) {
   if (p.wtype == 1)
     return p.M <= 16 ? launch_decode_t<WK_INT4, 1>(p, stream)
                      : launch_decode_t<WK_INT4, 2>(p, stream);
+  if (p.wtype == 2)
+    return p.M <= 16 ? launch_decode_t<WK_F16, 1>(p, stream)
+                     : launch_decode_t<WK_F16, 2>(p, stream);
   if (p.M >= FMLP_H16_MIN_M)
     return p.M <= 16 ? launch_decode_t<WK_BF16H, 1>(p, stream)
                      : launch_decode_t<WK_BF16H, 2>(p, stream);

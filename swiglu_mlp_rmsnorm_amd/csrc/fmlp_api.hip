@@ -32,6 +32,10 @@ Span span(const void* p, size_t bytes) {
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
 
+bool wtype_ok(int32_t wtype) {
+  return wtype == FMLP_W_BF16 || wtype == FMLP_W_INT4_G32 || wtype == FMLP_W_F16;
+}
+
 bool shape_ok(int64_t d, int64_t ff) {
   return d > 0 && ff > 0 && d % 32 == 0 && ff % 32 == 0 && d <= kMaxD && ff <= kMaxFF;
 }
@@ -64,7 +68,7 @@ int check_device() {
   return g_dev_ok[dev] ? FMLP_OK : FMLP_ERR_DEVICE;
 }
 
-std::mutex g_quant_mutex;  // the range flag is one per device
+std::mutex g_flag_mutex;  // the range flags are one per device
 
 }  // namespace
 
@@ -77,7 +81,7 @@ const char* fmlp_status_string(int status) {
     case FMLP_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
     case FMLP_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
     case FMLP_ERR_WORKSPACE: return "workspace too small";
-    case FMLP_ERR_RANGE: return "int4 scale out of fp16 range";
+    case FMLP_ERR_RANGE: return "value out of fp16 range";
     case FMLP_ERR_HIP: return "HIP runtime error";
     case FMLP_ERR_DEVICE: return "current device is not gfx950";
     default: return "unknown status";
@@ -133,11 +137,25 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* sc
              ss = span(scales, (size_t)fmlp::int4_scale_bytes(rows, K));
   if (overlap(sw, sq) || overlap(sw, ss) || overlap(sq, ss)) return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;
-  std::lock_guard<std::mutex> lock(g_quant_mutex);
+  std::lock_guard<std::mutex> lock(g_flag_mutex);
   int range_error = 0;
   hipError_t e = fmlp::launch_quantize(static_cast<const uint16_t*>(w), rows, K,
                                        static_cast<uint8_t*>(q), static_cast<uint16_t*>(scales),
                                        static_cast<hipStream_t>(stream), &range_error);
+  if (e != hipSuccess) return hip_fail(e);
+  return range_error ? FMLP_ERR_RANGE : FMLP_OK;
+}
+
+int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream) {
+  if (!w || !out || n <= 0 || n % 8 != 0) return FMLP_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(out)) return FMLP_ERR_ALIGNMENT;
+  if (overlap(span(w, (size_t)n * 2), span(out, (size_t)n * 2))) return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  std::lock_guard<std::mutex> lock(g_flag_mutex);
+  int range_error = 0;
+  hipError_t e = fmlp::launch_convert_f16(static_cast<const uint16_t*>(w),
+                                          static_cast<uint16_t*>(out), n,
+                                          static_cast<hipStream_t>(stream), &range_error);
   if (e != hipSuccess) return hip_fail(e);
   return range_error ? FMLP_ERR_RANGE : FMLP_OK;
 }
@@ -159,8 +177,7 @@ int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K
 }
 
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
-  if (M < 0 || M > kMaxM || !shape_ok(d, ff) || (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32))
-    return 0;
+  if (M < 0 || M > kMaxM || !shape_ok(d, ff) || !wtype_ok(wtype)) return 0;
   // the largest need of the paths the problem may take; the single-pass
   // term is kept at its M = kFusedMaxM value above that, so the size never
   // decreases as M grows (a buffer sized for the largest M serves them all)
@@ -181,7 +198,7 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
                     const void* gu_scales, const void* w_down, const void* down_scales, void* y,
                     int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
                     void* stream, int32_t path) {
-  if (wtype != FMLP_W_BF16 && wtype != FMLP_W_INT4_G32) return FMLP_ERR_INVALID_ARG;
+  if (!wtype_ok(wtype)) return FMLP_ERR_INVALID_ARG;
   if (activation != FMLP_ACT_SILU && activation != FMLP_ACT_GELU_TANH &&
       activation != FMLP_ACT_GELU_ERF)
     return FMLP_ERR_INVALID_ARG;
@@ -206,7 +223,7 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
   const bool decode = single || path == FMLP_PATH_DECODE ||
                       (path == FMLP_PATH_AUTO && M <= fmlp::kDecodeMaxM);
   if (decode && M > fmlp::kDecodeMaxM) return FMLP_ERR_UNSUPPORTED_SHAPE;
-  if (single && (int4 || M > fmlp::kFusedMaxM)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (single && (wtype != FMLP_W_BF16 || M > fmlp::kFusedMaxM)) return FMLP_ERR_UNSUPPORTED_SHAPE;
 
   const size_t need = single   ? fmlp::fused_partial_bytes(M, d, ff)
                       : decode ? fmlp::decode_workspace_bytes(M, d, ff)

@@ -13,10 +13,10 @@ struct Problem {
   const uint16_t* x;       // bf16 [M, d]
   const uint16_t* gamma;   // bf16 [d]
   float eps;
-  int wtype;               // 0 bf16, 1 int4 group-32
-  const void* w_gu;        // tiled bf16 [2ff, d] | tiled int4 codes
+  int wtype;               // 0 bf16, 1 int4 group-32, 2 fp16
+  const void* w_gu;        // tiled bf16 or fp16 [2ff, d] | tiled int4 codes
   const uint16_t* s_gu;    // tiled fp16 scales (int4)
-  const void* w_down;      // tiled bf16 [d, ff] | tiled int4 codes
+  const void* w_down;      // tiled bf16 or fp16 [d, ff] | tiled int4 codes
   const uint16_t* s_down;  // tiled fp16 scales (int4)
   uint16_t* y;             // bf16 [M, d]
   int M, d, ff;
@@ -47,6 +47,8 @@ hipError_t launch_tile_matrix(const uint16_t* w, uint16_t* out, int64_t R, int64
                               hipStream_t stream);
 hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q,
                            uint16_t* scales, hipStream_t stream, int* range_error);
+hipError_t launch_convert_f16(const uint16_t* w, uint16_t* out, int64_t n, hipStream_t stream,
+                              int* range_error);
 hipError_t launch_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t K,
                           float* out, hipStream_t stream);
 

@@ -60,6 +60,46 @@ hipError_t launch_tile_matrix(const uint16_t* w, uint16_t* out, int64_t R, int64
   return launch_tile(w, nullptr, out, R, K, stream);
 }
 
+// ---------------------------------------------------------------- fp16 weights
+__device__ int g_f16_range_error;
+
+__global__ void k_f16_flag_reset() { g_f16_range_error = 0; }
+
+// bf16 -> fp16 by truncation toward zero, 8 elements per thread: the same
+// conversion the prefill GEMM applies to bf16 weight fragments in registers
+// (bf16x8_to_f16x8), so a forward on the converted weights reads the values
+// that one on the bf16 weights does. Non-finite values and magnitudes above
+// 65504 raise the range flag (NaN fails the comparison as well).
+__global__ __launch_bounds__(256) void k_convert_f16(const uint16_t* __restrict__ w,
+                                                     uint16_t* __restrict__ out, int64_t n8) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n8) return;
+  const u32x4 v = ld16(w + t * 8);
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    ok = ok && fabsf(bf16_lo(v[j])) <= 65504.0f && fabsf(bf16_hi(v[j])) <= 65504.0f;
+  if (!ok) atomicOr(&g_f16_range_error, 1);
+  st16(out + t * 8, bf16x8_to_f16x8(v));
+}
+
+hipError_t launch_convert_f16(const uint16_t* w, uint16_t* out, int64_t n, hipStream_t stream,
+                              int* range_error) {
+  hipLaunchKernelGGL(k_f16_flag_reset, dim3(1), dim3(1), 0, stream);
+  const int64_t n8 = n / 8;
+  launch_kernel(KK_CONVERT_F16, k_convert_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                stream, w, out, n8);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int flag = 0;
+  e = hipMemcpyFromSymbolAsync(&flag, HIP_SYMBOL(g_f16_range_error), sizeof(int), 0,
+                               hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return e;
+  e = hipStreamSynchronize(stream);
+  *range_error = flag;
+  return e;
+}
+
 // ---------------------------------------------------------------- int4
 __device__ int g_quant_range_error;
 

@@ -686,7 +686,8 @@ static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, int sp
 size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype) {
   size_t total = 0;
   prefill_ws(nullptr, M, d, ff, plan_down(M, d, ff).splits, &total);
-  if (wtype == 0) total -= align256((size_t)2 * ff * d * 2) + align256((size_t)d * ff * 2);
+  // (the fp16 expansion of the weights: int4 only)
+  if (wtype != 1) total -= align256((size_t)2 * ff * d * 2) + align256((size_t)d * ff * 2);
   return total;
 }
 
@@ -737,6 +738,9 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   if (p.wtype == 0)
     return prefill_gemms<false>(p, w, reinterpret_cast<const uint16_t*>(p.w_gu),
                                 reinterpret_cast<const uint16_t*>(p.w_down), g2, stream);
+  if (p.wtype == 2)  // fp16 weights: the fp16 products read them as they are
+    return prefill_gemms<true>(p, w, reinterpret_cast<const uint16_t*>(p.w_gu),
+                               reinterpret_cast<const uint16_t*>(p.w_down), g2, stream);
   if ((e = launch_dequant_f16(reinterpret_cast<const uint8_t*>(p.w_gu), p.s_gu, 2 * p.ff, p.d,
                               w.wgu16, stream)) != hipSuccess)
     return e;

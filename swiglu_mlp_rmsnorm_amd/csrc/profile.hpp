@@ -27,6 +27,7 @@ enum KernelKind {
   KK_DECODE_FUSED_BF16,
   KK_PARTIAL_REDUCE,
   KK_READ_PROBE,
+  KK_CONVERT_F16,
   KK_COUNT
 };
 

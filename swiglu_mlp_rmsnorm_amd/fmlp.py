@@ -30,6 +30,7 @@ FMLP_ERR_DEVICE = -7
 
 FMLP_W_BF16 = 0
 FMLP_W_INT4_G32 = 1
+FMLP_W_F16 = 2
 
 FMLP_PATH_AUTO = 0
 FMLP_PATH_DECODE = 1
@@ -42,7 +43,7 @@ FMLP_ACT_GELU_ERF = 2
 
 EXPORTS = (
     "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",
-    "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
+    "fmlp_convert_f16", "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
     "fmlp_profile_read", "fmlp_kernel_name", "fmlp_read_probe",
 )
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.fmlp_int4_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.fmlp_quantize_int4.argtypes = [P, I64, I64, P, P, P]
         L.fmlp_dequant_int4.argtypes = [P, P, I64, I64, P, P]
+        L.fmlp_convert_f16.argtypes = [P, P, I64, P]
         L.fmlp_workspace_size.argtypes = [I64, I64, I64, I32]
         L.fmlp_workspace_size.restype = SZ
         fwd = [P, P, ctypes.c_float, I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.fmlp_kernel_name.argtypes = [I32]
         L.fmlp_kernel_name.restype = ctypes.c_char_p
         for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
-                     "fmlp_quantize_int4", "fmlp_dequant_int4",
+                     "fmlp_quantize_int4", "fmlp_dequant_int4", "fmlp_convert_f16",
                      "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex", "fmlp_last_hip_error",
                      "fmlp_profile_enable", "fmlp_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -201,6 +203,20 @@ def fmlp_dequant_int4(q, scales, rows, K, out=None, stream=None):
     return out
 
 
+def fmlp_convert_f16(w, out=None, stream=None):
+    """bf16 weights (any shape, e.g. the tiled matrices) -> fp16 of the same
+    shape, truncating toward zero; the FMLP_W_F16 weight type."""
+    _need(w, torch.bfloat16, "w")
+    if out is None:
+        out = torch.empty(w.shape, dtype=torch.float16, device=w.device)
+    _need(out, torch.float16, "out")
+    if out.numel() != w.numel():
+        raise ValueError("out must hold as many elements as w")
+    _check(lib().fmlp_convert_f16(_ptr(w), _ptr(out), w.numel(), _stream(stream)),
+           "fmlp_convert_f16")
+    return out
+
+
 def fmlp_workspace_size(M: int, d: int, ff: int, wtype: int = FMLP_W_BF16) -> int:
     return int(lib().fmlp_workspace_size(M, d, ff, wtype))
 
@@ -224,12 +240,13 @@ def _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, 
             if t.numel() < cb or s_.numel() * 2 < sb:
                 raise ValueError("int4 weight buffers too small for the shapes")
     else:
-        _need(w_gu, torch.bfloat16, "w_gu")
-        _need(w_down, torch.bfloat16, "w_down")
+        wdt = torch.float16 if w_gu.dtype == torch.float16 else torch.bfloat16
+        _need(w_gu, wdt, "w_gu")
+        _need(w_down, wdt, "w_down")
         ff = w_down.shape[1]
-        wtype = FMLP_W_BF16
+        wtype = FMLP_W_F16 if wdt == torch.float16 else FMLP_W_BF16
         if w_gu.shape != (2 * ff, d) or w_down.shape != (d, ff):
-            raise ValueError("bf16 weight shapes do not match x")
+            raise ValueError("weight shapes do not match x")
     if gamma.shape != (d,):
         raise ValueError("gamma must be [d]")
     if y is None:
@@ -275,7 +292,7 @@ def fmlp_forward(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, 
     """y = W_down(SiLU(W_gate n) * (W_up n)), n = RMSNorm(x); bf16 x [M,d] -> y [M,d].
 
     bf16 weights: tiled w_gu [2ff,d] (fmlp_pack_interleaved) and tiled w_down
-    [d,ff] (fmlp_pack_matrix). int4 weights: the flat tiled code/scale
+    [d,ff] (fmlp_pack_matrix); fp16 weights: those after fmlp_convert_f16. int4 weights: the flat tiled code/scale
     buffers of fmlp_quantize_int4, with ff given explicitly.
     Output and workspace are allocated with torch when not given.
     """

@@ -92,3 +92,34 @@ class Int4Layer:
 
 def bf16_inputs(M, d, seed, device="cuda"):
     return synth.activations(M, d, seed, device), synth.gamma(d, seed + 1, device)
+
+
+class F16Layer(Bf16Layer):
+    """The seeded bf16 weights converted to fp16 (FMLP_W_F16): the library
+    converts its packed tiles, the oracle converts the same host bits itself."""
+
+    def __init__(self, d, ff, seed, device="cuda"):
+        super().__init__(d, ff, seed, device)
+        self.hgu_t = F.fmlp_convert_f16(self.wgu_t)
+        self.hd_t = F.fmlp_convert_f16(self.wd_t)
+        wg, wu, wd = self.host
+        hgu, bad1 = oracle.bf16_to_f16_trunc(oracle.pack_interleaved(wg, wu))
+        hd, bad2 = oracle.bf16_to_f16_trunc(wd)
+        assert bad1 == 0 and bad2 == 0
+        self.host16 = (hgu, hd)
+
+    def oracle(self, x, g, eps):
+        return oracle.forward_f16_ex(synth.bits(x), synth.bits(g), eps, *self.host16)[0]
+
+    def forward(self, x, g, eps, **kw):
+        return F.fmlp_forward_path(x, g, eps, self.hgu_t, self.hd_t, **kw)
+
+    def oracle_ex(self, x, g, eps, act, res):
+        return oracle.forward_f16_ex(synth.bits(x), synth.bits(g), eps, *self.host16, act=act,
+                                     residual=None if res is None else synth.bits(res))
+
+    def forward_ex(self, x, g, eps, **kw):
+        return F.fmlp_forward_ex(x, g, eps, self.hgu_t, self.hd_t, **kw)
+
+    def forward_bf16(self, x, g, eps, **kw):
+        return F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **kw)

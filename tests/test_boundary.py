@@ -70,6 +70,10 @@ def fwd(M=1, d=256, ff=704, eps=1e-5, wtype=0, path=0, ws_bytes=BIG, **over):
     (dict(M=33, path=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
     (dict(M=9, path=3), F.FMLP_ERR_UNSUPPORTED_SHAPE),
     (dict(M=1, path=3, wtype=1), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(M=1, path=3, wtype=2), F.FMLP_ERR_UNSUPPORTED_SHAPE),
+    (dict(wtype=3), F.FMLP_ERR_INVALID_ARG),
+    (dict(wtype=2, ws_bytes=100), F.FMLP_ERR_WORKSPACE),
+    (dict(wtype=2, y=A["wd"]), F.FMLP_ERR_INVALID_ARG),
     (dict(path=4), F.FMLP_ERR_INVALID_ARG),
     (dict(ws_bytes=100), F.FMLP_ERR_WORKSPACE),
     (dict(y=A["x"]), F.FMLP_ERR_INVALID_ARG),
@@ -133,6 +137,32 @@ def test_int4_prefill_passes_the_host_checks():
     # accept them exactly as they accept bf16 (the call then needs a GPU)
     assert fwd(M=64, wtype=1) == fwd(M=64, wtype=0)
     assert fwd(M=64, wtype=1) != F.FMLP_ERR_UNSUPPORTED_SHAPE
+
+
+def test_f16_weights_pass_the_host_checks():
+    # fp16 weights: same buffer sizes as bf16, scales ignored (may be NULL),
+    # on either path; the workspace matches bf16's except for the single pass
+    for M in (1, 16, 17, 64):
+        assert fwd(M=M, wtype=2, sgu=None, sd=None) == fwd(M=M, wtype=0)
+    ws = F.fmlp_workspace_size
+    assert ws(2048, 4096, 14336, 2) == ws(2048, 4096, 14336, 0)
+    for M in (9, 33):  # no single-pass partials (the bf16 size keeps them at every M)
+        assert ws(M, 4096, 14336, 2) < ws(M, 4096, 14336, 0)
+    assert ws(2048, 4096, 14336, 2) < ws(2048, 4096, 14336, 1)
+
+
+def test_convert_f16_validation():
+    L = F.lib()
+    a, c = A["x"], A["y"]
+    assert L.fmlp_convert_f16(None, c, 64, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, None, 64, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, c, 0, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, c, 60, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, ctypes.c_void_p(A["y"].value + 2), 64,
+                              None) == F.FMLP_ERR_ALIGNMENT
+    assert L.fmlp_convert_f16(a, a, 64, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, ctypes.c_void_p(A["x"].value + 64), 64,
+                              None) == F.FMLP_ERR_INVALID_ARG
 
 
 def test_zero_tokens_is_a_no_op():

@@ -1,0 +1,124 @@
+"""GPU parity of the fp16 weight type (FMLP_W_F16): the library's bf16 ->
+fp16 conversion bit for bit against the oracle's, the forward on converted
+weights against the oracle's forward on its own conversion of the same seeded
+bf16 weights, on both kernel paths, and bit-identity with the bf16 weight
+type where both paths take the same fp16 values (the prefill GEMMs, and
+decode from 17 tokens on, convert bf16 weights in registers exactly as
+fmlp_convert_f16 does)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from swiglu_mlp_rmsnorm_amd import fmlp as F
+from swiglu_mlp_rmsnorm_amd import synth
+
+from parity_util import F16Layer, assert_parity, bf16_inputs
+
+pytestmark = pytest.mark.gpu
+EPS = synth.EPS
+TINY_D, TINY_FF = 256, 704
+
+
+@pytest.fixture(scope="module")
+def tiny16():
+    return F16Layer(TINY_D, TINY_FF, 10)
+
+
+def _dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+# ----------------------------------------------------------------- conversion
+
+def test_convert_every_in_range_pattern_bit_exact():
+    # every bf16 pattern the conversion accepts, padded to a multiple of 8
+    allb = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    v = torch.from_numpy(allb.view(np.int16)).view(torch.bfloat16).double().numpy()
+    keep = allb[np.isfinite(v) & (np.abs(v) <= 65504.0)]
+    keep = np.concatenate([keep, np.zeros((-keep.size) % 8, np.uint16)])
+    out = F.fmlp_convert_f16(_dev_bf16(keep))
+    ref, bad = oracle.bf16_to_f16_trunc(keep)
+    assert bad == 0
+    assert np.array_equal(synth.bits(out), ref)
+
+
+@pytest.mark.parametrize("R,K", [(16, 32), (5728, 704), (8192, 4096)])
+def test_convert_weights_bit_exact(R, K):
+    w = synth.bf16_weight(R, K, 70 + R, "cuda")
+    out = F.fmlp_convert_f16(w)
+    ref, bad = oracle.bf16_to_f16_trunc(synth.bits(w))
+    assert bad == 0 and out.shape == w.shape
+    assert np.array_equal(synth.bits(out), ref)
+
+
+@pytest.mark.parametrize("bad_bits", [0x4780, 0xC780, 0x7F80, 0xFF80, 0x7FC0, 0x7F7F])
+def test_convert_range_error(bad_bits):
+    # one out-of-range element anywhere in a large buffer is reported; a
+    # clean call right after reports nothing (the flag is cleared per call)
+    w = synth.bf16_weight(64, 4096, 71, "cuda")
+    w.view(torch.int16).view(-1)[123457] = int(np.int16(np.uint16(bad_bits)))
+    with pytest.raises(F.FmlpError) as e:
+        F.fmlp_convert_f16(w)
+    assert e.value.status == F.FMLP_ERR_RANGE
+    w.view(torch.int16).view(-1)[123457] = 0
+    F.fmlp_convert_f16(w)
+
+
+# ----------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 9, 16, 17, 31, 32])
+def test_decode_f16_ragged(tiny16, M):
+    x, g = bf16_inputs(M, TINY_D, 900 + M)
+    assert_parity(tiny16.forward(x, g, EPS), tiny16.oracle(x, g, EPS), f"f16 decode M={M}")
+
+
+@pytest.mark.parametrize("M,path", [(33, F.FMLP_PATH_AUTO), (70, F.FMLP_PATH_AUTO),
+                                    (257, F.FMLP_PATH_AUTO), (1, F.FMLP_PATH_PREFILL),
+                                    (32, F.FMLP_PATH_PREFILL)])
+def test_prefill_f16(tiny16, M, path):
+    x, g = bf16_inputs(M, TINY_D, 950 + M)
+    assert_parity(tiny16.forward(x, g, EPS, path=path), tiny16.oracle(x, g, EPS),
+                  f"f16 prefill M={M}")
+
+
+@pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 40), (512, 1376, 5),
+                                    (512, 1376, 70), (1024, 20480, 4), (3072, 256, 20)])
+def test_f16_shapes(d, ff, M):
+    layer = F16Layer(d, ff, 60 + d)
+    x, g = bf16_inputs(M, d, 970 + M)
+    assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"f16 d={d} ff={ff} M={M}")
+
+
+@pytest.mark.parametrize("act", [F.FMLP_ACT_GELU_TANH, F.FMLP_ACT_GELU_ERF])
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 3), (F.FMLP_PATH_DECODE, 20),
+                                    (F.FMLP_PATH_PREFILL, 70)])
+def test_variants_f16(tiny16, act, path, M):
+    x, g = bf16_inputs(M, TINY_D, 990 + M)
+    res = synth.activations(M, TINY_D, 997 + M, "cuda")
+    y, h = tiny16.forward_ex(x, g, EPS, activation=act, residual=res, path=path)
+    ref, href = tiny16.oracle_ex(x, g, EPS, act, res)
+    assert_parity(y, ref, f"f16 act={act} M={M} path={path}")
+    assert np.array_equal(synth.bits(h), href), "residual stream differs"
+
+
+def test_single_pass_rejects_f16(tiny16):
+    x, g = bf16_inputs(2, TINY_D, 999)
+    with pytest.raises(F.FmlpError) as e:
+        tiny16.forward(x, g, EPS, path=F.FMLP_PATH_SINGLE_PASS)
+    assert e.value.status == F.FMLP_ERR_UNSUPPORTED_SHAPE
+
+
+# ----------------------------------------------------------------- bit-identity with bf16
+
+@pytest.mark.parametrize("d,ff,M,path", [
+    (256, 704, 70, F.FMLP_PATH_PREFILL), (256, 704, 5, F.FMLP_PATH_PREFILL),
+    (256, 704, 17, F.FMLP_PATH_DECODE), (256, 704, 32, F.FMLP_PATH_DECODE),
+    (4096, 14336, 512, F.FMLP_PATH_PREFILL), (4096, 14336, 32, F.FMLP_PATH_DECODE),
+])
+def test_f16_weights_equal_bf16_weights_bitwise(d, ff, M, path):
+    layer = F16Layer(d, ff, 80 + M)
+    x, g = bf16_inputs(M, d, 1000 + M)
+    y16 = layer.forward(x, g, EPS, path=path)
+    yb = layer.forward_bf16(x, g, EPS, path=path)
+    assert torch.equal(y16.view(torch.int16), yb.view(torch.int16))
