@@ -54,6 +54,9 @@ def parse():
                     help="gate activation; other than silu runs fmlp_forward_ex")
     ap.add_argument("--residual", action="store_true",
                     help="add a residual input before the norm (fmlp_forward_ex)")
+    ap.add_argument("--weights", choices=("stored", "f16"), default="stored",
+                    help="f16: run bf16 workloads on their weights converted to fp16 "
+                         "(fmlp_convert_f16, the FMLP_W_F16 weight type)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (the "
                          "known-size reference for the HBM byte counters) and exit")
@@ -215,6 +218,9 @@ def run_one(wname, M, steps, warmup, args):
     w = synth.WORKLOADS[wname]
     dev = torch.device("cuda:0")
     d, ff = w.d, w.ff
+    w16 = args.weights == "f16"
+    if w16 and w.wtype != "bf16":
+        raise SystemExit(f"--weights f16 converts bf16 weights; {wname} holds {w.wtype}")
     path = args.path if args.path != "auto" else ("decode" if M <= 32 else "prefill")
     pcode = None if args.path == "auto" else PATHS[args.path]  # None: fmlp_forward itself
     ex = args.activation != "silu" or args.residual  # the variants run fmlp_forward_ex
@@ -228,14 +234,18 @@ def run_one(wname, M, steps, warmup, args):
                 host0 = tuple(synth.bits(t) for t in layers[0])
         else:
             wg, wu, wd = synth.layer_bf16(w, l, dev)
-            layers.append((F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd)))
+            L = (F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
+            if w16:  # (2 bytes per weight either way)
+                L = (F.fmlp_convert_f16(L[0]), F.fmlp_convert_f16(L[1]))
+            layers.append(L)
             if l == 0 and not args.no_cpu_baseline:
                 host0 = (synth.bits(wg), synth.bits(wu), synth.bits(wd))
             del wg, wu, wd
         xs.append(synth.inputs(w, M, dev, layer=l))
     torch.cuda.synchronize()
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, 1 if w.wtype == "int4" else 0),
+    wt = F.FMLP_W_INT4_G32 if w.wtype == "int4" else F.FMLP_W_F16 if w16 else F.FMLP_W_BF16
+    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, wt),
                      dtype=torch.uint8, device=dev)
     res = synth.activations(M, d, 977, dev) if args.residual else None
     hout = torch.empty((M, d), dtype=torch.bfloat16, device=dev) if args.residual else None
@@ -339,7 +349,8 @@ def run_one(wname, M, steps, warmup, args):
                     "unit": unit, "frac": round(achieved / peak, 4),
                     "units_per_step": dom_units,
                     "launches_per_step": kernels[dom]["launches_per_step"],
-                    "traffic": measured_traffic(dom, wname, M)}
+                    # (the committed counter runs are of the stored weight types)
+                    "traffic": None if w16 else measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
         t = k["us_per_step"]
         if name.startswith("decode") or name in ("act_prep", "partial_reduce"):
@@ -381,10 +392,10 @@ def run_one(wname, M, steps, warmup, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4-bf16" if w.wtype == "int4" else "bf16",
+        "dtype": "int4-bf16" if w.wtype == "int4" else "f16-bf16" if w16 else "bf16",
         "data": "synthetic",
         "config": {"workload": wname, "M": M, "d": d, "ff": ff, "weight_sets": w.sets,
-                   "wtype": w.wtype, "path": path, "activation": args.activation,
+                   "wtype": "f16" if w16 else w.wtype, "path": path, "activation": args.activation,
                    "residual": bool(args.residual), "parallelism": "none (1 GPU)"},
         "step_gb_per_s": round(step_gbs, 1),
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
