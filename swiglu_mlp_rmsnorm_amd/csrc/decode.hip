@@ -152,7 +152,7 @@ static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 // groups (d/16 over the row blocks per workgroup), split each into k slices when that spreads the work more evenly over the
 // 256 CUs (time ~ rounds of workgroups / k), keeping at least min_units K
 // units per slice; at most kMaxSplit.
-constexpr int kMaxSplit = 4;
+constexpr int kMaxSplit = 8;
 static int down_splits(int64_t blocks, int64_t ff, bool int4) {
 #ifdef FMLP_DN_SPLIT
   return FMLP_DN_SPLIT;
@@ -876,13 +876,25 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
     const int rl = o % (RB * 16), t = o / (RB * 16);
     const int64_t yi = (int64_t)t * d + rb0 * 16 + rl;
     // all slices' loads in flight before the first add (one load and its
-    // wait per slice would chain their latencies): unconditional, slices past
-    // the last re-read it and are masked out; summed in slice order
+    // wait per slice would chain their latencies): unconditional within each
+    // group of four (the second group only when there are more than four
+    // slices), slices past the last re-read it and are masked out; summed in
+    // slice order
+    static_assert(kMaxSplit == 8, "two groups of four partial loads");
     float pv[kMaxSplit];
 #pragma unroll
-    for (int k = 0; k < kMaxSplit; ++k)
+    for (int k = 0; k < 4; ++k)
       pv[k] = __hip_atomic_load(part + (int64_t)(k < splits ? k : splits - 1) * M * d + yi,
                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (splits > 4) {
+#pragma unroll
+      for (int k = 4; k < 8; ++k)
+        pv[k] = __hip_atomic_load(part + (int64_t)(k < splits ? k : splits - 1) * M * d + yi,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+#pragma unroll
+      for (int k = 4; k < 8; ++k) pv[k] = 0.f;
+    }
     float sum = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxSplit; ++k) sum += k < splits ? pv[k] : 0.f;
