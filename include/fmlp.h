@@ -149,7 +149,8 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
  * other layout. A storage option: the prefill GEMMs' fp16 products then
  * read the weights as they are, with no conversion in the inner loop.
  *   w    : bf16 [n], read only.     out : fp16 [n]; must not overlap w.
- *   n    : element count, a positive multiple of 8.
+ *   n    : element count, a positive multiple of 8, at most (2^31 - 1) * 2048
+ *          (FMLP_ERR_UNSUPPORTED_SHAPE above).
  * Synchronises `stream`. Returns FMLP_ERR_RANGE if some w[i] is not finite
  * or exceeds 65504 in magnitude (out then undefined).
  */

@@ -20,6 +20,9 @@ int hip_fail(hipError_t e) {
 }
 
 constexpr int64_t kMaxD = 65536, kMaxFF = 262144, kMaxM = int64_t(1) << 24;
+// fmlp_convert_f16: 8 elements per thread, 256 threads per workgroup, and a
+// grid of at most 2^31 - 1 workgroups
+constexpr int64_t kMaxConvert = int64_t(0x7fffffff) * 2048;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -148,6 +151,7 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* sc
 
 int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream) {
   if (!w || !out || n <= 0 || n % 8 != 0) return FMLP_ERR_INVALID_ARG;
+  if (n > kMaxConvert) return FMLP_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(w) || !aligned16(out)) return FMLP_ERR_ALIGNMENT;
   if (overlap(span(w, (size_t)n * 2), span(out, (size_t)n * 2))) return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;

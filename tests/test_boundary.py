@@ -158,6 +158,7 @@ def test_convert_f16_validation():
     assert L.fmlp_convert_f16(a, None, 64, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_convert_f16(a, c, 0, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_convert_f16(a, c, 60, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_convert_f16(a, c, 0x7FFFFFFF * 2048 + 8, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
     assert L.fmlp_convert_f16(a, ctypes.c_void_p(A["y"].value + 2), 64,
                               None) == F.FMLP_ERR_ALIGNMENT
     assert L.fmlp_convert_f16(a, a, 64, None) == F.FMLP_ERR_INVALID_ARG
