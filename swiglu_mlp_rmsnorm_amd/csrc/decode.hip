@@ -110,10 +110,16 @@
 #define FMLP_BIG_DN_S 8    // and its waves (M <= 16)
 #endif
 #ifndef FMLP_BIG_DN_S2
-#define FMLP_BIG_DN_S2 16  // and its waves (M > 16)
+#define FMLP_BIG_DN_S2 8   // and its waves (M > 16; 16 measured 3-9% slower)
 #endif
 #ifndef FMLP_BIG_GU_RB2
-#define FMLP_BIG_GU_RB2 4  // bf16 gate/up row blocks per workgroup for M > 16
+#define FMLP_BIG_GU_RB2 4  // bf16 gate/up row blocks per workgroup for M > 16 ...
+#endif
+#ifndef FMLP_BIG_GU_RB2W
+#define FMLP_BIG_GU_RB2W 8 // ... or this many, where that adds no row blocks to the most
+#endif                     // any CU streams (big_gu_wide)
+#ifndef FMLP_Q4_BIG_GU_RB
+#define FMLP_Q4_BIG_GU_RB 4  // int4 gate/up row blocks per workgroup for 4 < M <= 16
 #endif
 #ifndef FMLP_MASK_ACT
 #define FMLP_MASK_ACT 0    // activation loads only in lanes that hold a token
@@ -1121,7 +1127,8 @@ static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t
   constexpr bool kStage =
       FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_GU));
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
-  // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks
+  // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks; a
+  // larger RB is launched only where launch_decode_t checked that it does
   const dim3 grid((2 * p.ff) / (16 * RB)), block(64 * S);
   auto go = [&](auto kern, uint32_t shmem) {
     launch_kernel(kind, kern, grid, block, shmem, stream, p.w_gu, p.s_gu, act0, act1, p.eps, ws.a0,
@@ -1190,9 +1197,21 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // 10 % in down; bf16 gate/up gains 3-4 % (Phi-3, Llama-8B), while bf16
   // down loses up to 14 %, so the bf16 down kernel reads its a per wave.
   auto lds_budget = [](int64_t wgs) -> int64_t { return wgs <= 256 ? 96 * 1024 : 32 * 1024; };
-  constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2;
-  const bool gu_big = big && WK != WK_INT4;
-  const int64_t gu_wgs = (2 * p.ff) / (16 * (gu_big ? BGRB : RB));
+  constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2, BGRBW = FMLP_BIG_GU_RB2W;
+  constexpr int Q4B = FMLP_Q4_BIG_GU_RB;
+  // int4 takes Q4B row blocks from M > FMLP_BIG_M up to 16 tokens (its
+  // registers hold RB at two token blocks); bf16 / fp16 at two token blocks
+  // take BGRBW instead of BGRB where that divides the row blocks and adds none
+  // to the most any CU streams (rounds of 256 workgroups times row blocks):
+  // measured 4-7% faster at Llama-8B M=17..32 (224 workgroups), while at
+  // Phi-3 (128 of them) it would double the largest share
+  const bool gu_big = big && (WK != WK_INT4 || NCB == 1);
+  const int64_t gblocks = (2 * p.ff) / 16;
+  auto most_per_cu = [gblocks](int64_t rb) { return (gblocks / rb + 255) / 256 * rb; };
+  const bool gu_wide = gu_big && WK != WK_INT4 && NCB == 2 && gblocks % BGRBW == 0 &&
+                       most_per_cu(BGRBW) <= most_per_cu(BGRB);
+  const int gu_rb = gu_wide ? BGRBW : gu_big ? (WK == WK_INT4 ? Q4B : BGRB) : RB;
+  const int64_t gu_wgs = gblocks / gu_rb;
   const int64_t gu_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * p.d;
   // (bf16 gate/up staging, when enabled, does not cover the residual prologue)
   constexpr bool kStageGu =
@@ -1205,11 +1224,17 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const bool dl = (kStage || FMLP_DEC_LDS_BF16_DN) && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
 
   const int ncnt = splits > 1 ? (int)(p.d / 16) : 0;
-  if (gu_big)
-    launch_gateup<WK, NCB, WK != WK_INT4 ? BGRB : RB>(p, ws, act0, act1, ncnt, gl, gu_lds,
-                                                      stream);
-  else
+  if (gu_wide) {
+    if constexpr (WK != WK_INT4 && NCB == 2)
+      launch_gateup<WK, NCB, BGRBW>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
+  } else if (gu_big) {
+    if constexpr (WK != WK_INT4)
+      launch_gateup<WK, NCB, BGRB>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
+    else if constexpr (NCB == 1)
+      launch_gateup<WK, NCB, Q4B>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
+  } else {
     launch_gateup<WK, NCB, RB>(p, ws, act0, act1, ncnt, gl, gu_lds, stream);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (bdrb)
     // (int4 with two token blocks keeps 8 waves: its registers do not fit 16)

@@ -83,7 +83,8 @@ def test_prefill_f16(tiny16, M, path):
 
 
 @pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 40), (512, 1376, 5),
-                                    (512, 1376, 70), (1024, 20480, 4), (3072, 256, 20)])
+                                    (512, 1376, 70), (1024, 20480, 4), (3072, 256, 20),
+                                    (64, 8256, 32)])
 def test_f16_shapes(d, ff, M):
     layer = F16Layer(d, ff, 60 + d)
     x, g = bf16_inputs(M, d, 970 + M)
