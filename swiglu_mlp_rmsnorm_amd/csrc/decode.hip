@@ -100,6 +100,9 @@
 #ifndef FMLP_BIG_M
 #define FMLP_BIG_M 4       // above this M, the activation loads of each K unit are
 #endif                     // shared by more weight rows (the settings below)
+#ifndef FMLP_BIG_DN_M
+#define FMLP_BIG_DN_M 1    // the down kernel's large-M settings from this M on (exclusive)
+#endif
 #ifndef FMLP_BIG_GU_RB
 #define FMLP_BIG_GU_RB 4   // bf16 gate/up row blocks per workgroup for M > FMLP_BIG_M
 #endif
@@ -1184,10 +1187,13 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // takes FMLP_BIG_GU_RB row blocks per workgroup, and the down projection
   // FMLP_BIG_DN_RB, split along K to keep enough workgroups.
   const bool big = p.M > FMLP_BIG_M;
-  // down: DRB row blocks per workgroup when they divide d and leave enough
-  // workgroups to cover the CUs; else one, split along K when that helps
+  // down: BDRB row blocks per workgroup, split along K, from M > FMLP_BIG_DN_M
+  // (two tokens on: measured 4-10% faster down kernels at M = 2..4 on the
+  // Phi-3, Llama-8B and 70B int4 shapes); otherwise DRB row blocks per
+  // workgroup when they divide d and leave enough workgroups to cover the
+  // CUs; else one, split along K when that helps
   constexpr int BDRB = FMLP_BIG_DN_RB;
-  const bool bdrb = big && p.d % (16 * BDRB) == 0;
+  const bool bdrb = p.M > FMLP_BIG_DN_M && p.d % (16 * BDRB) == 0;
   const bool drb = !bdrb && DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
   const int dn_rb = bdrb ? BDRB : drb ? DRB : 1;
   const int splits = drb ? 1 : down_splits(p.d / (16 * dn_rb), p.ff, WK == WK_INT4);
@@ -1205,8 +1211,12 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // to the most any CU streams (rounds of 256 workgroups times row blocks):
   // measured 4-7% faster at Llama-8B M=17..32 (224 workgroups), while at
   // Phi-3 (128 of them) it would double the largest share
-  const bool gu_big = big && (WK != WK_INT4 || NCB == 1);
+  // bf16 / fp16 also take BGRB from two tokens on where that still leaves
+  // more than one round of workgroups (Llama-8B: 448; measured 3-20% faster
+  // at M = 2..4, while at Phi-3's 256 it is slower)
   const int64_t gblocks = (2 * p.ff) / 16;
+  const bool gu_big = WK == WK_INT4 ? big && NCB == 1
+                                    : big || (p.M > 1 && gblocks / BGRB > 256);
   auto most_per_cu = [gblocks](int64_t rb) { return (gblocks / rb + 255) / 256 * rb; };
   const bool gu_wide = gu_big && WK != WK_INT4 && NCB == 2 && gblocks % BGRBW == 0 &&
                        most_per_cu(BGRBW) <= most_per_cu(BGRB);

@@ -137,7 +137,10 @@ def test_both_paths_at_the_crossover(tiny, M, path):
                                     (4096, 1024, 3),
                                     # 2ff/16 = 1032 row blocks: the eight-block gate/up
                                     # workgroups at two token blocks (M > 16)
-                                    (64, 8256, 17), (64, 8256, 32), (64, 8256, 9)])
+                                    (64, 8256, 17), (64, 8256, 32), (64, 8256, 9),
+                                    # more than 256 four-block gate/up workgroups: the
+                                    # large-M gate/up settings from two tokens on
+                                    (64, 8256, 2), (64, 8256, 4)])
 def test_odd_shapes(d, ff, M):
     layer = Bf16Layer(d, ff, 20 + d)
     x, g = bf16_inputs(M, d, 400 + M)
