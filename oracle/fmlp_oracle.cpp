@@ -12,7 +12,7 @@
 //   same page: RMSNorm -> interleaved gate-up matmul -> SiLU*mul -> down
 //   projection (Figure 4: part1 RMSNorm, part2 interleaved gate/up fusion,
 //   part3 down projection). So h = RMSNorm(x).
-//   Readings where the pages are silent (all listed in the design doc):
+//   Readings where the pages are silent:
 //     RMSNorm(x)_k = gamma_k * x_k / sqrt(mean_k(x^2) + eps)   (no mean
 //       subtraction, no bias, gamma is a plain multiplier);
 //     SiLU(t) = t / (1 + exp(-t))  (Swish with beta = 1; SwiGLU);
@@ -24,7 +24,7 @@
 //       q = clamp(round_half_even(fp32(w / s)), -8, 7), q = 0 when s == 0,
 //       two's-complement nibbles, even k in the low nibble.
 //
-//   Variants beyond Eq(1) (also readings, listed in the design doc):
+//   Variants beyond Eq(1) (also readings):
 //     activation of the gate branch: SiLU (Eq(1)), or GELU, the activation the
 //       Together AI fusion post (blog.hotdry.top) names for its fused MLP;
 //       the pages give no GELU formula, so both usual forms are offered:

@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where there is no GPU, so the CPU
-    # suite stays green; on a GPU machine they run and must pass.
+    # suite stays green; on a machine with an MI355X they run and must pass.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
