@@ -6,9 +6,12 @@ SiLU*mul -> down projection) on one layer, the weight set rotating every
 step through `sets` distinct layers so the 256 MB Infinity Cache cannot serve
 repeats. Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line (stdout). Default workload: Phi-3-mini-shaped decode,
-d=3072, ff=8192, M=1, 32 weight sets. `--workload`/`--M` select another
-configuration; `--all` prints one line per (workload, M).
+Prints ONE JSON line (stdout). Default: the Llama-3.1-8B-shaped prefill,
+d=4096, ff=14336, M=2048 tokens (the MFMA half of the metric), with the
+three decode M=1 workloads (Phi-3-mini-, Llama-3.1-8B- and 70B-int4-shaped;
+the HBM half) measured in the same run and reported inside the same line
+under "decode_m1". `--workload`/`--M` select one configuration alone;
+`--all` prints one line per (workload, M).
 """
 from __future__ import annotations
 
@@ -27,7 +30,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused-MLP tokens/s + % HBM roofline (decode M=1) / % MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
-DEFAULT_WORKLOAD = "phi3mini_decode_d3072_ff8192"
+DEFAULT_WORKLOAD = "llama8b_prefill_d4096_ff14336"
+DEFAULT_M = 2048
+DECODE_M1 = ("phi3mini_decode_d3072_ff8192", "llama8b_decode_d4096_ff14336",
+             "llama70b_int4_decode_d8192_ff28672")
 
 
 def log(*a):
@@ -39,11 +45,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help=f"one workload alone (default: {DEFAULT_WORKLOAD} M={DEFAULT_M} with the "
+                         "decode M=1 lines)")
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--all", action="store_true", help="every (workload, M); one line each")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="wall-clock budget of the CPU-oracle baseline sample")
+                    help="wall-clock budget of the CPU-oracle baseline sample (all threads; the "
+                         "one-thread figure takes a third of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
     ap.add_argument("--no-spread", action="store_true",
@@ -169,37 +178,52 @@ def measured_traffic(kernel, workload, M):
 # ----------------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
-    """Time the fp64 CPU oracle on a bounded sample of the same workload
-    (weight set 0; the seeded row-major weights, or for int4 the seeded tiled
-    buffers expanded by the oracle's own layout code)."""
+    """Time the fp64 CPU oracle, as it stands, on a bounded sample of the same
+    workload (weight set 0, the same seeded row-major weights and inputs):
+    rows are independent, so it runs calls on consecutive row subsets until
+    the budget is spent, first with every OpenMP thread, then with one."""
     from oracle import oracle
     x, g = host_inputs
     if w.wtype == "int4":
-        q_gu, s_gu, q_d, s_d = host_layer
-        host_layer = (*oracle.untile_int4(q_gu, s_gu, 2 * w.ff, w.d),
-                      *oracle.untile_int4(q_d, s_d, w.d, w.ff))
-    # rows are independent: for large M, run row subsets until the budget is spent
-    rows_per_call = M if M <= 32 else 1
-    done_rows, calls = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        r0 = (calls * rows_per_call) % M
-        xs = x[r0:r0 + rows_per_call]
-        if w.wtype == "int4":
-            q_gu, s_gu, q_d, s_d = host_layer
-            oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, q_d, s_d)
-        else:
-            wg, wu, wd = host_layer
+        qg, sg, qu, su, qd, sd = host_layer
+        q_gu, s_gu = oracle.pack_interleaved_int4(qg, sg, qu, su)
+
+        def call(xs):
+            oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, qd, sd)
+    else:
+        wg, wu, wd = host_layer
+
+        def call(xs):
             oracle.forward_unfused(xs, g, w_eps(), wg, wu, wd)
-        done_rows += xs.shape[0]
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+
+    def timed(rows_per_call, budget):
+        done, calls = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            r0 = (calls * rows_per_call) % M
+            xs = x[r0:r0 + rows_per_call]
+            call(xs)
+            done += xs.shape[0]
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done, calls, el
+
+    threads = oracle.threads()
+    rows_per_call = min(M, 16)
+    done, calls, el = timed(rows_per_call, budget_s)
+    oracle.set_threads(1)
+    try:
+        done1, calls1, el1 = timed(1, budget_s / 3)
+    finally:
+        oracle.set_threads(threads)
     return {
-        "value": done_rows / el, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-        "sample": (f"{calls} oracle forward call(s) of {rows_per_call} row(s) on weight set 0 of "
-                   f"{w.name} (fp64, {el:.1f} s)"),
+        "value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "nproc": os.cpu_count(), "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+        "value_1core": done1 / el1,
+        "sample": (f"{calls} oracle forward call(s) of {rows_per_call} row(s) of the {M}-token "
+                   f"input on weight set 0 of {w.name} (fp64, {threads} threads, {el:.1f} s); "
+                   f"then {calls1} call(s) of 1 row on 1 thread ({el1:.1f} s)"),
     }
 
 
@@ -210,7 +234,36 @@ def w_eps():
 
 # ----------------------------------------------------------------------------- run
 
-def run_one(wname, M, steps, warmup, args):
+def build_layers(w, dev, w16, keep_host):
+    """The rotated weight sets, packed by the library; with keep_host, also
+    the host bits of set 0's row-major tensors (for the CPU baseline)."""
+    from swiglu_mlp_rmsnorm_amd import fmlp as F
+    from swiglu_mlp_rmsnorm_amd import synth
+    layers, host0 = [], None
+    for l in range(w.sets):
+        if w.wtype == "int4":
+            qg, sg, qu, su, qd, sd = synth.layer_int4(w, l, dev)
+            layers.append((*F.fmlp_pack_int4_interleaved(qg, sg, qu, su),
+                           *F.fmlp_pack_int4_matrix(qd, sd)))
+            if l == 0 and keep_host:
+                host0 = tuple(synth.bits(t) for t in (qg, sg, qu, su, qd, sd))
+            del qg, sg, qu, su, qd, sd
+        else:
+            wg, wu, wd = synth.layer_bf16(w, l, dev)
+            L = (F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
+            if w16:  # (2 bytes per weight either way)
+                L = (F.fmlp_convert_f16(L[0]), F.fmlp_convert_f16(L[1]))
+            layers.append(L)
+            if l == 0 and keep_host:
+                host0 = (synth.bits(wg), synth.bits(wu), synth.bits(wd))
+            del wg, wu, wd
+    return layers, host0
+
+
+def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True, live_profile=False):
+    """Measure one (workload, M). live_profile: the per-kernel HIP events are
+    recorded in the timed region itself (the kernels' own start/stop stamps
+    on their launch stream); otherwise in a second, untimed pass."""
     import torch
     from swiglu_mlp_rmsnorm_amd import fmlp as F
     from swiglu_mlp_rmsnorm_amd import synth
@@ -224,51 +277,48 @@ def run_one(wname, M, steps, warmup, args):
     path = args.path if args.path != "auto" else ("decode" if M <= 32 else "prefill")
     pcode = None if args.path == "auto" else PATHS[args.path]  # None: fmlp_forward itself
     ex = args.activation != "silu" or args.residual  # the variants run fmlp_forward_ex
+    cpu = cpu and not args.no_cpu_baseline and not ex  # the baseline times the plain Eq(1) step
     log(f"[bench] {wname} M={M}: building {w.sets} weight set(s)")
-    layers, xs = [], []
-    host0 = None  # row-major / untiled copies of set 0 for the CPU baseline
-    for l in range(w.sets):
-        if w.wtype == "int4":
-            layers.append(synth.layer_int4(w, l, dev))
-            if l == 0 and not args.no_cpu_baseline:
-                host0 = tuple(synth.bits(t) for t in layers[0])
-        else:
-            wg, wu, wd = synth.layer_bf16(w, l, dev)
-            L = (F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
-            if w16:  # (2 bytes per weight either way)
-                L = (F.fmlp_convert_f16(L[0]), F.fmlp_convert_f16(L[1]))
-            layers.append(L)
-            if l == 0 and not args.no_cpu_baseline:
-                host0 = (synth.bits(wg), synth.bits(wu), synth.bits(wd))
-            del wg, wu, wd
-        xs.append(synth.inputs(w, M, dev, layer=l))
+    layers, host0 = build_layers(w, dev, w16, cpu)
+    xs = [synth.inputs(w, M, dev, layer=l) for l in range(w.sets)]
     torch.cuda.synchronize()
     y = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
     wt = F.FMLP_W_INT4_G32 if w.wtype == "int4" else F.FMLP_W_F16 if w16 else F.FMLP_W_BF16
-    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, wt),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, wt), dtype=torch.uint8, device=dev)
     res = synth.activations(M, d, 977, dev) if args.residual else None
     hout = torch.empty((M, d), dtype=torch.bfloat16, device=dev) if args.residual else None
+    if ex:
+        fwd = functools.partial(F.fmlp_forward_ex, path=pcode or 0,
+                                activation=ACTS[args.activation], residual=res, h_out=hout)
+    elif pcode is None:
+        fwd = F.fmlp_forward
+    else:
+        fwd = functools.partial(F.fmlp_forward_path, path=pcode)
 
     def step(i):
         L = layers[i % w.sets]
         x, g = xs[i % w.sets]
-        if ex:
-            fwd = functools.partial(F.fmlp_forward_ex, path=pcode or 0,
-                                    activation=ACTS[args.activation], residual=res, h_out=hout)
-        elif pcode is None:
-            fwd = F.fmlp_forward
-        else:
-            fwd = functools.partial(F.fmlp_forward_path, path=pcode)
         if w.wtype == "int4":
             fwd(x, g, synth.EPS, L[0], L[2], L[1], L[3], y=y, workspace=ws, ff=ff)
         else:
             fwd(x, g, synth.EPS, L[0], L[1], y=y, workspace=ws)
 
+    def collect_kernels(nsteps):
+        out = {}
+        for name, (n, ms) in F.fmlp_profile_read().items():
+            # a kernel kind may launch more than once per step (the gate/up
+            # GEMM's tail launch): rates below use its time per step
+            out[name] = {"launches": n, "avg_us": ms * 1e3 / n,
+                         "launches_per_step": n / nsteps, "us_per_step": ms * 1e3 / nsteps}
+        return out
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {warmup} done; timing {steps} steps")
+    live = live_profile and not args.no_profile
+    if live:
+        F.fmlp_profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -278,6 +328,10 @@ def run_one(wname, M, steps, warmup, args):
     e1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    kernels = {}
+    if live:
+        kernels = collect_kernels(steps)
+        F.fmlp_profile_enable(False)
     ms_per_step = e0.elapsed_time(e1) / steps
     wall_ms_per_step = (t1 - t0) * 1e3 / steps
     tokens_per_s = M / (ms_per_step * 1e-3)
@@ -289,8 +343,8 @@ def run_one(wname, M, steps, warmup, args):
     # (median, p10, p90 of their us/step); and the same steps captured once as
     # a HIP graph (one rotation of weight sets) and replayed, which shows what
     # host launch overhead the plain loop carries.
-    spread = None
-    if not args.no_spread:
+    spr = None
+    if spread and not args.no_spread:
         win = []
         for r in range(5):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -301,26 +355,22 @@ def run_one(wname, M, steps, warmup, args):
             torch.cuda.synchronize()
             win.append(a.elapsed_time(b) * 1e3 / steps)
         win.sort()
-        spread = {"windows": 5, "steps_per_window": steps,
-                  "us_per_step_p10": round(win[0] + 0.4 * (win[1] - win[0]), 3),
-                  "us_per_step_median": round(win[2], 3),
-                  "us_per_step_p90": round(win[3] + 0.6 * (win[4] - win[3]), 3)}
-        spread["graph_us_per_step"] = graph_us_per_step(step, w.sets, steps)
-        log(f"[bench] spread {json.dumps(spread)}")
+        spr = {"windows": 5, "steps_per_window": steps,
+               "us_per_step_p10": round(win[0] + 0.4 * (win[1] - win[0]), 3),
+               "us_per_step_median": round(win[2], 3),
+               "us_per_step_p90": round(win[3] + 0.6 * (win[4] - win[3]), 3)}
+        spr["graph_us_per_step"] = graph_us_per_step(step, w.sets, steps)
+        log(f"[bench] spread {json.dumps(spr)}")
 
     # per-kernel durations from HIP events recorded by the library on its launch stream
-    kernels = {}
-    if not args.no_profile:
+    if not live and not args.no_profile:
         F.fmlp_profile_enable(True)
         for i in range(steps):
             step(i)
         torch.cuda.synchronize()
-        for name, (n, ms) in F.fmlp_profile_read().items():
-            # a kernel kind may launch more than once per step (the gate/up
-            # GEMM's tail launch): rates below use its time per step
-            kernels[name] = {"launches": n, "avg_us": ms * 1e3 / n,
-                             "launches_per_step": n / steps, "us_per_step": ms * 1e3 / steps}
+        kernels = collect_kernels(steps)
         F.fmlp_profile_enable(False)
+    if kernels:
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
     if "decode_fused_bf16" in kernels:
@@ -339,8 +389,10 @@ def run_one(wname, M, steps, warmup, args):
         dom = "gemm_gateup_silu_f16"
         dom_units = 2.0 * M * (2 * ff) * d
         unit, peak, bound = "TFLOP/s", MFMA_PEAK_TFLOPS, "mfma"
-    # the dominant kernel's algorithmic units and time per step (its launches
-    # in one step together: one for decode, one or two for the gate/up GEMM)
+    # The dominant kernel's algorithmic units per step over its time per step
+    # (its launches in one step together: one for decode, one or two for the
+    # gate/up GEMM), i.e. units per launch over the average launch duration
+    # when it launches once per step.
     roofline = None
     if dom in kernels:
         step_s = kernels[dom]["us_per_step"] * 1e-6
@@ -349,6 +401,8 @@ def run_one(wname, M, steps, warmup, args):
                     "unit": unit, "frac": round(achieved / peak, 4),
                     "units_per_step": dom_units,
                     "launches_per_step": kernels[dom]["launches_per_step"],
+                    "us_per_step": round(kernels[dom]["us_per_step"], 3),
+                    "events": "timed region" if live else "separate untimed pass",
                     # (the committed counter runs are of the stored weight types)
                     "traffic": None if w16 else measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
@@ -364,23 +418,36 @@ def run_one(wname, M, steps, warmup, args):
 
     # The HBM read rate a plain streaming kernel reaches on exactly the bytes
     # the dominant decode kernel streams (the gate/up weights of each rotated
-    # set, read once per launch): the practical ceiling its roofline fraction
-    # should be read against.
+    # set, read once per launch), and on the whole step's weight bytes (both
+    # matrices of each set read back to back): the practical ceilings the
+    # roofline fractions should be read against.
     ceiling = None
     if path == "decode" and not args.no_profile:
         ceiling = read_ceiling([L[0] for L in layers], steps)
+        whole = read_ceiling_step(layers, w.wtype, steps)
+        if ceiling is not None:
+            ceiling["step_weights"] = whole
         if roofline is not None and ceiling:
             ceiling["dominant_kernel_frac_of_ceiling"] = round(
                 roofline["achieved"] / ceiling["gb_per_s"], 4)
 
-    cpu = None
-    if not args.no_cpu_baseline and not ex:  # the oracle baseline times the plain Eq(1) step
+    cpu_rec = None
+    if cpu:
         host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
         log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
-        cpu = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds)
+        cpu_rec = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds)
 
     step_gbs = sb / (ms_per_step * 1e-3) / 1e9
     step_tflops = step_flops(M, d, ff) / (ms_per_step * 1e-3) / 1e12
+    # the whole step against the roofline of its bound (what the metric names)
+    if bound == "mfma":
+        step_roof = {"bound": "mfma", "achieved": round(step_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(step_tflops / MFMA_PEAK_TFLOPS, 4)}
+    else:
+        step_roof = {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(step_gbs / HBM_PEAK_GBS, 4)}
+    dtype = ("int4-f16" if w.wtype == "int4" else
+             "f16" if (w16 or path == "prefill" or "act_prep" in kernels) else "bf16")
     rec = {
         "metric": METRIC,
         "value": round(tokens_per_s, 2),
@@ -392,21 +459,25 @@ def run_one(wname, M, steps, warmup, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4-bf16" if w.wtype == "int4" else "f16-bf16" if w16 else "bf16",
+        "dtype": dtype,
+        "dtype_detail": ("MFMA operands: " + {
+            "bf16": "bf16 weights x bf16 hi+lo activations",
+            "f16": "fp16 (bf16 weights converted exactly in registers)",
+            "int4-f16": "fp16 from int4 codes and fp16 group scales"}[dtype]
+            + "; fp32 accumulation; bf16 x, gamma and y"),
         "data": "synthetic",
         "config": {"workload": wname, "M": M, "d": d, "ff": ff, "weight_sets": w.sets,
                    "wtype": "f16" if w16 else w.wtype, "path": path, "activation": args.activation,
                    "residual": bool(args.residual), "parallelism": "none (1 GPU)"},
         "step_gb_per_s": round(step_gbs, 1),
-        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_tflop_per_s": round(step_tflops, 2),
-        "step_mfma_frac": round(step_tflops / MFMA_PEAK_TFLOPS, 4),
+        "step_roofline": step_roof,
         "host_wall_ms_per_step": round(wall_ms_per_step, 6),
         "roofline": roofline,
         "read_ceiling": ceiling,
-        "spread": spread,
+        "spread": spr,
         "kernels": kernels,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_rec,
     }
     del layers, xs
     torch.cuda.empty_cache()
@@ -445,10 +516,38 @@ def graph_us_per_step(step, period, steps):
     return round(us, 3)
 
 
+def _probe(buffers, steps, wgs_list):
+    """fmlp_read_probe over each buffer list entry in turn (each entry a list
+    of tensors read back to back), best rate over the grid sizes."""
+    import torch
+    from swiglu_mlp_rmsnorm_amd import fmlp as F
+    nbytes = sum(t.numel() * t.element_size() for t in buffers[0])
+    best = None
+    sink = torch.empty(4096 * 256, dtype=torch.int32, device=buffers[0][0].device)
+    for wgs in wgs_list:
+        for i in range(2 * len(buffers)):
+            for t in buffers[i % len(buffers)]:
+                F.fmlp_read_probe(t, sink, wgs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            for t in buffers[i % len(buffers)]:
+                F.fmlp_read_probe(t, sink, wgs)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbs > best["gb_per_s"]:
+            best = {"bytes_per_step": nbytes, "launches_per_step": len(buffers[0]),
+                    "workgroups": wgs, "us_per_step": round(us, 3), "gb_per_s": round(gbs, 1)}
+    return best
+
+
 def read_ceiling(buffers, steps):
-    """Streaming-read probe (fmlp_read_probe) over the rotated weight buffers,
-    timed with the library's dispatch-stamped events; the best of three grid
-    sizes."""
+    """Streaming-read probe (fmlp_read_probe) over the rotated gate/up weight
+    buffers, timed with the library's dispatch-stamped events; the best of
+    three grid sizes."""
     import torch
     from swiglu_mlp_rmsnorm_amd import fmlp as F
     nbytes = buffers[0].numel() * buffers[0].element_size()
@@ -472,6 +571,15 @@ def read_ceiling(buffers, steps):
     return best
 
 
+def read_ceiling_step(layers, wtype, steps):
+    """The same probe over a whole step's weight bytes: each rotated set's
+    W_gu and W_down (and int4 scales) read back to back, as one step's two
+    launches read them, timed over the whole sequence with stream events (so
+    the gaps between the launches count, as they do in a step)."""
+    bufs = [list(L) for L in layers]  # bf16: (w_gu, w_down); int4: codes and scales
+    return _probe(bufs, steps, (1024, 2048))
+
+
 def default_steps(w, M):
     # ~1 s of timed GPU work per line, a whole number of rotations
     if M > 32:
@@ -493,6 +601,15 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
 
 
+def decode_summary(rec):
+    """The fields of a decode M=1 record that the default line nests."""
+    keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "step_gb_per_s",
+            "step_roofline", "roofline", "read_ceiling", "spread", "kernels")
+    out = {k: rec[k] for k in keep}
+    out["config"] = rec["config"]
+    return out
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -507,21 +624,35 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     from swiglu_mlp_rmsnorm_amd import synth
-    jobs = []
+
+    def steps_for(wname, M):
+        s, wu = default_steps(synth.WORKLOADS[wname], M)
+        return (args.steps if args.steps is not None else s,
+                args.warmup if args.warmup is not None else wu)
+
     if args.all:
         for wname, w in synth.WORKLOADS.items():
             for M in w.Ms:
-                jobs.append((wname, M))
-    else:
+                st, wu = steps_for(wname, M)
+                print(json.dumps(run_one(wname, M, st, wu, args, live_profile=M > 32)), flush=True)
+        return
+    if args.workload is not None:
         w = synth.WORKLOADS[args.workload]
-        jobs.append((args.workload, args.M if args.M is not None else w.Ms[0]))
-    for wname, M in jobs:
-        w = synth.WORKLOADS[wname]
-        s, wu = default_steps(w, M)
-        steps = args.steps if args.steps is not None else s
-        warmup = args.warmup if args.warmup is not None else wu
-        rec = run_one(wname, M, steps, warmup, args)
-        print(json.dumps(rec), flush=True)
+        M = args.M if args.M is not None else w.Ms[0]
+        st, wu = steps_for(args.workload, M)
+        print(json.dumps(run_one(args.workload, M, st, wu, args, live_profile=M > 32)), flush=True)
+        return
+    # default: the prefill headline, then the decode M=1 workloads (their own
+    # default step counts: whole rotations of their weight sets), one line
+    M = args.M if args.M is not None else DEFAULT_M
+    st, wu = steps_for(DEFAULT_WORKLOAD, M)
+    rec = run_one(DEFAULT_WORKLOAD, M, st, wu, args, live_profile=True)
+    dec = {}
+    for wname in DECODE_M1:
+        s, wu2 = default_steps(synth.WORKLOADS[wname], 1)
+        dec[wname] = decode_summary(run_one(wname, 1, s, wu2, args, cpu=False))
+    rec["decode_m1"] = dec
+    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

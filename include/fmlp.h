@@ -118,24 +118,65 @@ int fmlp_pack_interleaved(const void* w_gate, const void* w_up, void* w_gu,
 int fmlp_pack_matrix(const void* w, void* w_tiled, int64_t rows, int64_t K,
                      void* stream);
 
+/*
+ * int4 exchange format (row-major, what a caller holds or receives from
+ * fmlp_quantize_int4): for a logical matrix [rows, K], K % 32 == 0,
+ *   q      : uint8 [rows, K/2]; column k is nibble k%2 of byte k/2 (even k
+ *            in the low nibble, odd k in the high one), two's complement,
+ *            values -8..7;
+ *   scales : fp16 [rows, K/32]; scale (r, g) applies to columns 32g..32g+31
+ *            of row r, so w[r, k] = scales[r, k/32] * q[r, k].
+ * The pages only name Q4_K / Q4_K_M (llama.cpp PR digest, blog.cecily.jp);
+ * this is the plainest symmetric group format. fmlp_forward reads int4 in
+ * the tiled layout above, written from this format by fmlp_pack_int4_*.
+ */
+
 /* Byte sizes of the tiled int4 code and scale buffers of a [rows, K] matrix. */
 int fmlp_int4_sizes(int64_t rows, int64_t K, size_t* code_bytes,
                     size_t* scale_bytes);
 
 /*
- * Quantise a tiled bf16 matrix (logical [rows, K]) to tiled int4 with one
- * fp16 scale per group of 32 consecutive elements of a row (the pages only
- * name Q4_K / Q4_K_M in the llama.cpp PR digest; this is the plainest
- * symmetric group format):
+ * Quantise a bf16 row-major matrix [rows, K] to the int4 exchange format,
+ * one fp16 scale per group of 32 consecutive elements of a row:
  *   s = fp16_rne( fp32(max_group |w|) / 7 )      (IEEE fp32 division)
  *   q = clamp( round_half_even( fp32(w) / fp32(s) ), -8, 7 ),  q = 0 if s == 0
+ *   w      : bf16 [rows, K] row-major, read only.
+ *   q      : uint8 [rows, K/2], scales : fp16 [rows, K/32] (exchange format).
+ *   rows >= 1 (no row blocking), K % 32 == 0; buffers must not overlap.
  * Synchronises `stream`. Returns FMLP_ERR_RANGE if some group holds a
  * non-finite weight or its scale overflows fp16 (outputs then undefined).
- * Groups never cross rows, so quantising the interleaved gate/up matrix
+ * Groups never cross rows, so quantising the row-interleaved gate/up matrix
  * equals interleaving the quantised gate and up matrices.
  */
 int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
                        void* scales, void* stream);
+
+/*
+ * Interleave quantised gate and up weights into one matrix and store it in
+ * the tiled int4 layout (the int4 counterpart of fmlp_pack_interleaved:
+ * FastTPS review section 3 item 3, one matmul over interleaved gate/up rows;
+ * llama.cpp PR digest, gate and up rows alternate).
+ *   q_gate, q_up : uint8 [ff, d/2];  s_gate, s_up : fp16 [ff, d/32]
+ *                  (exchange format), read only.
+ *   q_gu, s_gu   : tiled codes and scales of the logical [2ff, d] matrix
+ *                  whose row 2i is gate row i and row 2i+1 is up row i;
+ *                  sizes from fmlp_int4_sizes(2ff, d). Bit copies.
+ * d, ff as for fmlp_forward. Outputs must not overlap any input or each
+ * other (FMLP_ERR_INVALID_ARG). Asynchronous.
+ */
+int fmlp_pack_int4_interleaved(const void* q_gate, const void* s_gate,
+                               const void* q_up, const void* s_up, int64_t ff,
+                               int64_t d, void* q_gu, void* s_gu, void* stream);
+
+/*
+ * Store an int4 matrix given in the exchange format [rows, K] (used for
+ * W_down [d, ff]) in the tiled int4 layout. rows % 16 == 0, K % 32 == 0;
+ * q_tiled / s_tiled sized by fmlp_int4_sizes(rows, K), not overlapping the
+ * inputs or each other. Asynchronous.
+ */
+int fmlp_pack_int4_matrix(const void* q, const void* scales, int64_t rows,
+                          int64_t K, void* q_tiled, void* s_tiled,
+                          void* stream);
 
 /*
  * Convert bf16 weights to fp16 for the FMLP_W_F16 weight type: element i of
@@ -157,18 +198,20 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q,
 int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream);
 
 /*
- * Expand tiled int4 to row-major fp32 [rows, K]: out[r,k] = float(s[r,k/32])
- * * q[r,k], exact in fp32. A test hook for the in-register expansion the
- * int4 forward kernels perform; not used by fmlp_forward.
+ * Expand int4 in the exchange format to row-major fp32 [rows, K]:
+ * out[r,k] = float(scales[r,k/32]) * q[r,k], exact in fp32. A test hook for
+ * the expansion the int4 forward kernels perform in registers; not used by
+ * fmlp_forward. rows >= 1, K % 32 == 0; out must not overlap the inputs.
  */
 int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows,
                       int64_t K, float* out, void* stream);
 
 /*
  * Bytes of scratch fmlp_forward needs for this problem (for any path it may
- * take), or 0 when the shape is unsupported. Depends only on the arguments,
- * and never decreases as M grows with d, ff and wtype fixed, so a buffer
- * sized for the largest M serves every smaller one.
+ * take, fmlp_forward_path's forced ones included), or 0 when the shape is
+ * unsupported. Depends only on the arguments, and never decreases as M grows
+ * with d, ff and wtype fixed, so a buffer sized for the largest M serves
+ * every smaller one.
  */
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
 
@@ -181,7 +224,9 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *                             w_down tiled bf16 [d, ff] (fmlp_pack_matrix);
  *                             gu_scales and down_scales ignored (may be NULL)
  *                FMLP_W_INT4_G32: tiled int4 codes + scales of the same two
- *                             logical matrices (fmlp_quantize_int4). Decode
+ *                             logical matrices (fmlp_quantize_int4, then
+ *                             fmlp_pack_int4_interleaved for W_gu and
+ *                             fmlp_pack_int4_matrix for W_down). Decode
  *                             (M <= 32) dequantises in registers, exactly;
  *                             prefill first expands both matrices to fp16
  *                             tiles in the workspace (s*q rounded once to
@@ -197,10 +242,13 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *                bytes; contents on entry are ignored, on exit undefined.
  *   M == 0 is a no-op returning FMLP_OK (x and y may then be NULL).
  * Accumulation is fp32. The normalised input and the SiLU*mul intermediate
- * are kept as bf16 hi + lo pairs (about 2^-17 relative) on the bf16 decode
- * path up to 16 tokens, and as fp16 on every other path (|values| must stay
- * below 65504 there; the prefill path also converts bf16 weights, or s*q,
- * to fp16 the way fmlp_convert_f16 does, so the same bound holds for them).
+ * are kept as bf16 hi + lo pairs (about 2^-17 relative, the range of fp32)
+ * on the bf16 decode path up to 16 tokens, and as fp16 on every other path
+ * (the prefill path also converts bf16 weights, or s*q, to fp16 the way
+ * fmlp_convert_f16 does). On those paths an intermediate beyond +-65504
+ * becomes +-inf, so that row of y comes out non-finite (inf or NaN), never
+ * a finite wrong value; magnitudes below 2^-14 lose relative precision
+ * gradually (fp16 subnormals).
  * Not bitwise identical across paths; deterministic for a given path and
  * shape. Concurrent calls must not share a workspace.
  */

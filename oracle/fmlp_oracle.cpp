@@ -378,17 +378,28 @@ int64_t oracle_bf16_to_f16_trunc(const uint16_t* w, int64_t n, uint16_t* out) {
 
 // Weight access: one callback-free struct per storage kind keeps the three
 // forward variants on the same arithmetic.
+// Every binary16 pattern's value, decoded once by f16_value (a cache of that
+// function: the forward reads the same doubles it would compute).
+static const double* f16_table() {
+  static double* t = [] {
+    double* v = new double[65536];
+    for (uint32_t h = 0; h < 65536; ++h) v[h] = f16_value((uint16_t)h);
+    return v;
+  }();
+  return t;
+}
+
 struct WeightView {
   int kind;                 // 0 bf16, 1 int4 group-32, 2 fp16
   const uint16_t* bf;       // bf16 (kind 0) or fp16 (kind 2) [rows, K]
   const uint8_t* q;         // int4 [rows, K/2]
   const uint16_t* s;        // fp16 [rows, K/32]
   int64_t K;
+  const double* f16 = f16_table();
   double at(int64_t row, int64_t k) const {
     if (kind == 0) return bf16_value(bf[row * K + k]);
-    if (kind == 2) return f16_value(bf[row * K + k]);
-    return f16_value(s[row * (K / 32) + k / 32]) *
-           (double)int4_at(q + row * (K / 2), k);
+    if (kind == 2) return f16[bf[row * K + k]];
+    return f16[s[row * (K / 32) + k / 32]] * (double)int4_at(q + row * (K / 2), k);
   }
 };
 
@@ -501,6 +512,15 @@ int oracle_omp_threads(void) {
   return omp_get_max_threads();
 #else
   return 1;
+#endif
+}
+
+// Set that thread count (results do not depend on it).
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
 #endif
 }
 

@@ -72,6 +72,7 @@ def _load():
             "oracle_forward_bf16": (None, [P, P, D, P, P, I64, I64, I64, P]),
             "oracle_forward_int4": (None, [P, P, D, P, P, P, P, I64, I64, I64, P]),
             "oracle_omp_threads": (ctypes.c_int, []),
+            "oracle_set_threads": (None, [ctypes.c_int]),
             "oracle_bf16_to_f16_trunc": (I64, [P, I64, P]),
             "oracle_forward_f16_ex": (None, [P, P, P, P, D, ctypes.c_int, P, P, I64, I64, I64,
                                              P]),
@@ -103,6 +104,11 @@ def _p(a: np.ndarray):
 
 def threads() -> int:
     return _load().oracle_omp_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the OpenMP loops from now on (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def bf16_to_double(b: int) -> float:
@@ -174,6 +180,16 @@ def pack_interleaved(w_gate: np.ndarray, w_up: np.ndarray) -> np.ndarray:
     out = np.empty((2 * ff, d), np.uint16)
     _load().oracle_pack_interleaved(_p(w_gate), _p(w_up), _p(out), ff, d)
     return out
+
+
+def pack_interleaved_int4(q_gate, s_gate, q_up, s_up):
+    """Row interleave of int4 matrices in the exchange format (codes uint8
+    [ff, d/2], scales fp16 bits [ff, d/32]): gate row i -> row 2i, up row i
+    -> row 2i+1. The packer above moves each row's raw bytes (codes viewed
+    as 16-bit pairs; d/2 is even)."""
+    qg, qu = _c(q_gate, np.uint8), _c(q_up, np.uint8)
+    q = pack_interleaved(qg.view(np.uint16), qu.view(np.uint16)).view(np.uint8)
+    return q, pack_interleaved(_c(s_gate, np.uint16), _c(s_up, np.uint16))
 
 
 def quantize_int4(w: np.ndarray):

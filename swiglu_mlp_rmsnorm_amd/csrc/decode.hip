@@ -48,104 +48,40 @@
 #include "launch.hpp"
 #include "profile.hpp"
 
-// Tuning (compile-time; defaults chosen by measurement on MI355X).
-#ifndef FMLP_GU_RB
-#define FMLP_GU_RB 2  // 16-row blocks per gate/up workgroup
-#endif
-#ifndef FMLP_GU_S
-#define FMLP_GU_S 8   // waves per gate/up workgroup (split K)
-#endif
-#ifndef FMLP_GU_P
-#define FMLP_GU_P 2   // ring depth (tiles in flight per wave and row block)
-#endif
-#ifndef FMLP_GU_S_MANY
-#define FMLP_GU_S_MANY 4     // waves per gate/up workgroup when there are many workgroups
-#endif
-#ifndef FMLP_GU_MANY_WGS
-#define FMLP_GU_MANY_WGS 768  // "many": at least this many gate/up workgroups
-#endif
-#ifndef FMLP_DN_S
-#define FMLP_DN_S 16
-#endif
-#ifndef FMLP_DN_P
-#define FMLP_DN_P 1
-#endif
-#ifndef FMLP_Q4_P
-#define FMLP_Q4_P 1   // int4 ring depth (super-tiles of 4 groups)
-#endif
-#ifndef FMLP_Q4_DN_P
-#define FMLP_Q4_DN_P FMLP_Q4_P  // int4 down ring depth
-#endif
-#ifndef FMLP_Q4_GU_RB
-#define FMLP_Q4_GU_RB 2  // int4 gate/up row blocks per workgroup
-#endif
-#ifndef FMLP_DN_SPLIT_S
-#define FMLP_DN_SPLIT_S 8  // waves per workgroup of a K-split down launch
-#endif
-#ifndef FMLP_DN_RB
-#define FMLP_DN_RB 1     // down row blocks per workgroup (bf16)
-#endif
-#ifndef FMLP_Q4_DN_RB
-#define FMLP_Q4_DN_RB 2  // down row blocks per workgroup (int4)
-#endif
-#ifndef FMLP_FU_S
-#define FMLP_FU_S 16     // waves per single-pass workgroup
-#endif
-#ifndef FMLP_FU_P
-#define FMLP_FU_P 1      // single-pass gate/up ring depth
-#endif
-#ifndef FMLP_FU_DQ
-#define FMLP_FU_DQ 8     // single-pass down tiles in flight per wave
-#endif
-#ifndef FMLP_BIG_M
-#define FMLP_BIG_M 4       // above this M, the activation loads of each K unit are
-#endif                     // shared by more weight rows (the settings below)
-#ifndef FMLP_BIG_DN_M
-#define FMLP_BIG_DN_M 1    // the down kernel's large-M settings from this M on (exclusive)
-#endif
-#ifndef FMLP_BIG_GU_RB
-#define FMLP_BIG_GU_RB 4   // bf16 gate/up row blocks per workgroup for M > FMLP_BIG_M
-#endif
-#ifndef FMLP_BIG_DN_RB
-#define FMLP_BIG_DN_RB 4   // down row blocks per workgroup for M > FMLP_BIG_M (split K)
-#endif
-#ifndef FMLP_BIG_DN_S
-#define FMLP_BIG_DN_S 8    // and its waves (M <= 16)
-#endif
-#ifndef FMLP_BIG_DN_S2
-#define FMLP_BIG_DN_S2 8   // and its waves (M > 16; 16 measured 3-9% slower)
-#endif
-#ifndef FMLP_BIG_GU_RB2
-#define FMLP_BIG_GU_RB2 4  // bf16 gate/up row blocks per workgroup for M > 16 ...
-#endif
-#ifndef FMLP_BIG_GU_RB2W
-#define FMLP_BIG_GU_RB2W 8 // ... or this many, where that adds no row blocks to the most
-#endif                     // any CU streams (big_gu_wide)
-#ifndef FMLP_Q4_BIG_GU_RB
-#define FMLP_Q4_BIG_GU_RB 4  // int4 gate/up row blocks per workgroup for 4 < M <= 16
-#endif
-#ifndef FMLP_MASK_ACT
-#define FMLP_MASK_ACT 0    // activation loads only in lanes that hold a token
-#endif
-#ifndef FMLP_DEC_LDS_BF16_DN
-#define FMLP_DEC_LDS_BF16_DN 0  // also stage the bf16 down kernel's a (small M)
-#endif
-#ifndef FMLP_DEC_LDS_BF16_GU
-#define FMLP_DEC_LDS_BF16_GU 1  // also stage bf16 gate/up activations (small M, no residual)
-#endif
-#ifndef FMLP_DEC_LDS
-#define FMLP_DEC_LDS 1     // stage small-M activations in LDS (0: read them per wave)
-#endif
-#ifndef FMLP_H16_MIN_M
-#define FMLP_H16_MIN_M 17  // bf16 weights: from this M on, fp16 activations (WK_BF16H);
-                           // measured: -10% at Llama-8B M=32, no gain at M=16 (the prep
-                           // launch costs what the kernels save), a loss at M=8
-#endif
-#ifndef FMLP_FU_DYN_LDS
-#define FMLP_FU_DYN_LDS 0  // extra (unused) LDS per single-pass workgroup, bytes
-#endif
-
 namespace fmlp {
+
+// Launch settings, each chosen by measurement on MI355X.
+constexpr int kGuRb = 2;          // 16-row blocks per gate/up workgroup
+constexpr int kGuS = 8;           // waves per gate/up workgroup (split K)
+constexpr int kGuP = 2;           // ring depth (tiles in flight per wave and row block)
+constexpr int kGuSMany = 4;       // waves per gate/up workgroup when there are many workgroups
+constexpr int kGuManyWgs = 768;   // "many": at least this many gate/up workgroups
+constexpr int kDnS = 16;          // waves per down workgroup
+constexpr int kDnP = 1;           // down ring depth
+constexpr int kQ4P = 1;           // int4 ring depth (super-tiles of 4 groups), both kernels
+constexpr int kQ4GuRb = 2;        // int4 gate/up row blocks per workgroup
+constexpr int kDnSplitS = 8;      // waves per workgroup of a K-split down launch
+constexpr int kDnRb = 1;          // down row blocks per workgroup (bf16)
+constexpr int kQ4DnRb = 2;        // down row blocks per workgroup (int4)
+constexpr int kFuS = 16;          // waves per single-pass workgroup
+constexpr int kFuP = 1;           // single-pass gate/up ring depth
+constexpr int kFuDq = 8;          // single-pass down tiles in flight per wave
+// Above kBigM tokens the activation loads of each K unit are shared by more
+// weight rows (the settings below).
+constexpr int kBigM = 4;
+constexpr int kBigDnM = 1;        // the down kernel's large-M settings above this M
+constexpr int kBigGuRb = 4;       // bf16 gate/up row blocks per workgroup for M > kBigM
+constexpr int kBigDnRb = 4;       // down row blocks per workgroup for M > kBigDnM (split K)
+constexpr int kBigDnS = 8;        // and its waves (M <= 16)
+constexpr int kBigDnS2 = 8;       // and its waves (M > 16; 16 measured 3-9% slower)
+constexpr int kBigGuRb2 = 4;      // bf16 gate/up row blocks per workgroup for M > 16 ...
+constexpr int kBigGuRb2w = 8;     // ... or this many, where that adds no row blocks to the
+                                  // most any CU streams (gu_wide below)
+constexpr int kQ4BigGuRb = 4;     // int4 gate/up row blocks per workgroup for 4 < M <= 16
+// bf16 weights: from this M on, fp16 activations (WK_BF16H); measured -10% at
+// Llama-8B M=32, no gain at M=16 (the prep launch costs what the kernels
+// save), a loss at M=8.
+constexpr int kH16MinM = 17;
 
 // Weight kinds: bf16 weights with the bf16 hi + lo activation pair; int4
 // weights; bf16 weights with fp16 activations (several tokens: one MFMA per
@@ -158,22 +94,24 @@ constexpr bool wk_h16(int wk) { return wk == WK_BF16H || wk == WK_F16; }
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Down-projection split along K (see k_decode_down): with `blocks` row-block
-// groups (d/16 over the row blocks per workgroup), split each into k slices when that spreads the work more evenly over the
-// 256 CUs (time ~ rounds of workgroups / k), keeping at least min_units K
-// units per slice; at most kMaxSplit.
+// groups (d/16 over the row blocks per workgroup), split each into k slices
+// when that spreads the work more evenly over the 256 CUs (time ~ rounds of
+// workgroups / k), keeping at least min_units K units per slice; at most
+// kMaxSplit. The kernel gives each slice ceil(nu / splits) units, so the
+// count is taken as ceil(nu / ceil(nu / k)): then (splits - 1) slices of that
+// length cover fewer than nu units and no slice is empty.
 constexpr int kMaxSplit = 8;
 static int down_splits(int64_t blocks, int64_t ff, bool int4) {
-#ifdef FMLP_DN_SPLIT
-  return FMLP_DN_SPLIT;
-#endif
   const int64_t nu = int4 ? (ff + 127) / 128 : ff / 32;
   const int64_t min_units = int4 ? 4 : 16;
   int best = 1;
   double tb = (double)((blocks + 255) / 256);
   for (int k = 2; k <= kMaxSplit; ++k) {
     if (nu / k < min_units) break;
-    const double t = (double)((blocks * k + 255) / 256) / k;
-    if (t < tb - 1e-9) tb = t, best = k;
+    const int64_t per = (nu + k - 1) / k;
+    const int s = (int)((nu + per - 1) / per);
+    const double t = (double)((blocks * s + 255) / 256) / s;
+    if (t < tb - 1e-9) tb = t, best = s;
   }
   return best;
 }
@@ -414,19 +352,6 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) wb[slot][rb] = ld16_stream(wt + ((rb0 + rb) * nkb + kb) * 512);
       if constexpr (!kLds) {
-#if FMLP_MASK_ACT
-        // only lanes that hold a token load activations (at M = 1 that is 4
-        // lanes of 64; the rest would re-read the same 64 bytes)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          if (tok[cb]) {
-            hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
-            if (MODE == ACT_HL) lb[slot][cb] = ld16(act1 + aoff[cb] + kb * 32);
-            if (MODE == ACT_XR) lb[slot][cb] = ld16(res + aoff[cb] + kb * 32);  // residual
-          }
-        }
-        if (kX && tok[0]) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
-#else
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           hb[slot][cb] = ld16(act0 + aoff[cb] + kb * 32);
@@ -434,7 +359,6 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
           if (MODE == ACT_XR) lb[slot][cb] = ld16(res + aoff[cb] + kb * 32);  // residual
         }
         if (kX) gb[slot] = ld16(act1 + grp * 8 + kb * 32);
-#endif
       }
     };
     // no branches around the first loads, so that the compiler's wait for
@@ -541,7 +465,7 @@ __device__ __forceinline__ void gemv_core(const void* __restrict__ w,
           const int kb = q * 4 + j < nkb ? q * 4 + j : nkb - 1;  // padding groups are skipped
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
-            if (!FMLP_MASK_ACT || tok[cb]) ab[slot][j][cb] = ld16(act0 + aoff[cb] + kb * 32);
+            ab[slot][j][cb] = ld16(act0 + aoff[cb] + kb * 32);
         }
       }
     };
@@ -1081,15 +1005,15 @@ hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
   float* part = reinterpret_cast<float*>(p.ws);
   const int nw = p.ff / 32;
   auto go = [&](auto kern) {
-    launch_kernel(KK_DECODE_FUSED_BF16, kern, dim3(nw), dim3(64 * FMLP_FU_S), FMLP_FU_DYN_LDS,
+    launch_kernel(KK_DECODE_FUSED_BF16, kern, dim3(nw), dim3(64 * kFuS), 0,
                   stream, static_cast<const uint16_t*>(p.w_gu),
                   static_cast<const uint16_t*>(p.w_down), p.x, p.gamma, p.eps, part, p.M, p.d,
                   p.ff, p.act, p.res, p.hout);
   };
   if (p.res)
-    go(k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ, true>);
+    go(k_decode_fused<kFuS, kFuP, kFuDq, true>);
   else
-    go(k_decode_fused<FMLP_FU_S, FMLP_FU_P, FMLP_FU_DQ, false>);
+    go(k_decode_fused<kFuS, kFuP, kFuDq, false>);
   hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
   launch_kernel(KK_PARTIAL_REDUCE, k_partial_reduce, dim3(p.d / 16, p.M), dim3(256), 0, stream,
@@ -1104,7 +1028,7 @@ hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
 template <int WK, int NCB, int DRB, int S, bool STAGE>
 static void launch_down(const Problem& p, const DecodeWs& ws, int splits, bool lds,
                         int64_t lds_bytes, hipStream_t stream) {
-  constexpr int DP = WK == WK_INT4 ? FMLP_Q4_DN_P : FMLP_DN_P;
+  constexpr int DP = WK == WK_INT4 ? kQ4P : kDnP;
   const int kind = WK == WK_INT4 ? KK_DECODE_DOWN_INT4 : KK_DECODE_DOWN_BF16;
   const dim3 grid(p.d / (16 * DRB), splits), block(64 * S);
   // int4 at M = 1: one accumulator row per lane holds the token
@@ -1126,9 +1050,9 @@ template <int WK, int NCB, int RB, int S>
 static void launch_gateup_s(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
                             const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
                             hipStream_t stream) {
-  constexpr int GP = WK == WK_INT4 ? FMLP_Q4_P : FMLP_GU_P;
+  constexpr int GP = WK == WK_INT4 ? kQ4P : kGuP;
   constexpr bool kStage =
-      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_GU));
+      NCB == 1 && (WK == WK_INT4 || WK == WK_BF16);
   const int kind = WK == WK_INT4 ? KK_DECODE_GATEUP_INT4 : KK_DECODE_GATEUP_BF16;
   // 2ff is a multiple of 64, so RB <= 4 divides the gate/up row blocks; a
   // larger RB is launched only where launch_decode_t checked that it does
@@ -1158,21 +1082,21 @@ template <int WK, int NCB, int RB>
 static void launch_gateup(const Problem& p, const DecodeWs& ws, const uint16_t* act0,
                           const uint16_t* act1, int ncnt, bool lds, int64_t lds_bytes,
                           hipStream_t stream) {
-  if (WK != WK_INT4 && NCB == 1 && (2 * p.ff) / (16 * RB) >= FMLP_GU_MANY_WGS)
-    launch_gateup_s<WK, NCB, RB, FMLP_GU_S_MANY>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
+  if (WK != WK_INT4 && NCB == 1 && (2 * p.ff) / (16 * RB) >= kGuManyWgs)
+    launch_gateup_s<WK, NCB, RB, kGuSMany>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
   else
-    launch_gateup_s<WK, NCB, RB, FMLP_GU_S>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
+    launch_gateup_s<WK, NCB, RB, kGuS>(p, ws, act0, act1, ncnt, lds, lds_bytes, stream);
 }
 
 template <int WK, int NCB>
 static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const DecodeWs ws = decode_ws(p);
-  constexpr int GRB = WK == WK_INT4 ? FMLP_Q4_GU_RB : FMLP_GU_RB;
+  constexpr int GRB = WK == WK_INT4 ? kQ4GuRb : kGuRb;
   constexpr int RB = (NCB == 1) ? GRB : (GRB > 2 ? 2 : GRB);
-  constexpr int DRB = WK == WK_INT4 ? FMLP_Q4_DN_RB : FMLP_DN_RB;
-  constexpr bool kStage = FMLP_DEC_LDS && NCB == 1 && WK == WK_INT4;
+  constexpr int DRB = WK == WK_INT4 ? kQ4DnRb : kDnRb;
+  constexpr bool kStage = NCB == 1 && WK == WK_INT4;
   constexpr bool kStageDn =
-      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_DN));
+      NCB == 1 && WK == WK_INT4;
   hipError_t e;
   if constexpr (WK != WK_BF16) {
     launch_kernel(KK_ACT_PREP, k_act_prep<WK == WK_INT4>, dim3(p.M), dim3(512), 0, stream, p.x,
@@ -1184,16 +1108,16 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const uint16_t* act1 = WK == WK_BF16 ? p.gamma : nullptr;
   // Larger M: every K unit's activation loads (M tokens per wave) cost as
   // much as its weight loads, so more weight rows share them: bf16 gate/up
-  // takes FMLP_BIG_GU_RB row blocks per workgroup, and the down projection
-  // FMLP_BIG_DN_RB, split along K to keep enough workgroups.
-  const bool big = p.M > FMLP_BIG_M;
-  // down: BDRB row blocks per workgroup, split along K, from M > FMLP_BIG_DN_M
+  // takes kBigGuRb row blocks per workgroup, and the down projection
+  // kBigDnRb, split along K to keep enough workgroups.
+  const bool big = p.M > kBigM;
+  // down: BDRB row blocks per workgroup, split along K, from M > kBigDnM
   // (two tokens on: measured 4-10% faster down kernels at M = 2..4 on the
   // Phi-3, Llama-8B and 70B int4 shapes); otherwise DRB row blocks per
   // workgroup when they divide d and leave enough workgroups to cover the
   // CUs; else one, split along K when that helps
-  constexpr int BDRB = FMLP_BIG_DN_RB;
-  const bool bdrb = p.M > FMLP_BIG_DN_M && p.d % (16 * BDRB) == 0;
+  constexpr int BDRB = kBigDnRb;
+  const bool bdrb = p.M > kBigDnM && p.d % (16 * BDRB) == 0;
   const bool drb = !bdrb && DRB > 1 && p.d % (16 * DRB) == 0 && p.d / (16 * DRB) >= 256;
   const int dn_rb = bdrb ? BDRB : drb ? DRB : 1;
   const int splits = drb ? 1 : down_splits(p.d / (16 * dn_rb), p.ff, WK == WK_INT4);
@@ -1203,9 +1127,9 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   // 10 % in down; bf16 gate/up gains 3-4 % (Phi-3, Llama-8B), while bf16
   // down loses up to 14 %, so the bf16 down kernel reads its a per wave.
   auto lds_budget = [](int64_t wgs) -> int64_t { return wgs <= 256 ? 96 * 1024 : 32 * 1024; };
-  constexpr int BGRB = NCB == 1 ? FMLP_BIG_GU_RB : FMLP_BIG_GU_RB2, BGRBW = FMLP_BIG_GU_RB2W;
-  constexpr int Q4B = FMLP_Q4_BIG_GU_RB;
-  // int4 takes Q4B row blocks from M > FMLP_BIG_M up to 16 tokens (its
+  constexpr int BGRB = NCB == 1 ? kBigGuRb : kBigGuRb2, BGRBW = kBigGuRb2w;
+  constexpr int Q4B = kQ4BigGuRb;
+  // int4 takes Q4B row blocks from M > kBigM up to 16 tokens (its
   // registers hold RB at two token blocks); bf16 / fp16 at two token blocks
   // take BGRBW instead of BGRB where that divides the row blocks and adds none
   // to the most any CU streams (rounds of 256 workgroups times row blocks):
@@ -1225,13 +1149,13 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   const int64_t gu_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * p.d;
   // (bf16 gate/up staging, when enabled, does not cover the residual prologue)
   constexpr bool kStageGu =
-      FMLP_DEC_LDS && NCB == 1 && (WK == WK_INT4 || (WK == WK_BF16 && FMLP_DEC_LDS_BF16_GU));
+      NCB == 1 && (WK == WK_INT4 || WK == WK_BF16);
   const bool gl = kStageGu && (WK == WK_INT4 || !p.res) && p.M <= kLdsMaxM &&
                   gu_lds <= lds_budget(gu_wgs);
   const int ukd = WK == WK_INT4 ? 128 : 32, nud = (p.ff + ukd - 1) / ukd;
   const int64_t dn_wgs = (p.d / (16 * dn_rb)) * splits;
   const int64_t dn_lds = (int64_t)(WK == WK_BF16 ? 4 : 2) * p.M * ((nud + splits - 1) / splits) * ukd;
-  const bool dl = (kStage || FMLP_DEC_LDS_BF16_DN) && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
+  const bool dl = kStage && p.M <= kLdsMaxM && dn_lds <= lds_budget(dn_wgs);
 
   const int ncnt = splits > 1 ? (int)(p.d / 16) : 0;
   if (gu_wide) {
@@ -1248,15 +1172,15 @@ static hipError_t launch_decode_t(const Problem& p, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (bdrb)
     // (int4 with two token blocks keeps 8 waves: its registers do not fit 16)
-    launch_down<WK, NCB, BDRB, (NCB == 1 || WK == WK_INT4) ? FMLP_BIG_DN_S : FMLP_BIG_DN_S2,
+    launch_down<WK, NCB, BDRB, (NCB == 1 || WK == WK_INT4) ? kBigDnS : kBigDnS2,
                 kStageDn>(p, ws, splits, dl, dn_lds, stream);
   else if (drb)
-    launch_down<WK, NCB, DRB, (NCB == 2 && WK == WK_INT4) ? 8 : FMLP_DN_S, kStageDn>(
+    launch_down<WK, NCB, DRB, (NCB == 2 && WK == WK_INT4) ? 8 : kDnS, kStageDn>(
         p, ws, splits, dl, dn_lds, stream);
   else if (splits == 1)
-    launch_down<WK, NCB, 1, FMLP_DN_S, kStageDn>(p, ws, splits, dl, dn_lds, stream);
+    launch_down<WK, NCB, 1, kDnS, kStageDn>(p, ws, splits, dl, dn_lds, stream);
   else  // split slices are short: 8 waves each, so that more of them are resident per CU
-    launch_down<WK, NCB, 1, FMLP_DN_SPLIT_S, kStageDn>(p, ws, splits, dl, dn_lds, stream);
+    launch_down<WK, NCB, 1, kDnSplitS, kStageDn>(p, ws, splits, dl, dn_lds, stream);
   return hipGetLastError();
 }
 
@@ -1267,7 +1191,7 @@ hipError_t launch_decode(const Problem& p, hipStream_t stream) {
   if (p.wtype == 2)
     return p.M <= 16 ? launch_decode_t<WK_F16, 1>(p, stream)
                      : launch_decode_t<WK_F16, 2>(p, stream);
-  if (p.M >= FMLP_H16_MIN_M)
+  if (p.M >= kH16MinM)
     return p.M <= 16 ? launch_decode_t<WK_BF16H, 1>(p, stream)
                      : launch_decode_t<WK_BF16H, 2>(p, stream);
   return p.M <= 16 ? launch_decode_t<WK_BF16, 1>(p, stream) : launch_decode_t<WK_BF16, 2>(p, stream);

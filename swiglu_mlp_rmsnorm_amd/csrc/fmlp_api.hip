@@ -48,6 +48,11 @@ bool matrix_ok(int64_t rows, int64_t K) {
   return rows > 0 && K > 0 && rows % 16 == 0 && K % 32 == 0 && rows <= 2 * kMaxFF && K <= kMaxFF;
 }
 
+// a row-major [rows, K] matrix in the int4 exchange format (no row blocking)
+bool rowmajor_ok(int64_t rows, int64_t K) {
+  return rows > 0 && K > 0 && K % 32 == 0 && rows <= 2 * kMaxFF && K <= kMaxFF;
+}
+
 // Device check, cached once per device (querying properties on every launch
 // costs host time in a decode loop; the V100 report in the llama.cpp digest
 // measured exactly that).
@@ -133,11 +138,10 @@ int fmlp_int4_sizes(int64_t rows, int64_t K, size_t* code_bytes, size_t* scale_b
 int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* scales,
                        void* stream) {
   if (!w || !q || !scales) return FMLP_ERR_INVALID_ARG;
-  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!rowmajor_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FMLP_ERR_ALIGNMENT;
-  const Span sw = span(w, (size_t)rows * K * 2),
-             sq = span(q, (size_t)fmlp::int4_code_bytes(rows, K)),
-             ss = span(scales, (size_t)fmlp::int4_scale_bytes(rows, K));
+  const Span sw = span(w, (size_t)rows * K * 2), sq = span(q, (size_t)rows * (K / 2)),
+             ss = span(scales, (size_t)rows * (K / 32) * 2);
   if (overlap(sw, sq) || overlap(sw, ss) || overlap(sq, ss)) return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;
   std::lock_guard<std::mutex> lock(g_flag_mutex);
@@ -147,6 +151,49 @@ int fmlp_quantize_int4(const void* w, int64_t rows, int64_t K, void* q, void* sc
                                        static_cast<hipStream_t>(stream), &range_error);
   if (e != hipSuccess) return hip_fail(e);
   return range_error ? FMLP_ERR_RANGE : FMLP_OK;
+}
+
+int fmlp_pack_int4_interleaved(const void* q_gate, const void* s_gate, const void* q_up,
+                               const void* s_up, int64_t ff, int64_t d, void* q_gu, void* s_gu,
+                               void* stream) {
+  if (!q_gate || !s_gate || !q_up || !s_up || !q_gu || !s_gu) return FMLP_ERR_INVALID_ARG;
+  if (!shape_ok(d, ff)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(q_gate) || !aligned16(s_gate) || !aligned16(q_up) || !aligned16(s_up) ||
+      !aligned16(q_gu) || !aligned16(s_gu))
+    return FMLP_ERR_ALIGNMENT;
+  const size_t qb = (size_t)ff * (d / 2), sb = (size_t)ff * (d / 32) * 2;
+  const Span oq = span(q_gu, (size_t)fmlp::int4_code_bytes(2 * ff, d)),
+             os = span(s_gu, (size_t)fmlp::int4_scale_bytes(2 * ff, d));
+  const Span in[4] = {span(q_gate, qb), span(s_gate, sb), span(q_up, qb), span(s_up, sb)};
+  if (overlap(oq, os)) return FMLP_ERR_INVALID_ARG;
+  for (const Span& i : in)
+    if (overlap(oq, i) || overlap(os, i)) return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  hipError_t e = fmlp::launch_tile_int4(
+      static_cast<const uint8_t*>(q_gate), static_cast<const uint16_t*>(s_gate),
+      static_cast<const uint8_t*>(q_up), static_cast<const uint16_t*>(s_up), 2 * ff, d,
+      static_cast<uint8_t*>(q_gu), static_cast<uint16_t*>(s_gu), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+int fmlp_pack_int4_matrix(const void* q, const void* scales, int64_t rows, int64_t K,
+                          void* q_tiled, void* s_tiled, void* stream) {
+  if (!q || !scales || !q_tiled || !s_tiled) return FMLP_ERR_INVALID_ARG;
+  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!aligned16(q) || !aligned16(scales) || !aligned16(q_tiled) || !aligned16(s_tiled))
+    return FMLP_ERR_ALIGNMENT;
+  const Span iq = span(q, (size_t)rows * (K / 2)), is = span(scales, (size_t)rows * (K / 32) * 2);
+  const Span oq = span(q_tiled, (size_t)fmlp::int4_code_bytes(rows, K)),
+             os = span(s_tiled, (size_t)fmlp::int4_scale_bytes(rows, K));
+  if (overlap(oq, os) || overlap(oq, iq) || overlap(oq, is) || overlap(os, iq) || overlap(os, is))
+    return FMLP_ERR_INVALID_ARG;
+  if (int st = check_device()) return st;
+  hipError_t e = fmlp::launch_tile_int4(static_cast<const uint8_t*>(q),
+                                        static_cast<const uint16_t*>(scales), nullptr, nullptr,
+                                        rows, K, static_cast<uint8_t*>(q_tiled),
+                                        static_cast<uint16_t*>(s_tiled),
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FMLP_OK : hip_fail(e);
 }
 
 int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream) {
@@ -167,11 +214,11 @@ int fmlp_convert_f16(const void* w, void* out, int64_t n, void* stream) {
 int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K, float* out,
                       void* stream) {
   if (!q || !scales || !out) return FMLP_ERR_INVALID_ARG;
-  if (!matrix_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
+  if (!rowmajor_ok(rows, K)) return FMLP_ERR_UNSUPPORTED_SHAPE;
   if (!aligned16(q) || !aligned16(scales) || !aligned16(out)) return FMLP_ERR_ALIGNMENT;
   const Span so = span(out, (size_t)rows * K * 4);
-  if (overlap(so, span(q, (size_t)fmlp::int4_code_bytes(rows, K))) ||
-      overlap(so, span(scales, (size_t)fmlp::int4_scale_bytes(rows, K))))
+  if (overlap(so, span(q, (size_t)rows * (K / 2))) ||
+      overlap(so, span(scales, (size_t)rows * (K / 32) * 2)))
     return FMLP_ERR_INVALID_ARG;
   if (int st = check_device()) return st;
   hipError_t e = fmlp::launch_dequant(static_cast<const uint8_t*>(q),
@@ -182,14 +229,14 @@ int fmlp_dequant_int4(const void* q, const void* scales, int64_t rows, int64_t K
 
 size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
   if (M < 0 || M > kMaxM || !shape_ok(d, ff) || !wtype_ok(wtype)) return 0;
-  // the largest need of the paths the problem may take; the single-pass
-  // term is kept at its M = kFusedMaxM value above that, so the size never
-  // decreases as M grows (a buffer sized for the largest M serves them all)
-  size_t b = fmlp::prefill_workspace_bytes(M, d, ff, wtype);
-  if (M <= fmlp::kDecodeMaxM) {
-    const size_t dec = fmlp::decode_workspace_bytes(M, d, ff);
-    b = dec > b ? dec : b;
-  }
+  // the largest need of the paths the problem may take, each the largest
+  // over every smaller M as well (decode and the single pass grow with M;
+  // the prefill envelope covers its split-K partials, which do not), so a
+  // buffer sized for the largest M serves every call
+  size_t b = fmlp::prefill_workspace_envelope(M, d, ff, wtype);
+  const int64_t md = M < fmlp::kDecodeMaxM ? M : fmlp::kDecodeMaxM;
+  const size_t dec = fmlp::decode_workspace_bytes(md, d, ff);
+  b = dec > b ? dec : b;
   if (wtype == FMLP_W_BF16) {
     const size_t one = fmlp::fused_partial_bytes(M < fmlp::kFusedMaxM ? M : fmlp::kFusedMaxM, d, ff);
     b = one > b ? one : b;
@@ -250,6 +297,9 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
   const Span sw = span(workspace, workspace_bytes);
   if (overlap(sw, span(x, (size_t)M * d * 2)) || overlap(sw, span(gamma, (size_t)d * 2)) ||
       overlap(sw, span(w_gu, wgu_b)) || overlap(sw, span(w_down, wd_b)))
+    return FMLP_ERR_INVALID_ARG;
+  if (int4 && (overlap(sw, span(gu_scales, (size_t)fmlp::int4_scale_bytes(2 * ff, d))) ||
+               overlap(sw, span(down_scales, (size_t)fmlp::int4_scale_bytes(d, ff)))))
     return FMLP_ERR_INVALID_ARG;
   if (residual) {
     // the residual stream is written while x and the residual are still read

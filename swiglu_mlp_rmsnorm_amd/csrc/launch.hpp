@@ -40,6 +40,8 @@ inline int64_t int4_scale_bytes(int64_t R, int64_t K) { return (R / 16) * ((K + 
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff);
 size_t fused_partial_bytes(int64_t M, int64_t d, int64_t ff);
 size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype);
+// The largest prefill_workspace_bytes(M', d, ff, wtype) over 1 <= M' <= M.
+size_t prefill_workspace_envelope(int64_t M, int64_t d, int64_t ff, int wtype);
 
 hipError_t launch_pack(const uint16_t* w_gate, const uint16_t* w_up, uint16_t* w_gu, int64_t ff,
                        int64_t d, hipStream_t stream);
@@ -51,6 +53,11 @@ hipError_t launch_convert_f16(const uint16_t* w, uint16_t* out, int64_t n, hipSt
                               int* range_error);
 hipError_t launch_dequant(const uint8_t* q, const uint16_t* scales, int64_t rows, int64_t K,
                           float* out, hipStream_t stream);
+// Row-major int4 [R, K] (or the row interleave of two [R/2, K] matrices when
+// qb is non-null) -> the tiled int4 layout.
+hipError_t launch_tile_int4(const uint8_t* qa, const uint16_t* sa, const uint8_t* qb,
+                            const uint16_t* sb, int64_t R, int64_t K, uint8_t* qt, uint16_t* st,
+                            hipStream_t stream);
 
 hipError_t launch_decode(const Problem& p, hipStream_t stream);
 hipError_t launch_decode_fused(const Problem& p, hipStream_t stream);

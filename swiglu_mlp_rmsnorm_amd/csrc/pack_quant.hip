@@ -1,6 +1,7 @@
 // Weight preparation: gate/up row interleave into the fragment-tiled layout,
-// plain tiling (for W_down), int4 group-32 quantisation of a tiled matrix,
-// and the int4 -> fp32 expansion test hook.
+// plain tiling (for W_down), int4 group-32 quantisation and its fp32
+// expansion (test hook) in the row-major exchange format, and the tiling of
+// row-major int4 (interleaved or plain) into the layout the kernels read.
 //
 // Fragment-tiled bf16 layout of a logical matrix W [R, K] (R % 16 == 0,
 // K % 32 == 0): one 1024-byte tile per (16-row block rb, 32-column block kb),
@@ -101,39 +102,31 @@ hipError_t launch_convert_f16(const uint16_t* w, uint16_t* out, int64_t n, hipSt
 }
 
 // ---------------------------------------------------------------- int4
+// Exchange format (row-major, what callers hold): codes q uint8 [R, K/2],
+// column k in byte k/2, even k in the low nibble, two's complement; scales
+// fp16 [R, K/32], one per group of 32 consecutive columns of a row.
 __device__ int g_quant_range_error;
 
 __global__ void k_quant_flag_reset() { g_quant_range_error = 0; }
 
-// One thread per (row, group) of the padded group range; 16 consecutive
-// threads take the 16 rows of a block so their tile reads are contiguous.
+// One thread per (row, group), consecutive threads along a row's groups.
 // s = fp16_rne(max|w| / 7) with IEEE fp32 division; q = clamp(rint(w / s),
 // -8, 7) with rint rounding half to even; q = 0 when s == 0.
-__global__ __launch_bounds__(256) void k_quantize_int4(const uint16_t* __restrict__ wt,
-                                                       int64_t R, int64_t K,
-                                                       uint32_t* __restrict__ qt,
-                                                       uint16_t* __restrict__ st) {
-  const int64_t nkb = K / 32, nq = (K + 127) / 128, gpad = nq * 4;
+__global__ __launch_bounds__(256) void k_quantize_int4(const uint16_t* __restrict__ w, int64_t R,
+                                                       int64_t K, uint8_t* __restrict__ q,
+                                                       uint16_t* __restrict__ sc) {
+  const int64_t ng = K / 32;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (R / 16) * gpad * 16) return;
-  const int i = (int)(t & 15);
-  const int64_t g = (t >> 4) % gpad, rb = (t >> 4) / gpad;
-  const int64_t word0 = (rb * nq + g / 4) * 256 + (g % 4);  // + 4*slot
-  const int64_t sidx = (rb * nq + g / 4) * 64 + i * 4 + (g % 4);
-  if (g >= nkb) {  // padding group
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) qt[word0 + (sub * 16 + i) * 4] = 0u;
-    st[sidx] = 0;
-    return;
-  }
+  if (t >= R * ng) return;
+  const int64_t r = t / ng, g = t - r * ng;
   float f[32];
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
-    const u32x4 v = ld16(wt + (rb * nkb + g) * 512 + (sub * 16 + i) * 8);
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 v = ld16(w + r * K + g * 32 + c * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f[sub * 8 + 2 * j] = bf16_lo(v[j]);
-      f[sub * 8 + 2 * j + 1] = bf16_hi(v[j]);
+      f[c * 8 + 2 * j] = bf16_lo(v[j]);
+      f[c * 8 + 2 * j + 1] = bf16_hi(v[j]);
     }
   }
   float mx = 0.0f;
@@ -149,29 +142,31 @@ __global__ __launch_bounds__(256) void k_quantize_int4(const uint16_t* __restric
     atomicOr(&g_quant_range_error, 1);
     return;
   }
-  st[sidx] = __builtin_bit_cast(uint16_t, sh);
+  sc[r * ng + g] = __builtin_bit_cast(uint16_t, sh);
+  u32x4 out;
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
+  for (int c = 0; c < 4; ++c) {
     uint32_t word = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       int qi = 0;
       if (s != 0.0f) {
-        const float r = rintf(__fdiv_rn(f[sub * 8 + m], s));
-        qi = (int)fminf(fmaxf(r, -8.0f), 7.0f);
+        const float rq = rintf(__fdiv_rn(f[c * 8 + m], s));
+        qi = (int)fminf(fmaxf(rq, -8.0f), 7.0f);
       }
       word |= (uint32_t)(qi & 0xF) << (4 * m);
     }
-    qt[word0 + (sub * 16 + i) * 4] = word;
+    out[c] = word;
   }
+  st16(q + r * (K / 2) + g * 16, out);
 }
 
-hipError_t launch_quantize(const uint16_t* wt, int64_t R, int64_t K, uint8_t* qt, uint16_t* st,
-                           hipStream_t stream, int* range_error) {
+hipError_t launch_quantize(const uint16_t* w, int64_t rows, int64_t K, uint8_t* q,
+                           uint16_t* scales, hipStream_t stream, int* range_error) {
   hipLaunchKernelGGL(k_quant_flag_reset, dim3(1), dim3(1), 0, stream);
-  const int64_t threads = (R / 16) * ((K + 127) / 128) * 4 * 16;
+  const int64_t threads = rows * (K / 32);
   launch_kernel(KK_QUANTIZE, k_quantize_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256),
-                0, stream, wt, R, K, reinterpret_cast<uint32_t*>(qt), st);
+                0, stream, w, rows, K, q, scales);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int flag = 0;
@@ -184,38 +179,86 @@ hipError_t launch_quantize(const uint16_t* wt, int64_t R, int64_t K, uint8_t* qt
 }
 
 // One thread per (row, group): out[r, 32g + k] = float(s) * float(q), exact.
-__global__ __launch_bounds__(256) void k_dequant_int4(const uint32_t* __restrict__ qt,
-                                                      const uint16_t* __restrict__ st, int64_t R,
+__global__ __launch_bounds__(256) void k_dequant_int4(const uint8_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ sc, int64_t R,
                                                       int64_t K, float* __restrict__ out) {
-  const int64_t nkb = K / 32, nq = (K + 127) / 128;
+  const int64_t ng = K / 32;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= R * nkb) return;
-  const int64_t r = t / nkb, g = t % nkb;
-  const int64_t rb = r >> 4;
-  const int i = (int)(r & 15);
-  const float s = (float)__builtin_bit_cast(_Float16, st[(rb * nq + g / 4) * 64 + i * 4 + g % 4]);
+  if (t >= R * ng) return;
+  const int64_t r = t / ng, g = t - r * ng;
+  const float s = (float)__builtin_bit_cast(_Float16, sc[r * ng + g]);
+  const u32x4 words = ld16(q + r * (K / 2) + g * 16);
   float* o = out + r * K + g * 32;
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub) {
-    const uint32_t word = qt[(rb * nq + g / 4) * 256 + (sub * 16 + i) * 4 + g % 4];
+  for (int c = 0; c < 4; ++c) {
     float v[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const int nib = (int)((word >> (4 * m)) & 0xF);
+      const int nib = (int)((words[c] >> (4 * m)) & 0xF);
       v[m] = s * (float)(nib >= 8 ? nib - 16 : nib);
     }
-    st16(o + sub * 8, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                            __float_as_uint(v[3])});
-    st16(o + sub * 8 + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
-                                __float_as_uint(v[6]), __float_as_uint(v[7])});
+    st16(o + c * 8, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3])});
+    st16(o + c * 8 + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                              __float_as_uint(v[6]), __float_as_uint(v[7])});
   }
 }
 
-hipError_t launch_dequant(const uint8_t* qt, const uint16_t* st, int64_t R, int64_t K, float* out,
+hipError_t launch_dequant(const uint8_t* q, const uint16_t* s, int64_t R, int64_t K, float* out,
                           hipStream_t stream) {
   const int64_t threads = R * (K / 32);
   launch_kernel(KK_DEQUANT, k_dequant_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                stream, reinterpret_cast<const uint32_t*>(qt), st, R, K, out);
+                stream, q, s, R, K, out);
+  return hipGetLastError();
+}
+
+// Row-major int4 -> the tiled int4 layout (file comment). One thread per
+// 16-byte slot L of super-tile (rb, sq): row r = 16 rb + L % 16, word j the 8
+// codes of group 4 sq + j at columns 8 (L / 16) .. +7, i.e. the 4 bytes of
+// the row-major row at byte (32 (4 sq + j) + 8 (L / 16)) / 2. Threads with
+// L < 16 also write their row's 4 scales of the super-tile. Groups past K/32
+// get zero codes and scales. With qb non-null the logical matrix is the row
+// interleave of a (even rows) and b (odd rows), [2 Ra, K]: the gate/up
+// interleave of FastTPS review section 3 item 3 and the llama.cpp PR digest,
+// applied to quantised rows (quantisation groups never cross rows).
+__global__ __launch_bounds__(256) void k_tile_int4(const uint8_t* __restrict__ qa,
+                                                   const uint16_t* __restrict__ sa,
+                                                   const uint8_t* __restrict__ qb,
+                                                   const uint16_t* __restrict__ sb, int64_t R,
+                                                   int64_t K, uint8_t* __restrict__ qt,
+                                                   uint16_t* __restrict__ st) {
+  const int64_t nq = (K + 127) / 128, ng = K / 32;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= (R / 16) * nq * 64) return;
+  const int L = (int)(c & 63);
+  const int64_t tile = c >> 6, rb = tile / nq, sq = tile - rb * nq;
+  const int64_t r = rb * 16 + (L & 15);
+  const int64_t src_row = qb ? (r >> 1) : r;
+  const uint8_t* qrow = (qb && (r & 1) ? qb : qa) + src_row * (K / 2);
+  const uint16_t* srow = (qb && (r & 1) ? sb : sa) + src_row * ng;
+  u32x4 o;
+  uint16_t sv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t g = sq * 4 + j;
+    const bool real = g < ng;
+    o[j] = real ? *reinterpret_cast<const uint32_t*>(qrow + (g * 32 + (L >> 4) * 8) / 2) : 0u;
+    sv[j] = real ? srow[g] : (uint16_t)0;
+  }
+  st16(qt + c * 16, o);
+  if (L < 16) {
+    uint16_t* d = st + tile * 64 + L * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = sv[j];
+  }
+}
+
+hipError_t launch_tile_int4(const uint8_t* qa, const uint16_t* sa, const uint8_t* qb,
+                            const uint16_t* sb, int64_t R, int64_t K, uint8_t* qt, uint16_t* st,
+                            hipStream_t stream) {
+  const int64_t threads = (R / 16) * ((K + 127) / 128) * 64;
+  launch_kernel(KK_PACK, k_tile_int4, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                stream, qa, sa, qb, sb, R, K, qt, st);
   return hipGetLastError();
 }
 

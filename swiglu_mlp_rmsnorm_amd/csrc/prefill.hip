@@ -25,11 +25,6 @@
 #include <mutex>
 #include <type_traits>
 
-#ifndef FMLP_SETPRIO
-#define FMLP_SETPRIO 0  // raise the wave priority over each sub-step's MFMA block (no gain with the
-                        // reads hoisted to the sub-step's top; +1% before)
-#endif
-
 namespace fmlp {
 
 static inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -432,26 +427,22 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   for (; kt + 4 < nkt; ++kt) {
     const int st1 = st == 4 ? 0 : st + 1, st4 = st == 0 ? 4 : st - 1;
     if (!kSpread) load_a(kt + 4, st4);
-    if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(1);
     frag_load_ordered(1, st, 1);
     if (kSpread) load_a(kt + 4, st4);
     mma(0);
     convert(1);
     interleave(std::integral_constant<int, C::A_PER_T>{});
     __builtin_amdgcn_sched_barrier(0);
-    if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T + C::A_PER_T));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (!kSpread) load_b(kt + 4, st4);
-    if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(1);
     frag_load_ordered(0, st1, 0);
     if (kSpread) load_b(kt + 4, st4);
     mma(1);
     convert(0);
     interleave(std::integral_constant<int, C::B_PER_T>{});
     __builtin_amdgcn_sched_barrier(0);
-    if (FMLP_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // (the activation reads were issued a whole sub-step ago: a free wait
     // that leaves the next iteration's first MFMAs nothing to wait for)
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
@@ -549,24 +540,12 @@ static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* ou
   return hipGetLastError();
 }
 
-#ifndef FMLP_DOWN_W4
-#define FMLP_DOWN_W4 1  // down GEMM's 256 x 256 tile on 4 waves (128 x 128 each)
-#endif
-#ifndef FMLP_S1_WGM
-#define FMLP_S1_WGM 2  // 256 x 128 tiles: 4 x FMLP_S1_WGM waves (8 measured ~0.7% faster than 4)
-#endif
-#ifndef FMLP_DN_WGN
-#define FMLP_DN_WGN 2  // wave grid of the down GEMM's 256 x 256 tile on 4 waves
-#endif
-#ifndef FMLP_DN_WGM
-#define FMLP_DN_WGM 2
-#endif
-#ifndef FMLP_S0_WGN
-#define FMLP_S0_WGN 4  // wave grid of the 256 x 256 tile
-#endif
-#ifndef FMLP_S0_WGM
-#define FMLP_S0_WGM 2
-#endif
+constexpr int kDownW4 = 1;  // down GEMM's 256 x 256 tile on 4 waves (128 x 128 each)
+constexpr int kS1Wgm = 2;  // 256 x 128 tiles: 4 x kS1Wgm waves (8 measured ~0.7% faster than 4)
+constexpr int kDnWgn = 2;  // wave grid of the down GEMM's 256 x 256 tile on 4 waves
+constexpr int kDnWgm = 2;
+constexpr int kS0Wgn = 4;  // wave grid of the 256 x 256 tile
+constexpr int kS0Wgm = 2;
 
 // Tile shapes: 0 = 256 x 256 (gate/up: 8 waves, 4 x 2; down: 4 waves, 2 x 2),
 // 1 = 256 x 128 (8 waves, 4 x 2), 2 = 128 x 128 (4 waves, 2 x 2). tail_rows > 0: the last tail_rows feature
@@ -617,20 +596,20 @@ static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const u
   hipError_t e = hipSuccess;
   if (n_main > 0) {
     // the down GEMM runs the 256 x 256 tile on 4 waves, the gate/up GEMM on
-    // FMLP_S0_WGN x FMLP_S0_WGM (measured best for each)
-    constexpr bool w4 = !epi_gate(EPI) && FMLP_DOWN_W4;
-    constexpr int s0n = w4 ? FMLP_DN_WGN : FMLP_S0_WGN, s0m = w4 ? FMLP_DN_WGM : FMLP_S0_WGM;
+    // kS0Wgn x kS0Wgm (measured best for each)
+    constexpr bool w4 = !epi_gate(EPI) && kDownW4;
+    constexpr int s0n = w4 ? kDnWgn : kS0Wgn, s0m = w4 ? kDnWgm : kS0Wgm;
     if (g.shape == 0)
       e = launch_gemm_t<8, 8, s0n, s0m, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
                                                   n_main);
     else if (g.shape == 1)
-      e = launch_gemm_t<8, 4, 4, FMLP_S1_WGM, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
+      e = launch_gemm_t<8, 4, 4, kS1Wgm, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
                                                         n_main);
     else
       e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
   }
   if (e != hipSuccess || g.tail_rows == 0) return e;
-  return launch_gemm_t<8, 4, 4, FMLP_S1_WGM, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream,
+  return launch_gemm_t<8, 4, 4, kS1Wgm, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream,
                                                       n_main, N);
 }
 
@@ -646,13 +625,16 @@ static GemmPlan with_tail(GemmPlan g, int M, int N) {
   return g;
 }
 
-#ifndef FMLP_GEMM_PLAN
-#define FMLP_GEMM_PLAN 0  // 0: by the time model; s*10 + k: shape s, k-way split of the down GEMM
-#endif
+// The down GEMM's plan depends on M only through its 128-token band (every
+// tile height divides 256, so the tile counts are those of the band's top),
+// and above kSplitMaxM tokens, where every shape fills the CUs many times
+// over, it never splits K.
+constexpr int64_t kPlanBand = 128;
+constexpr int64_t kSplitMaxM = 131072;
 
 static GemmPlan plan_down(int64_t M, int64_t d, int64_t ff) {
-  if (FMLP_GEMM_PLAN) return GemmPlan{FMLP_GEMM_PLAN / 10, FMLP_GEMM_PLAN % 10};
-  return plan_gemm((int)M, (int)d, (int)ff, true);
+  const int64_t Mb = (M + kPlanBand - 1) / kPlanBand * kPlanBand;
+  return plan_gemm((int)Mb, (int)d, (int)ff, M <= kSplitMaxM);
 }
 
 // Workspace regions, in order (each 256-byte aligned): n fp16 [pad32(M), d]
@@ -665,7 +647,8 @@ struct PrefillWs {
   uint16_t *wgu16, *wd16;
 };
 
-static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, int splits, size_t* total) {
+static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, size_t part_bytes,
+                            size_t* total) {
   PrefillWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -676,19 +659,42 @@ static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, int sp
   w.n = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * d * 2));
   w.a = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * ff * 2));
   w.r = reinterpret_cast<float*>(take((size_t)M * 4));
-  w.part = reinterpret_cast<float*>(take(splits > 1 ? (size_t)splits * M * d * 4 : 0));
+  w.part = reinterpret_cast<float*>(take(part_bytes));
   w.wgu16 = reinterpret_cast<uint16_t*>(take((size_t)2 * ff * d * 2));
   w.wd16 = reinterpret_cast<uint16_t*>(take((size_t)d * ff * 2));
   *total = off;
   return w;
 }
 
-size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype) {
+static size_t split_partial_bytes(int64_t M, int64_t d, int splits) {
+  return splits > 1 ? (size_t)splits * M * d * 4 : 0;
+}
+
+static size_t ws_total(int64_t M, int64_t d, int64_t ff, int wtype, size_t part_bytes) {
   size_t total = 0;
-  prefill_ws(nullptr, M, d, ff, plan_down(M, d, ff).splits, &total);
+  prefill_ws(nullptr, M, d, ff, part_bytes, &total);
   // (the fp16 expansion of the weights: int4 only)
   if (wtype != 1) total -= align256((size_t)2 * ff * d * 2) + align256((size_t)d * ff * 2);
   return total;
+}
+
+size_t prefill_workspace_bytes(int64_t M, int64_t d, int64_t ff, int wtype) {
+  return ws_total(M, d, ff, wtype, split_partial_bytes(M, d, plan_down(M, d, ff).splits));
+}
+
+// The largest split-partial region over every M' <= M: the plan is constant
+// on each 128-token band, so the partials of a band peak at its top (or at M
+// in the last band). Every other region grows with M.
+size_t prefill_workspace_envelope(int64_t M, int64_t d, int64_t ff, int wtype) {
+  size_t part = 0;
+  const int64_t top = M < kSplitMaxM ? M : kSplitMaxM;
+  for (int64_t b = kPlanBand;; b += kPlanBand) {
+    const int64_t m = b < top ? b : top;
+    const size_t pb = split_partial_bytes(m, d, plan_down(m, d, ff).splits);
+    part = pb > part ? pb : part;
+    if (b >= top) break;
+  }
+  return ws_total(M, d, ff, wtype, part);
 }
 
 template <bool AF16>
@@ -727,7 +733,8 @@ static hipError_t launch_dequant_f16(const uint8_t* q, const uint16_t* s, int64_
 hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   const GemmPlan g2 = plan_down(p.M, p.d, p.ff);
   size_t total = 0;
-  const PrefillWs w = prefill_ws(p.ws, p.M, p.d, p.ff, g2.splits, &total);
+  const PrefillWs w =
+      prefill_ws(p.ws, p.M, p.d, p.ff, split_partial_bytes(p.M, p.d, g2.splits), &total);
   launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
                 p.x, p.eps, w.r, (int)p.M, (int)p.d, p.res);
   const int64_t slots = pad32(p.M) * p.d / 8;

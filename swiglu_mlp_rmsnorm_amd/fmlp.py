@@ -13,9 +13,7 @@ import threading
 
 import torch
 
-# FMLP_LIB selects another build of the same library (e.g. a tuning variant).
-_LIB_PATH = os.environ.get("FMLP_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                       "libfmlp.so")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmlp.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -42,7 +40,8 @@ FMLP_ACT_GELU_TANH = 1
 FMLP_ACT_GELU_ERF = 2
 
 EXPORTS = (
-    "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4", "fmlp_dequant_int4",
+    "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4",
+    "fmlp_pack_int4_interleaved", "fmlp_pack_int4_matrix", "fmlp_dequant_int4",
     "fmlp_convert_f16", "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
     "fmlp_profile_read", "fmlp_kernel_name", "fmlp_read_probe",
@@ -74,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.fmlp_pack_matrix.argtypes = [P, P, I64, I64, P]
         L.fmlp_int4_sizes.argtypes = [I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
         L.fmlp_quantize_int4.argtypes = [P, I64, I64, P, P, P]
+        L.fmlp_pack_int4_interleaved.argtypes = [P, P, P, P, I64, I64, P, P, P]
+        L.fmlp_pack_int4_matrix.argtypes = [P, P, I64, I64, P, P, P]
         L.fmlp_dequant_int4.argtypes = [P, P, I64, I64, P, P]
         L.fmlp_convert_f16.argtypes = [P, P, I64, P]
         L.fmlp_workspace_size.argtypes = [I64, I64, I64, I32]
@@ -94,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.fmlp_kernel_name.argtypes = [I32]
         L.fmlp_kernel_name.restype = ctypes.c_char_p
         for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
-                     "fmlp_quantize_int4", "fmlp_dequant_int4", "fmlp_convert_f16",
+                     "fmlp_quantize_int4", "fmlp_pack_int4_interleaved",
+                     "fmlp_pack_int4_matrix", "fmlp_dequant_int4", "fmlp_convert_f16",
                      "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex", "fmlp_last_hip_error",
                      "fmlp_profile_enable", "fmlp_profile_read"):
             getattr(L, name).restype = ctypes.c_int
@@ -171,33 +173,75 @@ def fmlp_int4_sizes(rows: int, K: int):
 
 
 def fmlp_quantize_int4(w, q=None, scales=None, stream=None):
-    """Tiled bf16 [rows,K] -> (tiled int4 codes uint8, tiled fp16 scales), flat."""
+    """Row-major bf16 [rows, K] -> int4 exchange format: codes uint8
+    [rows, K/2] (even column in the low nibble) and fp16 scales [rows, K/32]."""
     _need(w, torch.bfloat16, "w")
     rows, K = w.shape
-    cb, sb = fmlp_int4_sizes(rows, K)
     if q is None:
-        q = torch.empty(cb, dtype=torch.uint8, device=w.device)
+        q = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty(sb // 2, dtype=torch.float16, device=w.device)
-    if q.numel() < cb or scales.numel() * 2 < sb:
-        raise ValueError("int4 buffers too small")
+        scales = torch.empty((rows, K // 32), dtype=torch.float16, device=w.device)
     _need(q, torch.uint8, "q")
     _need(scales, torch.float16, "scales")
+    if q.shape != (rows, K // 2) or scales.shape != (rows, K // 32):
+        raise ValueError("q must be [rows, K/2] and scales [rows, K/32]")
     _check(lib().fmlp_quantize_int4(_ptr(w), rows, K, _ptr(q), _ptr(scales), _stream(stream)),
            "fmlp_quantize_int4")
     return q, scales
 
 
-def fmlp_dequant_int4(q, scales, rows, K, out=None, stream=None):
-    """Tiled int4 (codes, scales) of a [rows, K] matrix -> exact row-major fp32."""
-    _need(q, torch.uint8, "q")
-    _need(scales, torch.float16, "scales")
+def _need_int4(q, s, name):
+    _need(q, torch.uint8, name + " codes")
+    _need(s, torch.float16, name + " scales")
+    if q.dim() != 2 or s.dim() != 2 or q.shape[0] != s.shape[0] or q.shape[1] != 16 * s.shape[1]:
+        raise ValueError(f"{name}: codes must be [rows, K/2] and scales [rows, K/32]")
+    return q.shape[0], q.shape[1] * 2
+
+
+def _tiled_int4_buffers(rows, K, device, q_tiled, s_tiled):
     cb, sb = fmlp_int4_sizes(rows, K)
-    if q.numel() < cb or scales.numel() * 2 < sb:
-        raise ValueError("int4 buffers too small")
+    if q_tiled is None:
+        q_tiled = torch.empty(cb, dtype=torch.uint8, device=device)
+    if s_tiled is None:
+        s_tiled = torch.empty(sb // 2, dtype=torch.float16, device=device)
+    _need(q_tiled, torch.uint8, "q_tiled")
+    _need(s_tiled, torch.float16, "s_tiled")
+    if q_tiled.numel() < cb or s_tiled.numel() * 2 < sb:
+        raise ValueError("tiled int4 buffers too small")
+    return q_tiled, s_tiled
+
+
+def fmlp_pack_int4_interleaved(q_gate, s_gate, q_up, s_up, q_gu=None, s_gu=None, stream=None):
+    """Exchange-format int4 gate and up [ff, d] -> tiled int4 (flat codes,
+    flat scales) of the interleaved [2ff, d] matrix (gate row i at 2i)."""
+    ff, d = _need_int4(q_gate, s_gate, "gate")
+    if _need_int4(q_up, s_up, "up") != (ff, d):
+        raise ValueError("up shape differs from gate")
+    q_gu, s_gu = _tiled_int4_buffers(2 * ff, d, q_gate.device, q_gu, s_gu)
+    _check(lib().fmlp_pack_int4_interleaved(_ptr(q_gate), _ptr(s_gate), _ptr(q_up), _ptr(s_up),
+                                            ff, d, _ptr(q_gu), _ptr(s_gu), _stream(stream)),
+           "fmlp_pack_int4_interleaved")
+    return q_gu, s_gu
+
+
+def fmlp_pack_int4_matrix(q, scales, q_tiled=None, s_tiled=None, stream=None):
+    """Exchange-format int4 [rows, K] -> tiled int4 (flat codes, flat scales)."""
+    rows, K = _need_int4(q, scales, "matrix")
+    q_tiled, s_tiled = _tiled_int4_buffers(rows, K, q.device, q_tiled, s_tiled)
+    _check(lib().fmlp_pack_int4_matrix(_ptr(q), _ptr(scales), rows, K, _ptr(q_tiled),
+                                       _ptr(s_tiled), _stream(stream)), "fmlp_pack_int4_matrix")
+    return q_tiled, s_tiled
+
+
+def fmlp_dequant_int4(q, scales, out=None, stream=None):
+    """Exchange-format int4 (codes [rows, K/2], scales [rows, K/32]) ->
+    exact row-major fp32 [rows, K]."""
+    rows, K = _need_int4(q, scales, "int4")
     if out is None:
         out = torch.empty((rows, K), dtype=torch.float32, device=q.device)
     _need(out, torch.float32, "out")
+    if out.shape != (rows, K):
+        raise ValueError("out must be [rows, K]")
     _check(lib().fmlp_dequant_int4(_ptr(q), _ptr(scales), rows, K, _ptr(out), _stream(stream)),
            "fmlp_dequant_int4")
     return out
@@ -292,8 +336,9 @@ def fmlp_forward(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, 
     """y = W_down(SiLU(W_gate n) * (W_up n)), n = RMSNorm(x); bf16 x [M,d] -> y [M,d].
 
     bf16 weights: tiled w_gu [2ff,d] (fmlp_pack_interleaved) and tiled w_down
-    [d,ff] (fmlp_pack_matrix); fp16 weights: those after fmlp_convert_f16. int4 weights: the flat tiled code/scale
-    buffers of fmlp_quantize_int4, with ff given explicitly.
+    [d,ff] (fmlp_pack_matrix); fp16 weights: those after fmlp_convert_f16.
+    int4 weights: the flat tiled code/scale buffers of fmlp_pack_int4_interleaved
+    (W_gu) and fmlp_pack_int4_matrix (W_down), with ff given explicitly.
     Output and workspace are allocated with torch when not given.
     """
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,

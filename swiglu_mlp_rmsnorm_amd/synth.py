@@ -9,9 +9,11 @@ two sides see bit-identical inputs.
 Workloads (synthetic stand-ins for the models the pages measure: Phi-3-mini,
 Llama-3.1-8B and Llama-70B shaped layers; no checkpoint or dataset is used):
   x ~ N(0,1), gamma = 1 + N(0,0.1), W_gate / W_up / W_down ~ N(0,0.02), all
-  rounded to bf16 (RNE); eps = 1e-5. int4 layers: every packed byte uniform in
-  [0,255], i.e. both nibbles uniform over the 16 two's-complement values
-  [-8,7]; scales ~ U(0.005,0.02) rounded to fp16.
+  rounded to bf16 (RNE); eps = 1e-5. int4 layers, in the row-major exchange
+  format (codes [rows, K/2], scales [rows, K/32]): every packed byte uniform
+  in [0,255], i.e. both nibbles uniform over the 16 two's-complement values
+  [-8,7]; scales ~ U(0.005,0.02) rounded to fp16. Gate, up and down are
+  drawn separately, as bf16 layers are.
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import torch
 EPS = 1e-5
 
 # tensor ids inside one layer's seed space
-T_X, T_GAMMA, T_WGATE, T_WUP, T_WDOWN, T_QGU, T_SGU, T_QD, T_SD = range(9)
+T_X, T_GAMMA, T_WGATE, T_WUP, T_WDOWN, T_QGATE, T_SGATE, T_QD, T_SD, T_QUP, T_SUP = range(11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -88,22 +90,12 @@ def bf16_weight(rows: int, cols: int, seed: int, device="cpu", std: float = 0.02
     return normal_bf16((rows, cols), 0.0, std, seed, device)
 
 
-def int4_tiled_sizes(rows: int, K: int):
-    """(code bytes, scale count) of the library's tiled int4 storage of a
-    [rows, K] matrix: 1024-byte super-tiles of 16 rows x 4 groups of 32."""
-    nq = (K + 127) // 128
-    return (rows // 16) * nq * 1024, (rows // 16) * nq * 64
-
-
 def int4_weight(rows: int, K: int, seed_q: int, seed_s: int, device="cpu"):
-    """Flat tiled int4 codes (uniform bytes) and flat fp16 scales ~U(0.005, 0.02).
-
-    Every byte is uniform, so every code is uniform over [-8, 7] whatever the
-    storage order; slots of padding groups (K not a multiple of 128) hold
-    random values that no consumer reads.
-    """
-    nb, ns = int4_tiled_sizes(rows, K)
-    return uniform_bytes((nb,), seed_q, device), uniform_f16((ns,), 0.005, 0.02, seed_s, device)
+    """Row-major int4 in the exchange format: codes uint8 [rows, K/2] (uniform
+    bytes, so every code is uniform over [-8, 7]) and fp16 scales
+    [rows, K/32] ~ U(0.005, 0.02)."""
+    return (uniform_bytes((rows, K // 2), seed_q, device),
+            uniform_f16((rows, K // 32), 0.005, 0.02, seed_s, device))
 
 
 def layer_bf16(w: Workload, layer: int, device="cpu"):
@@ -115,12 +107,13 @@ def layer_bf16(w: Workload, layer: int, device="cpu"):
 
 
 def layer_int4(w: Workload, layer: int, device="cpu"):
-    """Tiled int4 (q_gu, s_gu) of the logical [2ff, d] gate/up matrix (drawn
-    directly in interleaved row order) and (q_down, s_down) of [d, ff]."""
+    """Row-major int4 (codes, scales) of W_gate [ff, d], W_up [ff, d] and
+    W_down [d, ff]: (q_gate, s_gate, q_up, s_up, q_down, s_down)."""
     s = lambda t: seed_of(w.index, layer, t)
-    q_gu, s_gu = int4_weight(2 * w.ff, w.d, s(T_QGU), s(T_SGU), device)
+    q_g, s_g = int4_weight(w.ff, w.d, s(T_QGATE), s(T_SGATE), device)
+    q_u, s_u = int4_weight(w.ff, w.d, s(T_QUP), s(T_SUP), device)
     q_d, s_d = int4_weight(w.d, w.ff, s(T_QD), s(T_SD), device)
-    return q_gu, s_gu, q_d, s_d
+    return q_g, s_g, q_u, s_u, q_d, s_d
 
 
 def inputs(w: Workload, M: int, device="cpu", layer: int = 0):

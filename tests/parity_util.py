@@ -16,6 +16,56 @@ from swiglu_mlp_rmsnorm_amd import synth
 MAX_REL_TOL = 2e-2
 L1_REL_TOL = 3e-3
 
+# Guard regions: every output and scratch buffer the helpers below hand to
+# the library sits inside a larger allocation whose GUARD bytes before and
+# after it hold a sentinel; a write outside the buffer changes them.
+GUARD = 256
+SENTINEL = 0x5A
+
+
+class Guarded:
+    """A device buffer of `nbytes` with sentinel guards on both sides; its
+    interior starts as 0xFF bytes (NaN for bf16 and fp32)."""
+
+    def __init__(self, nbytes, device="cuda"):
+        self.n = int(nbytes)
+        self.buf = torch.full((self.n + 2 * GUARD,), SENTINEL, dtype=torch.uint8, device=device)
+        self.buf[GUARD:GUARD + self.n] = 0xFF
+
+    def bytes(self):
+        return self.buf[GUARD:GUARD + self.n]
+
+    def bf16(self, *shape):
+        return self.bytes().view(torch.bfloat16).view(*shape)
+
+    def check(self, what):
+        lo, hi = self.buf[:GUARD], self.buf[GUARD + self.n:]
+        assert torch.all(lo == SENTINEL) and torch.all(hi == SENTINEL), \
+            f"{what}: a write landed outside the buffer"
+
+
+def guarded_call(fn, M, d, ff, wtype, with_h=False, **kw):
+    """Run fn(..., y=, workspace=[, h_out=]) on guarded buffers (unless the
+    caller passed its own), then check every guard."""
+    guards = []
+    if kw.get("y") is None:
+        g = Guarded(M * d * 2)
+        kw["y"] = g.bf16(M, d)
+        guards.append(("y", g))
+    if kw.get("workspace") is None:
+        g = Guarded(max(F.fmlp_workspace_size(M, d, ff, wtype), 1))
+        kw["workspace"] = g.bytes()
+        guards.append(("workspace", g))
+    if with_h and kw.get("h_out") is None:
+        g = Guarded(M * d * 2)
+        kw["h_out"] = g.bf16(M, d)
+        guards.append(("h_out", g))
+    out = fn(**kw)
+    torch.cuda.synchronize()
+    for what, g in guards:
+        g.check(what)
+    return out
+
 
 def errors(y_gpu: torch.Tensor, y_ref: np.ndarray):
     y = y_gpu.detach().float().cpu().double().numpy()
@@ -50,8 +100,11 @@ class Bf16Layer:
         wg, wu, wd = self.host
         return oracle.forward_unfused(synth.bits(x), synth.bits(g), eps, wg, wu, wd)
 
+    wtype = F.FMLP_W_BF16
+
     def forward(self, x, g, eps, **kw):
-        return F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **k),
+                            x.shape[0], self.d, self.ff, self.wtype, **kw)
 
     def oracle_ex(self, x, g, eps, act, res):
         wg, wu, wd = self.host
@@ -59,35 +112,47 @@ class Bf16Layer:
                                          residual=None if res is None else synth.bits(res))
 
     def forward_ex(self, x, g, eps, **kw):
-        return F.fmlp_forward_ex(x, g, eps, self.wgu_t, self.wd_t, **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_ex(x, g, eps, self.wgu_t, self.wd_t, **k),
+                            x.shape[0], self.d, self.ff, self.wtype,
+                            with_h=kw.get("residual") is not None, **kw)
 
 
 class Int4Layer:
-    """Synthetic tiled int4 weights; the oracle untiles the same seeded bytes."""
+    """Synthetic int4 weights in the row-major exchange format (gate, up and
+    down drawn separately), packed to the tiled layout by the library; the
+    oracle interleaves the same seeded rows itself."""
 
     def __init__(self, d, ff, seed, device="cuda"):
         self.d, self.ff = d, ff
-        self.q_gu, self.s_gu = synth.int4_weight(2 * ff, d, seed, seed + 1, device)
-        self.q_d, self.s_d = synth.int4_weight(d, ff, seed + 2, seed + 3, device)
+        self.q_g, self.s_g = synth.int4_weight(ff, d, seed, seed + 1, device)
+        self.q_u, self.s_u = synth.int4_weight(ff, d, seed + 4, seed + 5, device)
+        self.q_dn, self.s_dn = synth.int4_weight(d, ff, seed + 2, seed + 3, device)
+        self.q_gu, self.s_gu = F.fmlp_pack_int4_interleaved(self.q_g, self.s_g, self.q_u, self.s_u)
+        self.q_d, self.s_d = F.fmlp_pack_int4_matrix(self.q_dn, self.s_dn)
         b = synth.bits
-        q_gu, s_gu = oracle.untile_int4(b(self.q_gu), b(self.s_gu), 2 * ff, d)
-        q_d, s_d = oracle.untile_int4(b(self.q_d), b(self.s_d), d, ff)
-        self.host = (q_gu, s_gu, q_d, s_d)
+        q_gu, s_gu = oracle.pack_interleaved_int4(b(self.q_g), b(self.s_g), b(self.q_u),
+                                                  b(self.s_u))
+        self.host = (q_gu, s_gu, b(self.q_dn), b(self.s_dn))
 
     def oracle(self, x, g, eps):
         return oracle.forward_int4(synth.bits(x), synth.bits(g), eps, *self.host)
 
+    wtype = F.FMLP_W_INT4_G32
+
     def forward(self, x, g, eps, **kw):
-        return F.fmlp_forward_path(x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d,
-                                   ff=self.ff, **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_path(
+            x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d, ff=self.ff, **k),
+            x.shape[0], self.d, self.ff, self.wtype, **kw)
 
     def oracle_ex(self, x, g, eps, act, res):
         return oracle.forward_int4_ex(synth.bits(x), synth.bits(g), eps, *self.host, act=act,
                                       residual=None if res is None else synth.bits(res))
 
     def forward_ex(self, x, g, eps, **kw):
-        return F.fmlp_forward_ex(x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d, ff=self.ff,
-                                 **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_ex(
+            x, g, eps, self.q_gu, self.q_d, self.s_gu, self.s_d, ff=self.ff, **k),
+            x.shape[0], self.d, self.ff, self.wtype, with_h=kw.get("residual") is not None,
+            **kw)
 
 
 def bf16_inputs(M, d, seed, device="cuda"):
@@ -112,14 +177,17 @@ class F16Layer(Bf16Layer):
         return oracle.forward_f16_ex(synth.bits(x), synth.bits(g), eps, *self.host16)[0]
 
     def forward(self, x, g, eps, **kw):
-        return F.fmlp_forward_path(x, g, eps, self.hgu_t, self.hd_t, **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_path(x, g, eps, self.hgu_t, self.hd_t, **k),
+                            x.shape[0], self.d, self.ff, F.FMLP_W_F16, **kw)
 
     def oracle_ex(self, x, g, eps, act, res):
         return oracle.forward_f16_ex(synth.bits(x), synth.bits(g), eps, *self.host16, act=act,
                                      residual=None if res is None else synth.bits(res))
 
     def forward_ex(self, x, g, eps, **kw):
-        return F.fmlp_forward_ex(x, g, eps, self.hgu_t, self.hd_t, **kw)
+        return guarded_call(lambda **k: F.fmlp_forward_ex(x, g, eps, self.hgu_t, self.hd_t, **k),
+                            x.shape[0], self.d, self.ff, F.FMLP_W_F16,
+                            with_h=kw.get("residual") is not None, **kw)
 
     def forward_bf16(self, x, g, eps, **kw):
-        return F.fmlp_forward_path(x, g, eps, self.wgu_t, self.wd_t, **kw)
+        return Bf16Layer.forward(self, x, g, eps, **kw)

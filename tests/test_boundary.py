@@ -79,6 +79,11 @@ def fwd(M=1, d=256, ff=704, eps=1e-5, wtype=0, path=0, ws_bytes=BIG, **over):
     (dict(y=A["x"]), F.FMLP_ERR_INVALID_ARG),
     (dict(y=A["ws"]), F.FMLP_ERR_INVALID_ARG),
     (dict(ws=A["wd"]), F.FMLP_ERR_INVALID_ARG),
+    # a workspace over the int4 scales (which the kernels read while they
+    # write the workspace)
+    (dict(wtype=1, ws=A["sgu"]), F.FMLP_ERR_INVALID_ARG),
+    (dict(wtype=1, ws=A["sd"]), F.FMLP_ERR_INVALID_ARG),
+    (dict(wtype=1, ws=ctypes.c_void_p((4 << 36) - 4096)), F.FMLP_ERR_INVALID_ARG),
 ])
 def test_forward_rejects_before_any_hip_call(kw, status):
     assert fwd(**kw) == status
@@ -189,21 +194,75 @@ def test_workspace_size():
                path=F.FMLP_PATH_SINGLE_PASS) == F.FMLP_ERR_WORKSPACE
 
 
+SHAPES = [(256, 704), (3072, 8192), (4096, 14336), (8192, 28672), (1024, 2048), (32, 3104),
+          (96, 6176), (4128, 64)]
+
+
+@pytest.mark.parametrize("d,ff", SHAPES)
+@pytest.mark.parametrize("wtype", [0, 1, 2])
+def test_workspace_size_never_decreases(d, ff, wtype):
+    # a buffer sized for the largest M serves every smaller M, on every path
+    ws = F.fmlp_workspace_size
+    sizes = [ws(M, d, ff, wtype) for M in range(0, 4097)]
+    for M in range(1, 4097):
+        assert sizes[M] >= sizes[M - 1], (d, ff, wtype, M, sizes[M - 1], sizes[M])
+    # and each size passes the forward's own check on every path it can take
+    for M in (1, 8, 31, 32, 33, 257, 258, 1000, 4096):
+        for path in (0, 1, 2, 3):
+            st = fwd(M=M, d=d, ff=ff, wtype=wtype, path=path, ws_bytes=sizes[4096])
+            assert st != F.FMLP_ERR_WORKSPACE, (d, ff, wtype, M, path)
+            st = fwd(M=M, d=d, ff=ff, wtype=wtype, path=path, ws_bytes=sizes[M])
+            assert st != F.FMLP_ERR_WORKSPACE, (d, ff, wtype, M, path)
+
+
 def test_pack_quant_dequant_validation():
     L = F.lib()
-    a, b, c = A["x"], A["g"], A["y"]
+    a, b, c, e = A["x"], A["g"], A["y"], A["ws"]
     assert L.fmlp_pack_interleaved(None, b, c, 704, 256, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_pack_interleaved(a, b, c, 704, 250, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
     assert L.fmlp_pack_interleaved(a, b, ctypes.c_void_p(A["y"].value + 2), 704, 256,
                                    None) == F.FMLP_ERR_ALIGNMENT
     assert L.fmlp_pack_interleaved(a, b, a, 704, 256, None) == F.FMLP_ERR_INVALID_ARG
+    # quantiser: row-major, any row count, K a multiple of 32
     assert L.fmlp_quantize_int4(a, 16, 48, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
-    assert L.fmlp_quantize_int4(a, 8, 64, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_quantize_int4(a, 0, 64, b, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
     assert L.fmlp_quantize_int4(a, 16, 64, None, c, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_quantize_int4(a, 16, 64, a, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_quantize_int4(a, 16, 64, b, ctypes.c_void_p(A["x"].value + 512),
+                                None) == F.FMLP_ERR_INVALID_ARG  # scales over w
+    assert L.fmlp_quantize_int4(a, 16, 64, b, ctypes.c_void_p(A["g"].value + 256),
+                                None) == F.FMLP_ERR_INVALID_ARG  # scales over q
+    assert L.fmlp_quantize_int4(a, 8, 64, b, ctypes.c_void_p(A["g"].value + 8),
+                                None) == F.FMLP_ERR_ALIGNMENT
+    # dequant: row-major in, any row count
     assert L.fmlp_dequant_int4(a, b, 0, 64, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_dequant_int4(a, b, 16, 48, c, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
     assert L.fmlp_dequant_int4(a, b, 16, 64, ctypes.c_void_p(A["y"].value + 4),
                                None) == F.FMLP_ERR_ALIGNMENT
+    assert L.fmlp_dequant_int4(a, b, 16, 64, ctypes.c_void_p(A["x"].value + 256),
+                               None) == F.FMLP_ERR_INVALID_ARG  # out over q
+    # int4 packers: the tiled outputs need 16-row blocks
+    assert L.fmlp_pack_int4_matrix(a, b, 24, 64, c, e, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_pack_int4_matrix(a, b, 16, 48, c, e, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_pack_int4_matrix(None, b, 16, 64, c, e, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_matrix(a, b, 16, 64, c, c, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_matrix(a, b, 16, 64, a, e, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_matrix(a, b, 16, 64, c, b, None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_matrix(a, b, 16, 64, c, ctypes.c_void_p(A["ws"].value + 2),
+                                   None) == F.FMLP_ERR_ALIGNMENT
+    g2, u1, u2 = A["sgu"], A["wd"], A["sd"]
+    assert L.fmlp_pack_int4_interleaved(a, b, u1, u2, 704, 250, c, e,
+                                        None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert L.fmlp_pack_int4_interleaved(a, b, u1, None, 704, 256, c, e,
+                                        None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_interleaved(a, b, u1, u2, 704, 256, u1, e,
+                                        None) == F.FMLP_ERR_INVALID_ARG  # codes over up
+    assert L.fmlp_pack_int4_interleaved(a, b, u1, u2, 704, 256, c, b,
+                                        None) == F.FMLP_ERR_INVALID_ARG  # scales over gate's
+    assert L.fmlp_pack_int4_interleaved(a, b, u1, u2, 704, 256, c, c,
+                                        None) == F.FMLP_ERR_INVALID_ARG
+    assert L.fmlp_pack_int4_interleaved(a, g2, u1, u2, 704, 256, c, ctypes.c_void_p(
+        A["ws"].value + 8), None) == F.FMLP_ERR_ALIGNMENT
     assert L.fmlp_pack_matrix(a, None, 16, 64, None) == F.FMLP_ERR_INVALID_ARG
     assert L.fmlp_pack_matrix(a, c, 24, 64, None) == F.FMLP_ERR_UNSUPPORTED_SHAPE
     assert L.fmlp_pack_matrix(a, a, 16, 64, None) == F.FMLP_ERR_INVALID_ARG

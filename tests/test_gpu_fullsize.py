@@ -1,7 +1,15 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times (fmlp_forward, automatic path choice, weight set 0 of each workload).
-Rows are independent, so the oracle runs on a sample of rows and the error
-bar is evaluated over those rows."""
+times (fmlp_forward, automatic path choice, a workspace of
+fmlp_workspace_size bytes, weight sets 0 and the last rotated one).
+
+The accuracy bar is evaluated over the whole [M, d] output of every
+configured (workload, M): the oracle (OpenMP over outputs) runs on all rows on
+the host once the GPU result has been copied back. Only int4 weights on the
+prefill path at M = 512 and 2048, beyond the workloads' own token counts,
+are checked on one sampled row per 64-token block at the full 70B shape
+(the fp64 oracle needs about 0.2 s per row there); the same path is checked
+on all rows at M = 64 at that shape, and at M = 512 / 2048 on a smaller
+layer (test_prefill_int4_large_m in test_gpu_parity.py)."""
 import numpy as np
 import pytest
 import torch
@@ -14,65 +22,93 @@ from parity_util import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-CASES = [
-    ("phi3mini_decode_d3072_ff8192", 1), ("phi3mini_decode_d3072_ff8192", 8),
-    ("llama8b_decode_d4096_ff14336", 1), ("llama8b_decode_d4096_ff14336", 4),
-    ("llama8b_decode_d4096_ff14336", 16), ("llama8b_decode_d4096_ff14336", 32),
-    ("llama8b_prefill_d4096_ff14336", 512), ("llama8b_prefill_d4096_ff14336", 2048),
-    ("llama70b_int4_decode_d8192_ff28672", 1), ("llama70b_int4_decode_d8192_ff28672", 16),
-    # int4 weights on the prefill path (beyond the workload's own M values)
-    ("llama70b_int4_decode_d8192_ff28672", 64),
-]
-
-
-def sample_rows(M, n):
-    if M <= n:
-        return list(range(M))
-    return sorted(set(int(r) for r in np.linspace(0, M - 1, n)))
-
-
-# the last of each decode workload's rotated weight sets as well as the first
-LAST_SET_CASES = [(n, 1, synth.WORKLOADS[n].sets - 1) for n in (
+# every (workload, M) the workloads configure, on weight set 0
+CASES = [(name, M, 0) for name, w in synth.WORKLOADS.items() for M in w.Ms]
+# the last of each decode workload's rotated weight sets as well
+CASES += [(n, 1, synth.WORKLOADS[n].sets - 1) for n in (
     "phi3mini_decode_d3072_ff8192", "llama8b_decode_d4096_ff14336",
     "llama70b_int4_decode_d8192_ff28672")]
+# int4 weights on the prefill path at the 70B shape, all rows
+CASES += [("llama70b_int4_decode_d8192_ff28672", 64, 0)]
 
 
-@pytest.mark.parametrize("wname,M,layer", [(n, M, 0) for n, M in CASES] + LAST_SET_CASES)
-def test_full_size_parity(wname, M, layer):
+class FullLayer:
+    """One weight set of a workload: device copies packed by the library, and
+    the host bits of the same seeded tensors for the oracle."""
+
+    def __init__(self, w, layer):
+        self.w = w
+        b = synth.bits
+        if w.wtype == "int4":
+            qg, sg, qu, su, qd, sd = synth.layer_int4(w, layer, "cuda")
+            self.dev = (*F.fmlp_pack_int4_interleaved(qg, sg, qu, su),
+                        *F.fmlp_pack_int4_matrix(qd, sd))
+            q_gu, s_gu = oracle.pack_interleaved_int4(b(qg), b(sg), b(qu), b(su))
+            self.host = (q_gu, s_gu, b(qd), b(sd))
+        else:
+            wg, wu, wd = synth.layer_bf16(w, layer, "cuda")
+            self.dev = (F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
+            self.host = (b(wg), b(wu), b(wd))
+
+    def forward(self, x, g):
+        w = self.w
+        wt = F.FMLP_W_INT4_G32 if w.wtype == "int4" else F.FMLP_W_BF16
+        ws = torch.empty(F.fmlp_workspace_size(x.shape[0], w.d, w.ff, wt), dtype=torch.uint8,
+                         device="cuda")
+        if w.wtype == "int4":
+            q_gu, s_gu, q_d, s_d = self.dev
+            return F.fmlp_forward(x, g, synth.EPS, q_gu, q_d, s_gu, s_d, ff=w.ff, workspace=ws)
+        return F.fmlp_forward(x, g, synth.EPS, *self.dev, workspace=ws)
+
+    def oracle(self, xb, gb):
+        if self.w.wtype == "int4":
+            return oracle.forward_int4(xb, gb, synth.EPS, *self.host)
+        return oracle.forward_unfused(xb, gb, synth.EPS, *self.host)
+
+
+@pytest.mark.parametrize("wname,M,layer", CASES)
+def test_full_size_parity_all_rows(wname, M, layer):
     w = synth.WORKLOADS[wname]
+    print(f"[fullsize] {wname} M={M} set {layer}: GPU forward", flush=True)
+    L = FullLayer(w, layer)
     x, g = synth.inputs(w, M, "cuda", layer=layer)
-    b = synth.bits
-    if w.wtype == "int4":
-        q_gu, s_gu, q_d, s_d = synth.layer_int4(w, layer, "cuda")
-        y = F.fmlp_forward(x, g, synth.EPS, q_gu, q_d, s_gu, s_d, ff=w.ff)
-        rows = sample_rows(M, 2)
-        host = (*oracle.untile_int4(b(q_gu), b(s_gu), 2 * w.ff, w.d),
-                *oracle.untile_int4(b(q_d), b(s_d), w.d, w.ff))
-        ref = oracle.forward_int4(b(x)[rows], b(g), synth.EPS, *host)
-    else:
-        wg, wu, wd = synth.layer_bf16(w, layer, "cuda")
-        y = F.fmlp_forward(x, g, synth.EPS, F.fmlp_pack_interleaved(wg, wu), F.fmlp_pack_matrix(wd))
-        rows = sample_rows(M, 8 if M <= 32 else 4)
-        ref = oracle.forward_unfused(b(x)[rows], b(g), synth.EPS, b(wg), b(wu), b(wd))
+    y = L.forward(x, g)
+    torch.cuda.synchronize()
+    print(f"[fullsize] {wname} M={M}: oracle on all {M} rows", flush=True)
+    ref = L.oracle(synth.bits(x), synth.bits(g))
+    mx, l1 = assert_parity(y, ref, f"{wname} M={M} set {layer} (all rows)")
+    print(f"[fullsize] {wname} M={M} set {layer}: max/rms={mx:.3e} L1={l1:.3e}", flush=True)
+
+
+def block_rows(M, block=64):
+    """One row per `block`-token block, at varying offsets inside the blocks."""
+    return [min(M - 1, b * block + (b * 37) % block) for b in range((M + block - 1) // block)]
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+def test_full_size_int4_prefill_sampled_rows(M):
+    w = synth.WORKLOADS["llama70b_int4_decode_d8192_ff28672"]
+    L = FullLayer(w, 0)
+    x, g = synth.inputs(w, M, "cuda")
+    y = L.forward(x, g)
     torch.cuda.synchronize()
     assert torch.all(torch.isfinite(y.float()))
-    mx, l1 = assert_parity(y[rows], ref, f"{wname} M={M} set {layer}")
-    print(f"{wname} M={M} set {layer} rows={rows}: max/rms={mx:.3e} L1={l1:.3e}")
+    rows = block_rows(M)
+    print(f"[fullsize] 70B int4 prefill M={M}: oracle on rows {rows}", flush=True)
+    ref = L.oracle(synth.bits(x)[rows], synth.bits(g))
+    mx, l1 = assert_parity(y[rows], ref, f"70B int4 prefill M={M} rows {rows}")
+    print(f"[fullsize] 70B int4 prefill M={M}: max/rms={mx:.3e} L1={l1:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("wname,M", [("phi3mini_decode_d3072_ff8192", 1),
                                      ("phi3mini_decode_d3072_ff8192", 8),
                                      ("llama8b_decode_d4096_ff14336", 1),
                                      ("llama8b_decode_d4096_ff14336", 4)])
-def test_full_size_single_pass(wname, M):
+def test_full_size_single_pass_all_rows(wname, M):
     w = synth.WORKLOADS[wname]
+    L = FullLayer(w, 0)
     x, g = synth.inputs(w, M, "cuda")
-    b = synth.bits
-    wg, wu, wd = synth.layer_bf16(w, 0, "cuda")
-    y = F.fmlp_forward_path(x, g, synth.EPS, F.fmlp_pack_interleaved(wg, wu),
-                            F.fmlp_pack_matrix(wd), path=F.FMLP_PATH_SINGLE_PASS)
-    rows = sample_rows(M, 8)
-    ref = oracle.forward_unfused(b(x)[rows], b(g), synth.EPS, b(wg), b(wu), b(wd))
+    y = F.fmlp_forward_path(x, g, synth.EPS, *L.dev, path=F.FMLP_PATH_SINGLE_PASS)
     torch.cuda.synchronize()
-    mx, l1 = assert_parity(y[rows], ref, f"single pass {wname} M={M}")
-    print(f"single pass {wname} M={M}: max/rms={mx:.3e} L1={l1:.3e}")
+    mx, l1 = assert_parity(y, L.oracle(synth.bits(x), synth.bits(g)), f"single pass {wname} M={M}")
+    print(f"[fullsize] single pass {wname} M={M}: max/rms={mx:.3e} L1={l1:.3e}", flush=True)

@@ -46,63 +46,82 @@ def test_pack_matrix_bit_exact(R, K):
 
 # ----------------------------------------------------------------- int4
 
-def _quantize_both(w_rowmajor):
-    """GPU: tile then quantise. Oracle: quantise row-major, then tile."""
-    R, K = w_rowmajor.shape
-    q, s = F.fmlp_quantize_int4(F.fmlp_pack_matrix(w_rowmajor))
-    st, q_ref, s_ref = oracle.quantize_int4(synth.bits(w_rowmajor))
-    assert st == 0
-    qt_ref, st_ref = oracle.tile_int4(q_ref, s_ref)
-    return (synth.bits(q), synth.bits(s)), (qt_ref, st_ref)
-
-
-@pytest.mark.parametrize("R,K", [(96, 704), (16, 128), (64, 4096)])
+@pytest.mark.parametrize("R,K", [(96, 704), (16, 128), (64, 4096), (5, 64), (1, 32)])
 def test_quantize_bit_exact(R, K):
+    # row-major in and out (the exchange format), any row count
     w = synth.bf16_weight(R, K, 5, "cuda")
-    # exact ties (w/s = +-k.5), an all-zero group, a ramp
-    ties = torch.tensor([0.875, 0.3125, -0.3125, 0.1875, -0.875, 0.0625] + [0.0] * 26)
-    w[3, 0:32] = ties.to(torch.bfloat16).cuda()
-    w[4, 32:64] = 0
-    w[5, 64:96] = torch.linspace(-3, 3, 32).to(torch.bfloat16).cuda()
-    (q, s), (q_ref, s_ref) = _quantize_both(w)
-    assert np.array_equal(q, q_ref)
-    assert np.array_equal(s, s_ref)
+    if R > 5:
+        # exact ties (w/s = +-k.5), an all-zero group, a ramp
+        ties = torch.tensor([0.875, 0.3125, -0.3125, 0.1875, -0.875, 0.0625] + [0.0] * 26)
+        w[3, 0:32] = ties.to(torch.bfloat16).cuda()
+        w[4, 32:64] = 0
+        w[5, 64:96] = torch.linspace(-3, 3, 32).to(torch.bfloat16).cuda()
+    q, s = F.fmlp_quantize_int4(w)
+    st, q_ref, s_ref = oracle.quantize_int4(synth.bits(w))
+    assert st == 0
+    assert np.array_equal(synth.bits(q), q_ref)
+    assert np.array_equal(synth.bits(s), s_ref)
 
 
 def test_quantize_commutes_with_interleave():
+    # quantising the row-interleaved matrix = interleaving the quantised rows
     wg = synth.bf16_weight(64, 256, 6, "cuda")
     wu = synth.bf16_weight(64, 256, 7, "cuda")
-    q1, s1 = F.fmlp_quantize_int4(F.fmlp_pack_interleaved(wg, wu))
-    st, qg, sg = oracle.quantize_int4(synth.bits(wg))
-    st2, qu, su = oracle.quantize_int4(synth.bits(wu))
-    q_il = np.empty((128, 128), np.uint8)
-    s_il = np.empty((128, 8), np.uint16)
-    q_il[0::2], q_il[1::2], s_il[0::2], s_il[1::2] = qg, qu, sg, su
-    qt, stt = oracle.tile_int4(q_il, s_il)
-    assert np.array_equal(synth.bits(q1), qt) and np.array_equal(synth.bits(s1), stt)
+    w_il = torch.empty((128, 256), dtype=torch.bfloat16, device="cuda")
+    w_il[0::2], w_il[1::2] = wg, wu
+    q1, s1 = F.fmlp_quantize_int4(w_il)
+    (qg, sg), (qu, su) = F.fmlp_quantize_int4(wg), F.fmlp_quantize_int4(wu)
+    assert torch.equal(q1[0::2], qg) and torch.equal(q1[1::2], qu)
+    assert torch.equal(s1[0::2].view(torch.int16), sg.view(torch.int16))
+    assert torch.equal(s1[1::2].view(torch.int16), su.view(torch.int16))
+    # and the tiled forms agree: pack_int4_interleaved(gate, up) == pack_int4_matrix(interleaved)
+    a = F.fmlp_pack_int4_interleaved(qg, sg, qu, su)
+    b = F.fmlp_pack_int4_matrix(q1, s1)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
 
 
 def test_quantize_range_error():
-    w = F.fmlp_pack_matrix(torch.full((16, 64), 1e6, dtype=torch.bfloat16, device="cuda"))
+    w = torch.full((16, 64), 1e6, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(F.FmlpError) as e:
         F.fmlp_quantize_int4(w)
     assert e.value.status == F.FMLP_ERR_RANGE
     w = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     w[1, 5] = float("nan")
     with pytest.raises(F.FmlpError):
-        F.fmlp_quantize_int4(F.fmlp_pack_matrix(w))
+        F.fmlp_quantize_int4(w)
     # a later valid call works again (the flag is reset per call)
     q, s = F.fmlp_quantize_int4(torch.ones((16, 128), dtype=torch.bfloat16, device="cuda"))
     assert torch.all(s == torch.tensor(1.0 / 7).half().cuda())
 
 
-@pytest.mark.parametrize("R,K", [(48, 704), (8192, 1024)])
+@pytest.mark.parametrize("R,K", [(48, 704), (8192, 1024), (3, 96)])
 def test_dequant_bit_exact(R, K):
     q, s = synth.int4_weight(R, K, 11, 12, "cuda")
-    got = F.fmlp_dequant_int4(q, s, R, K)
-    q_rm, s_rm = oracle.untile_int4(synth.bits(q), synth.bits(s), R, K)
-    ref = oracle.dequant_int4(q_rm, s_rm)
+    got = F.fmlp_dequant_int4(q, s)
+    ref = oracle.dequant_int4(synth.bits(q), synth.bits(s))
     assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("R,K", [(16, 32), (48, 704), (64, 4096), (8192, 28672)])
+def test_pack_int4_matrix_bit_exact(R, K):
+    # K = 704 and 32 leave padding groups in the last super-tile: zero codes and scales
+    q, s = synth.int4_weight(R, K, 13, 14, "cuda")
+    qt, st = F.fmlp_pack_int4_matrix(q, s)
+    qt_ref, st_ref = oracle.tile_int4(synth.bits(q), synth.bits(s))
+    assert np.array_equal(synth.bits(qt), qt_ref)
+    assert np.array_equal(synth.bits(st), st_ref)
+
+
+@pytest.mark.parametrize("ff,d", [(32, 32), (704, 256), (28672, 8192)])
+def test_pack_int4_interleaved_bit_exact(ff, d):
+    qg, sg = synth.int4_weight(ff, d, 15, 16, "cuda")
+    qu, su = synth.int4_weight(ff, d, 17, 18, "cuda")
+    qt, st = F.fmlp_pack_int4_interleaved(qg, sg, qu, su)
+    b = synth.bits
+    q_il, s_il = oracle.pack_interleaved_int4(b(qg), b(sg), b(qu), b(su))
+    qt_ref, st_ref = oracle.tile_int4(q_il, s_il)
+    assert np.array_equal(synth.bits(qt), qt_ref)
+    assert np.array_equal(synth.bits(st), st_ref)
 
 
 # ----------------------------------------------------------------- forward bf16
@@ -272,11 +291,23 @@ def test_prefill_int4_shapes(d, ff, M):
     assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 prefill d={d} ff={ff}")
 
 
+@pytest.mark.parametrize("M", [512, 2048])
+def test_prefill_int4_large_m(M):
+    # the int4 prefill path at the token counts of the prefill workload, all
+    # rows, on a layer small enough for the oracle (8 x 28 weight row bands)
+    layer = Int4Layer(1024, 3584, 57)
+    x, g = bf16_inputs(M, 1024, 860 + M)
+    assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 prefill M={M}")
+
+
 def test_int4_end_to_end_from_bf16(tiny):
-    # quantise with the library; the oracle quantises the same seeded bf16
-    # weights itself and runs Eq(1) on its own codes
-    q_gu, s_gu = F.fmlp_quantize_int4(tiny.wgu_t)
-    q_d, s_d = F.fmlp_quantize_int4(tiny.wd_t)
+    # quantise gate, up and down with the library in the exchange format,
+    # pack, run; the oracle quantises the same seeded bf16 weights itself
+    # and runs Eq(1) on its own codes
+    (qg, sg), (qu, su) = F.fmlp_quantize_int4(tiny.wg), F.fmlp_quantize_int4(tiny.wu)
+    qd, sd = F.fmlp_quantize_int4(tiny.wd)
+    q_gu, s_gu = F.fmlp_pack_int4_interleaved(qg, sg, qu, su)
+    q_d, s_d = F.fmlp_pack_int4_matrix(qd, sd)
     wg, wu, wd = tiny.host
     _, qg_o, sg_o = oracle.quantize_int4(oracle.pack_interleaved(wg, wu))
     _, qd_o, sd_o = oracle.quantize_int4(wd)

@@ -32,7 +32,10 @@ MUTATIONS = {
     "f16_sign_dropped": ("out[i] = (uint16_t)((w[i] & 0x8000u) | bits);", "out[i] = bits;"),
     "f16_exponent_bias": ("(((e2 - 1 + 15) << 10)", "(((e2 - 1 + 16) << 10)"),
     "f16_range_one_binade_high": ("a > 65504.0", "a > 65536.0"),
-    "f16_weights_read_as_bf16": ("if (kind == 2) return f16_value(", "if (kind == 2) return bf16_value("),
+    "f16_weights_read_as_bf16": ("if (kind == 2) return f16[bf[row * K + k]];",
+                                 "if (kind == 2) return bf16_value(bf[row * K + k]);"),
+    "int4_scale_of_next_group": ("f16[s[row * (K / 32) + k / 32]]", "f16[s[row * (K / 32) + (k + 1) / 32]]"),
+    "rms_mean_over_d_minus_1": ("std::sqrt(ss / (double)d + eps)", "std::sqrt(ss / (double)(d - 1) + eps)"),
 }
 
 

@@ -607,3 +607,96 @@ def test_f16_forward_equals_bf16_forward_when_exact():
     hd, _ = oracle.bf16_to_f16_trunc(wd)
     y16, _ = oracle.forward_f16_ex(x, g, 1e-5, hgu, hd)
     assert np.array_equal(y16, oracle.forward_bf16(x, g, 1e-5, wgu, wd))
+
+
+# ------------------------------------------------------------ brute force in decimal
+# The whole forward re-evaluated in Python's decimal arithmetic at 40
+# significant digits: every bf16 / fp16 input converts to Decimal exactly,
+# sqrt and exp are decimal's own, and nothing is shared with the C++ oracle
+# or with IEEE double arithmetic. The fp64 oracle must agree to within its
+# own rounding: 1e-12 of the sum of |terms| of each output.
+
+def _dec_forward(x, g, eps, wg, wu, wd, act_is_int4_scaled=False):
+    from decimal import Decimal, localcontext
+    with localcontext() as c:
+        c.prec = 40
+        M, d = x.shape
+        ff = wg.shape[0]
+        D = lambda v: Decimal(float(v))
+        eps_d = D(eps)
+        y = np.zeros((M, d))
+        mag = np.zeros((M, d))
+        for m in range(M):
+            xm = [D(v) for v in x[m]]
+            ss = sum(v * v for v in xm)
+            r = 1 / (ss / d + eps_d).sqrt()
+            n = [xm[k] * r * D(g[k]) for k in range(d)]
+            a = []
+            for i in range(ff):
+                gi = sum(D(wg[i, k]) * n[k] for k in range(d))
+                ui = sum(D(wu[i, k]) * n[k] for k in range(d))
+                a.append(gi / (1 + (-gi).exp()) * ui)
+            for j in range(d):
+                terms = [D(wd[j, i]) * a[i] for i in range(ff)]
+                y[m, j] = float(sum(terms))
+                mag[m, j] = float(sum(abs(t) for t in terms))
+        return y, mag
+
+
+@pytest.mark.parametrize("M,d,ff,seed", [(1, 2, 1, 11), (4, 64, 64, 12), (3, 32, 48, 13),
+                                         (2, 64, 16, 14)])
+def test_brute_force_decimal_bf16(M, d, ff, seed):
+    x = rand_bf16((M, d), 1.0, seed)
+    g = rand_bf16((d,), 0.1, seed + 1, mean=1.0)
+    wg = rand_bf16((ff, d), 0.3, seed + 2)
+    wu = rand_bf16((ff, d), 0.3, seed + 3)
+    wd = rand_bf16((d, ff), 0.3, seed + 4)
+    vals = [bf16_values(a) for a in (x, g, wg, wu, wd)]
+    for eps in (1e-5, 0.0):
+        ref, mag = _dec_forward(*vals[:2], eps, *vals[2:])
+        got = oracle.forward_unfused(x, g, eps, wg, wu, wd)
+        assert np.all(np.abs(got - ref) <= 1e-12 * mag + 1e-300), (eps, np.abs(got - ref).max())
+        got2 = oracle.forward_bf16(x, g, eps, oracle.pack_interleaved(wg, wu), wd)
+        assert np.array_equal(got, got2)
+
+
+def test_brute_force_decimal_large_and_tiny_magnitudes():
+    # rows of very different scales and a weight set with a large range of
+    # gate pre-activations (SiLU far into both tails)
+    x = np.concatenate([rand_bf16((1, 32), 1e4, 21), rand_bf16((1, 32), 1e-4, 22),
+                        rand_bf16((1, 32), 1.0, 23)])
+    g = rand_bf16((32,), 0.5, 24, mean=1.0)
+    wg = rand_bf16((24, 32), 3.0, 25)
+    wu = rand_bf16((24, 32), 0.02, 26)
+    wd = rand_bf16((32, 24), 0.02, 27)
+    vals = [bf16_values(a) for a in (x, g, wg, wu, wd)]
+    ref, mag = _dec_forward(*vals[:2], 1e-5, *vals[2:])
+    got = oracle.forward_unfused(x, g, 1e-5, wg, wu, wd)
+    assert np.all(np.abs(got - ref) <= 1e-12 * mag + 1e-300)
+
+
+def test_brute_force_decimal_int4():
+    # int4 weights: w = s * q exactly, in decimal as in the oracle
+    rng = np.random.default_rng(31)
+    M, d, ff = 2, 64, 32
+    x = rand_bf16((M, d), 1.0, 32)
+    g = rand_bf16((d,), 0.1, 33, mean=1.0)
+    q_gu = rng.integers(0, 256, (2 * ff, d // 2), dtype=np.uint8)
+    q_d = rng.integers(0, 256, (d, ff // 2), dtype=np.uint8)
+    s_gu = (rng.random((2 * ff, d // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+    s_d = (rng.random((d, ff // 32)) * 0.015 + 0.005).astype(np.float16).view(np.uint16)
+
+    def dense(q, s):
+        lo = (q & 0xF).astype(np.int64)
+        hi = (q >> 4).astype(np.int64)
+        codes = np.empty((q.shape[0], q.shape[1] * 2), np.int64)
+        codes[:, 0::2], codes[:, 1::2] = lo, hi
+        codes = np.where(codes >= 8, codes - 16, codes)
+        sc = np.repeat(s.view(np.float16).astype(np.float64), 32, axis=1)
+        return sc * codes  # exact: an 11-bit scale times a 4-bit integer
+
+    wgu = dense(q_gu, s_gu)
+    ref, mag = _dec_forward(bf16_values(x), bf16_values(g), 1e-5, wgu[0::2], wgu[1::2],
+                            dense(q_d, s_d))
+    got = oracle.forward_int4(x, g, 1e-5, q_gu, s_gu, q_d, s_d)
+    assert np.all(np.abs(got - ref) <= 1e-12 * mag + 1e-300)
