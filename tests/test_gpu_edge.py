@@ -37,6 +37,16 @@ def _rows_except(y, ref, bad, what):
         assert_parity(y[keep], ref[keep], what)
 
 
+def _each_row_except(y, ref, bad, what):
+    # The planted feature makes row magnitudes heavy-tailed (a row's outputs
+    # scale with its own SiLU*mul value of that feature), so rounding y to
+    # bf16 in the largest rows can exceed the bar against an rms over all
+    # rows: each row is scored against its own rms instead.
+    for m in range(y.shape[0]):
+        if m not in bad:
+            assert_parity(y[m:m + 1], ref[m:m + 1], f"{what}, row {m}")
+
+
 @pytest.mark.parametrize("wt,path,M", [("bf16", DEC, 5), ("bf16", DEC, 20), ("bf16", PRE, 40),
                                        ("bf16", SP, 3), ("int4", DEC, 3), ("int4", DEC, 20),
                                        ("int4", PRE, 40), ("f16", DEC, 4), ("f16", PRE, 40)])
@@ -51,25 +61,24 @@ def test_zero_row_with_zero_eps_is_nan(layers, wt, path, M):
     _rows_except(y, ref, {2}, f"{wt} path={path} M={M}, zero row 2, eps=0")
 
 
-def _overflow_layer(kind):
-    """Weights whose gate/up feature 0 rows are 2 * sign(x row 0): for x row 0
-    (all entries +-1, so r = 1 at eps = 0) the gate and up sums reach
-    2 * sum(gamma) ~ 512 and their product ~ 2.6e5, past fp16's 65504; for
-    random rows they stay ~ 2 * sqrt(d) = 32 (products ~ 1e3)."""
-    L = {"bf16": Bf16Layer, "f16": F16Layer}[kind](D, FF, 113)
-    return L
-
-
+# The planted feature: gate and up rows 0 are 32 at column 0 and zero
+# elsewhere, so feature 0 of a row is 32 n_0 for both branches, a single
+# product (well conditioned in any precision). Input row 0 is 1000 e_0, so
+# r = sqrt(d) / 1000 at eps = 0, n_0 = 16 gamma_0 and the gate and up sums
+# are ~512: their SiLU*mul product ~2.6e5 is past fp16's 65504. Other rows
+# have n_0 ~ N(0, 1): products below ~1e4.
 def _overflow_inputs(M):
     x, g = bf16_inputs(M, D, 130 + M)
-    sign = torch.where(torch.arange(D, device="cuda") % 3 == 0, -1.0, 1.0)
-    x[0] = sign.to(torch.bfloat16)
-    return x, g, sign
+    x[0] = 0
+    x[0, 0] = 1000.0
+    return x, g
 
 
-def _plant(L, sign):
-    L.wg[0] = (2 * sign).to(torch.bfloat16)
-    L.wu[0] = (2 * sign).to(torch.bfloat16)
+def _plant(L):
+    L.wg[0] = 0
+    L.wu[0] = 0
+    L.wg[0, 0] = 32.0
+    L.wu[0, 0] = 32.0
     L.wgu_t = F.fmlp_pack_interleaved(L.wg, L.wu)
     L.host = tuple(synth.bits(t) for t in (L.wg, L.wu, L.wd))
     if isinstance(L, F16Layer):
@@ -94,32 +103,31 @@ def _a_row_max(L, x, g):
     ("bf16", DEC, 20, False), ("bf16", PRE, 40, False),  # fp16 intermediate
     ("bf16", PRE, 4, False), ("f16", DEC, 4, False), ("f16", PRE, 40, False)])
 def test_intermediate_beyond_fp16_range(kind, path, M, row0_finite):
-    L = _overflow_layer(kind)
-    x, g, sign = _overflow_inputs(M)
-    _plant(L, sign)
+    L = {"bf16": Bf16Layer, "f16": F16Layer}[kind](D, FF, 113)
+    x, g = _overflow_inputs(M)
+    _plant(L)
     amax = _a_row_max(L, x, g)
     assert amax[0] > 2 * 65504 and torch.all(amax[1:] < 32768), amax
     y = L.forward(x, g, 0.0, path=path)
     ref = L.oracle(x, g, 0.0)
     if row0_finite:
-        assert_parity(y, ref, f"{kind} path={path} M={M}, large intermediate")
+        _each_row_except(y, ref, set(), f"{kind} path={path} M={M}")
     else:
         assert not torch.any(torch.isfinite(y[0].float())), "row 0 must be non-finite"
-        _rows_except(y, ref, {0}, f"{kind} path={path} M={M}, other rows")
+        _each_row_except(y, ref, {0}, f"{kind} path={path} M={M}")
 
 
 @pytest.mark.parametrize("path,M", [(DEC, 1), (DEC, 20), (PRE, 40)])
 def test_int4_intermediate_beyond_fp16_range(path, M):
-    # int4 codes of feature 0 set to +-7 along sign(x row 0), scale 0.25:
-    # gate and up sums ~ 1.75 * sum(gamma), product ~ 2e5; int4 carries n and
-    # a in fp16 on every path, so row 0 is non-finite there
+    # the same planted feature in int4: code 7 at column 0 with group scale
+    # 4.5 (w = 31.5), every other code of gate and up rows 0 zero; int4
+    # carries n and a in fp16 on every path, so row 0 is non-finite there
     L = Int4Layer(D, FF, 114)
-    x, g, sign = _overflow_inputs(M)
-    code = torch.where(sign > 0, 7, 9).to(torch.uint8)  # 9 = -7 in two's complement
-    packed = (code[0::2] | (code[1::2] << 4)).to(torch.uint8)
+    x, g = _overflow_inputs(M)
     for q, s in ((L.q_g, L.s_g), (L.q_u, L.s_u)):
-        q[0] = packed
-        s[0] = 0.25
+        q[0] = 0
+        q[0, 0] = 7
+        s[0, 0] = 4.5
     L.q_gu, L.s_gu = F.fmlp_pack_int4_interleaved(L.q_g, L.s_g, L.q_u, L.s_u)
     from oracle import oracle
     b = synth.bits
@@ -127,6 +135,6 @@ def test_int4_intermediate_beyond_fp16_range(path, M):
               *L.host[2:])
     y = L.forward(x, g, 0.0, path=path)
     ref = L.oracle(x, g, 0.0)
-    assert np.abs(ref[0]).max() > 0  # the oracle's row is finite
+    assert np.all(np.isfinite(ref[0])) and np.abs(ref[0]).max() > 0  # the oracle's row is finite
     assert not torch.any(torch.isfinite(y[0].float())), "row 0 must be non-finite"
-    _rows_except(y, ref, {0}, f"int4 path={path} M={M}, other rows")
+    _each_row_except(y, ref, {0}, f"int4 path={path} M={M}")
