@@ -294,6 +294,28 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
                     void* stream, int32_t path);
 
 /*
+ * fmlp_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Arguments, path choice, results and errors are those of
+ * fmlp_forward (the same kernels on the same path, so y is bitwise the
+ * same), except that the scratch is a fixed device array inside the library,
+ * FMLP_NOALLOC_SCRATCH_BYTES long, that each GPU the library runs on holds
+ * until the process ends. A problem whose automatic path needs more scratch
+ * returns FMLP_ERR_WORKSPACE; fmlp_workspace_size(M, d, ff, wtype) <=
+ * FMLP_NOALLOC_SCRATCH_BYTES guarantees it fits (every decode problem of up
+ * to 32 tokens with d <= 8192 and ff <= 28672 does). The call allocates and
+ * frees nothing. Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents (each call clears what it needs cleared), so calls
+ * that overlap in time on one GPU (several host threads, or several streams
+ * without ordering between them) race and must not be made.
+ */
+#define FMLP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fmlp_forward_noalloc(const void* x, const void* gamma, float eps,
+                         int32_t wtype, const void* w_gu, const void* gu_scales,
+                         const void* w_down, const void* down_scales, void* y,
+                         int64_t M, int64_t d, int64_t ff, void* stream);
+
+/*
  * Per-kernel timing (measurement support, not needed for computing).
  * fmlp_profile_enable(1) discards earlier records and starts launching every
  * kernel of the library with a pair of HIP events that the runtime stamps at

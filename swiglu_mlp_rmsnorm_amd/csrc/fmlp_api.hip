@@ -244,11 +244,43 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype) {
   return b + 256;  // room to align the base
 }
 
-int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void* gamma,
-                    float eps, int32_t activation, int32_t wtype, const void* w_gu,
-                    const void* gu_scales, const void* w_down, const void* down_scales, void* y,
-                    int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
-                    void* stream, int32_t path) {
+}  // extern "C"
+
+namespace {
+
+// The scratch of fmlp_forward_noalloc: its workspace, a file-scope device
+// array that every GPU the library runs on holds until the process ends (one
+// copy per device, each at its own address). Host code reaches its memory
+// only through the address hipGetSymbolAddress returns on that device.
+constexpr size_t kNoAllocScratchBytes = FMLP_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This device's scratch address (looked up once per device, with it current).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+// fmlp_forward_ex, and (noalloc) the same with the device scratch as the
+// workspace: then `workspace` is ignored and the problem must fit in it.
+int forward_impl(const void* x, const void* residual, void* h_out, const void* gamma, float eps,
+                 int32_t activation, int32_t wtype, const void* w_gu, const void* gu_scales,
+                 const void* w_down, const void* down_scales, void* y, int64_t M, int64_t d,
+                 int64_t ff, void* workspace, size_t workspace_bytes, void* stream, int32_t path,
+                 bool noalloc) {
   if (!wtype_ok(wtype)) return FMLP_ERR_INVALID_ARG;
   if (activation != FMLP_ACT_SILU && activation != FMLP_ACT_GELU_TANH &&
       activation != FMLP_ACT_GELU_ERF)
@@ -262,10 +294,12 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
   if (!std::isfinite(eps) || eps < 0.0f) return FMLP_ERR_INVALID_ARG;
   const bool int4 = wtype == FMLP_W_INT4_G32;
   if (M == 0) return FMLP_OK;
-  if (!x || !gamma || !w_gu || !w_down || !y || !workspace) return FMLP_ERR_INVALID_ARG;
+  if (!x || !gamma || !w_gu || !w_down || !y || (!noalloc && !workspace))
+    return FMLP_ERR_INVALID_ARG;
   if (int4 && (!gu_scales || !down_scales)) return FMLP_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(gamma) || !aligned16(w_gu) || !aligned16(w_down) ||
-      !aligned16(y) || !aligned16(workspace) || (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))) ||
+      !aligned16(y) || (!noalloc && !aligned16(workspace)) ||
+      (int4 && (!aligned16(gu_scales) || !aligned16(down_scales))) ||
       !aligned16(residual) || !aligned16(h_out))
     return FMLP_ERR_ALIGNMENT;
 
@@ -279,10 +313,15 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
   const size_t need = single   ? fmlp::fused_partial_bytes(M, d, ff)
                       : decode ? fmlp::decode_workspace_bytes(M, d, ff)
                                : fmlp::prefill_workspace_bytes(M, d, ff, wtype);
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return FMLP_ERR_WORKSPACE;
+    workspace = nullptr;  // set below, once the device is known
+    workspace_bytes = 0;
+  }
   // align the workspace base to 256 bytes inside the caller's buffer
-  const uintptr_t wbase = reinterpret_cast<uintptr_t>(workspace);
-  const uintptr_t abase = (wbase + 255) & ~uintptr_t(255);
-  if (workspace_bytes < need + (abase - wbase)) return FMLP_ERR_WORKSPACE;
+  uintptr_t wbase = reinterpret_cast<uintptr_t>(workspace);
+  uintptr_t abase = (wbase + 255) & ~uintptr_t(255);
+  if (!noalloc && workspace_bytes < need + (abase - wbase)) return FMLP_ERR_WORKSPACE;
 
   const size_t wgu_b = int4 ? (size_t)fmlp::int4_code_bytes(2 * ff, d) : (size_t)2 * ff * d * 2;
   const size_t wd_b = int4 ? (size_t)fmlp::int4_code_bytes(d, ff) : (size_t)d * ff * 2;
@@ -315,6 +354,12 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
   }
 
   if (int st = check_device()) return st;
+  if (noalloc) {
+    void* sp = nullptr;
+    if (hipError_t e = scratch_address(&sp)) return hip_fail(e);
+    workspace_bytes = kNoAllocScratchBytes;
+    wbase = abase = reinterpret_cast<uintptr_t>(sp);
+  }
 
   fmlp::Problem p;
   p.x = static_cast<const uint16_t*>(x);
@@ -339,6 +384,27 @@ int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void
                  : decode ? fmlp::launch_decode(p, s)
                           : fmlp::launch_prefill(p, s);
   return e == hipSuccess ? FMLP_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fmlp_forward_ex(const void* x, const void* residual, void* h_out, const void* gamma,
+                    float eps, int32_t activation, int32_t wtype, const void* w_gu,
+                    const void* gu_scales, const void* w_down, const void* down_scales, void* y,
+                    int64_t M, int64_t d, int64_t ff, void* workspace, size_t workspace_bytes,
+                    void* stream, int32_t path) {
+  return forward_impl(x, residual, h_out, gamma, eps, activation, wtype, w_gu, gu_scales, w_down,
+                      down_scales, y, M, d, ff, workspace, workspace_bytes, stream, path, false);
+}
+
+int fmlp_forward_noalloc(const void* x, const void* gamma, float eps, int32_t wtype,
+                         const void* w_gu, const void* gu_scales, const void* w_down,
+                         const void* down_scales, void* y, int64_t M, int64_t d, int64_t ff,
+                         void* stream) {
+  return forward_impl(x, nullptr, nullptr, gamma, eps, FMLP_ACT_SILU, wtype, w_gu, gu_scales,
+                      w_down, down_scales, y, M, d, ff, nullptr, 0, stream, FMLP_PATH_AUTO, true);
 }
 
 int fmlp_forward_path(const void* x, const void* gamma, float eps, int32_t wtype,

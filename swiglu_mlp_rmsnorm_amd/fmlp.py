@@ -35,6 +35,8 @@ FMLP_PATH_DECODE = 1
 FMLP_PATH_PREFILL = 2
 FMLP_PATH_SINGLE_PASS = 3
 
+FMLP_NOALLOC_SCRATCH_BYTES = 32 << 20
+
 FMLP_ACT_SILU = 0
 FMLP_ACT_GELU_TANH = 1
 FMLP_ACT_GELU_ERF = 2
@@ -43,6 +45,7 @@ EXPORTS = (
     "fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes", "fmlp_quantize_int4",
     "fmlp_pack_int4_interleaved", "fmlp_pack_int4_matrix", "fmlp_dequant_int4",
     "fmlp_convert_f16", "fmlp_workspace_size", "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
+    "fmlp_forward_noalloc",
     "fmlp_status_string", "fmlp_last_hip_error", "fmlp_profile_enable",
     "fmlp_profile_read", "fmlp_kernel_name", "fmlp_read_probe",
 )
@@ -82,6 +85,8 @@ def lib() -> ctypes.CDLL:
         fwd = [P, P, ctypes.c_float, I32, P, P, P, P, P, I64, I64, I64, P, SZ, P]
         L.fmlp_forward.argtypes = fwd
         L.fmlp_forward_path.argtypes = fwd + [I32]
+        L.fmlp_forward_noalloc.argtypes = [P, P, ctypes.c_float, I32, P, P, P, P, P, I64, I64, I64,
+                                           P]
         L.fmlp_forward_ex.argtypes = [P, P, P, P, ctypes.c_float, I32, I32, P, P, P, P, P, I64, I64,
                                       I64, P, SZ, P, I32]
         L.fmlp_status_string.argtypes = [ctypes.c_int]
@@ -97,7 +102,8 @@ def lib() -> ctypes.CDLL:
         for name in ("fmlp_pack_interleaved", "fmlp_pack_matrix", "fmlp_int4_sizes",
                      "fmlp_quantize_int4", "fmlp_pack_int4_interleaved",
                      "fmlp_pack_int4_matrix", "fmlp_dequant_int4", "fmlp_convert_f16",
-                     "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex", "fmlp_last_hip_error",
+                     "fmlp_forward", "fmlp_forward_path", "fmlp_forward_ex",
+                     "fmlp_forward_noalloc", "fmlp_last_hip_error",
                      "fmlp_profile_enable", "fmlp_profile_read"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -360,6 +366,40 @@ def fmlp_forward_ex(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=Non
     returned in h_out. Returns (y, h_out or None)."""
     return _forward(x, gamma, eps, w_gu, w_down, gu_scales, down_scales, y, workspace, stream,
                     path, ff, activation, residual, h_out)
+
+
+def fmlp_forward_noalloc(x, gamma, eps, w_gu, w_down, gu_scales=None, down_scales=None, y=None,
+                         stream=None, ff=None):
+    """fmlp_forward with the library's fixed device scratch instead of a
+    workspace (FMLP_NOALLOC_SCRATCH_BYTES); for callers that cannot allocate.
+    Calls that overlap in time on one GPU race on that scratch."""
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    M, d = x.shape
+    if w_gu.dtype == torch.uint8:
+        _need(w_gu, torch.uint8, "w_gu")
+        _need(w_down, torch.uint8, "w_down")
+        _need(gu_scales, torch.float16, "gu_scales")
+        _need(down_scales, torch.float16, "down_scales")
+        if ff is None:
+            raise ValueError("int4 weights are flat buffers: pass ff")
+        wtype = FMLP_W_INT4_G32
+    else:
+        wtype = FMLP_W_F16 if w_gu.dtype == torch.float16 else FMLP_W_BF16
+        _need(w_gu, w_gu.dtype, "w_gu")
+        _need(w_down, w_gu.dtype, "w_down")
+        ff = w_down.shape[1]
+        if w_gu.shape != (2 * ff, d) or w_down.shape != (d, ff):
+            raise ValueError("weight shapes do not match x")
+    if y is None:
+        y = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    _need(y, torch.bfloat16, "y")
+    if y.shape != (M, d):
+        raise ValueError("y must be [M, d]")
+    _check(lib().fmlp_forward_noalloc(_ptr(x), _ptr(gamma), float(eps), wtype, _ptr(w_gu),
+                                      _ptr(gu_scales), _ptr(w_down), _ptr(down_scales), _ptr(y),
+                                      M, d, ff, _stream(stream)), "fmlp_forward_noalloc")
+    return y
 
 
 def fmlp_read_probe(src, sink, workgroups: int, stream=None) -> None:

@@ -126,6 +126,33 @@ def test_forward_ex_zero_tokens_and_defaults():
         assert fwd_ex(r=None, h=None, **kw) == fwd(**kw)
 
 
+def test_noalloc_host_checks():
+    # fmlp_forward_noalloc: fmlp_forward's host-side checks, and a problem
+    # that does not fit the fixed scratch is rejected before any HIP call
+    L = F.lib()
+
+    def na(M=1, d=256, ff=704, wtype=0, **over):
+        p = dict(A)
+        p.update(over)
+        return L.fmlp_forward_noalloc(p["x"], p["g"], 1e-5, wtype, p["wgu"], p["sgu"], p["wd"],
+                                      p["sd"], p["y"], M, d, ff, None)
+    assert na(M=0, x=None, y=None) == F.FMLP_OK
+    assert na(wtype=7) == F.FMLP_ERR_INVALID_ARG
+    assert na(d=48) == F.FMLP_ERR_UNSUPPORTED_SHAPE
+    assert na(y=A["x"]) == F.FMLP_ERR_INVALID_ARG
+    assert na(wtype=1, sgu=None) == F.FMLP_ERR_INVALID_ARG
+    assert na(y=ctypes.c_void_p((7 << 36) + 8)) == F.FMLP_ERR_ALIGNMENT
+    assert na(M=2048, d=4096, ff=14336) == F.FMLP_ERR_WORKSPACE
+    assert F.fmlp_workspace_size(2048, 4096, 14336) > F.FMLP_NOALLOC_SCRATCH_BYTES
+    # every decode problem up to 32 tokens with d <= 8192, ff <= 28672 fits
+    # (the automatic path's own need; fmlp_workspace_size also covers the
+    # forced single-pass path, which this entry point never takes)
+    for d, ff in ((3072, 8192), (4096, 14336), (8192, 28672)):
+        for wt in (0, 1, 2):
+            for M in (1, 8, 16, 17, 32):
+                assert na(M=M, d=d, ff=ff, wtype=wt) != F.FMLP_ERR_WORKSPACE, (d, ff, wt, M)
+
+
 def test_read_probe_validation():
     L = F.lib()
     src, sink = ctypes.c_void_p(1 << 36), ctypes.c_void_p(2 << 36)
