@@ -8,16 +8,18 @@
 //      fp16 (Figure 4 part2; the [M, 2ff] gate/up product never reaches HBM).
 //   2. y = a W_down^T on fp16 MFMA, stored bf16 (Figure 4 part3).
 //
-// int4 weights: a pre-pass dequantises both matrices into fp16 in the same
-// fragment-tiled geometry (w = s*q, exact in fp32, rounded once to fp16:
-// relative error <= 2^-11, far inside the accuracy bar), and the GEMMs read
-// those fp16 tiles without conversion.
+// int4 weights are dequantised inside the GEMMs' weight-operand path (the
+// llama.cpp PR digest runs its quantized matmul and the GLU in one pass): the
+// codes of each K step (a quarter of the bf16 bytes) and their group scales
+// go to LDS by DMA, and each wave expands its fragments in registers to fp16
+// s*q (exact product, rounded once: relative error <= 2^-11, far inside the
+// accuracy bar) right before its MFMAs, as it converts bf16 fragments.
 //
 // Operands are fp16 rather than bf16: rounding n to bf16 alone costs about
 // 2e-2 max / 3.3e-3 mean relative error on Llama-8B-shaped layers, over the
 // accuracy bar, while bf16 weights convert to fp16 exactly in the fp16 normal
-// range and fp16 MFMA runs at the bf16 rate. Weights are converted while
-// they are staged into LDS.
+// range and fp16 MFMA runs at the bf16 rate. Weights are converted in
+// registers after their LDS reads.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "profile.hpp"
@@ -117,36 +119,6 @@ __global__ __launch_bounds__(256) void k_rms_tile(const uint16_t* __restrict__ x
   st16(n + g * 8, o);
 }
 
-// ---------------------------------------------------------------- int4 -> fp16 tiles
-// One thread per 16-byte chunk of the output (8 weights of one row): chunk
-// (tile, slot) of the fragment-tiled layout holds row 16*rb + slot%16,
-// columns 32*kb + 8*(slot/16) .. +7, tile = rb*(K/32) + kb. Its codes are one
-// word of the int4 super-tile of (rb, kb/4), its scale one fp16.
-__global__ __launch_bounds__(256) void k_dequant_f16_tiled(const uint32_t* __restrict__ qt,
-                                                           const uint16_t* __restrict__ st,
-                                                           int64_t R, int64_t K,
-                                                           uint16_t* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output chunk
-  const int64_t nkb = K >> 5, nq = (K + 127) >> 7;
-  if (c >= (R >> 4) * nkb * 64) return;
-  const int slot = (int)(c & 63);
-  const int64_t tile = c >> 6, rb = tile / nkb, kb = tile - rb * nkb;
-  const int64_t stile = rb * nq + (kb >> 2);
-  const uint32_t word = qt[stile * 256 + slot * 4 + (kb & 3)];
-  const float s = (float)__builtin_bit_cast(
-      _Float16, st[stile * 64 + (slot & 15) * 4 + (kb & 3)]);
-  u32x4 o;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q0 = (int)((word >> (8 * j)) << 28) >> 28;      // code 2j (low nibble)
-    const int q1 = (int)((word >> (8 * j + 4)) << 28) >> 28;  // code 2j+1
-    const _Float16 w0 = (_Float16)(s * (float)q0), w1 = (_Float16)(s * (float)q1);
-    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, w0) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, w1) << 16);
-  }
-  st16(out + c * 8, o);
-}
-
 // ---------------------------------------------------------------- GEMM
 // C[f, t] = sum_k W[f, k] * Act[t, k]; W in the fragment-tiled bf16 layout,
 // Act fp16 in the fragment-tiled activation layout above.
@@ -211,15 +183,29 @@ __device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <int NB, int MB, int WGN_, int WGM_>  // 32-row blocks per tile; wave grid
+// Weight kinds of the prefill GEMMs: bf16 tiles (converted to fp16 in
+// registers), fp16 tiles (read as they are), and int4 super-tiles with fp16
+// group scales (dequantised in registers, see int4x8_to_f16x8).
+enum { WF_BF16 = 0, WF_F16 = 1, WF_INT4 = 2 };
+
+template <int NB, int MB, int WGN_, int WGM_, int WKW = WF_BF16>  // 32-row blocks; wave grid
 struct GemmCfg {
   static constexpr int WGN = WGN_, WGM = WGM_, W = WGN * WGM, THREADS = 64 * W;
   static constexpr int BN = NB * 32, BM = MB * 32;
   static constexpr int WNB = NB / WGN, WMB = MB / WGM;  // 32-row blocks per wave
-  // 16-byte chunks per thread and step: weights 2*NB storage tiles of 1 KB,
-  // activations 2*MB fragments of 1 KB
-  static constexpr int A_PER_T = NB * 2 / W, B_PER_T = MB * 2 / W, LD_PER_T = A_PER_T + B_PER_T;
-  static constexpr int A_ELEMS = NB * 1024, B_ELEMS = MB * 1024;  // 16-bit elements per stage
+  static constexpr bool Q4 = WKW == WF_INT4;
+  // loads per thread and step: one per 16-row weight band (a 1 KB storage
+  // tile, or for int4 the band's 256 bytes of codes of the step's group),
+  // int4 also one of group scales (SC_BANDS bands per wave), and one per
+  // activation fragment of 1 KB
+  static constexpr int A_PER_T = NB * 2 / W, SC_BANDS = NB * 2 / W;
+  static constexpr int A_LD = A_PER_T + (Q4 ? 1 : 0);
+  static constexpr int B_PER_T = MB * 2 / W, LD_PER_T = A_LD + B_PER_T;
+  // 16-bit elements per stage: weights (tiles; or int4 codes, 128 per band,
+  // then 128 per wave of scale words), activations
+  static constexpr int A_CODE_ELEMS = NB * 2 * 128;
+  static constexpr int A_ELEMS = Q4 ? A_CODE_ELEMS + W * 128 : NB * 1024;
+  static constexpr int B_ELEMS = MB * 1024;
   static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
   static constexpr int STAGES = 5;
   static constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * 2;
@@ -227,6 +213,7 @@ struct GemmCfg {
   static constexpr int WAVES_PER_EU = (WNB * WMB >= 16) ? 1 : 2;
   static_assert((W == 4 || W == 8) && WNB >= 1 && WMB >= 1 && A_PER_T * W == NB * 2 &&
                 B_PER_T * W == MB * 2, "tile");
+  static_assert(!Q4 || SC_BANDS * 16 <= 64, "int4 scale lanes");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(3 * LD_PER_T < 64, "vmcnt field");
 };
@@ -239,15 +226,46 @@ constexpr int kBufWord3 = 0x00020000;
 __device__ __forceinline__ int buf_extent(int64_t bytes) {
   return bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
 }
-// One 16-byte-per-lane LDS DMA through a raw buffer descriptor over
-// [base, base + extent): lane l's 16 bytes at byte offset voff + soff land at
-// dst + 16 l. (The descriptor is built here, not in the kernel body: its
-// loop-invariant scalar setup is hoisted by the compiler.)
-__device__ __forceinline__ void buf_load_lds16(const uint16_t* base, int extent, lptr_t dst,
-                                               int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, extent, kBufWord3),
-      dst, 16, voff, soff, 0, 0);
+// One SZ-byte-per-lane LDS DMA (SZ = 16 or 4) through a raw buffer
+// descriptor over [base, base + extent): lane l's SZ bytes at byte offset
+// voff + soff land at dst + SZ l. (The descriptor is built here, not in the
+// kernel body: its loop-invariant scalar setup is hoisted by the compiler.)
+template <int SZ>
+__device__ __forceinline__ void buf_load_lds(const void* base, int extent, lptr_t dst, int voff,
+                                             int soff) {
+  static_assert(SZ == 4 || SZ == 16, "LDS DMA size");
+  const auto rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent, kBufWord3);
+  if constexpr (SZ == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, soff, 0, 0);
+}
+
+// Eight int4 codes (one 32-bit word, code m in bits 4m..4m+3, two's
+// complement) and their fp16 group scale -> the eight weights s*q as fp16 in
+// natural order, each the exact product rounded once to nearest even: the
+// same value as fp16(float(s) * q). With t = w ^ 0x88888888 every nibble is
+// q + 8; v_perm places nibbles 2j and 2j+1 in the low bytes of the two halves
+// of word j, and with 0x6400 in the high bytes the halves are the fp16
+// values 1024 + q + 8 (exact); a packed fp16 add of -1032 leaves q exactly,
+// and a packed fp16 multiply by s rounds s*q once.
+__device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, uint32_t s16) {
+  const uint32_t t = w ^ 0x88888888u;
+  const uint32_t ev = t & 0x0F0F0F0Fu;         // bytes: codes 0, 2, 4, 6 (+8)
+  const uint32_t od = (t >> 4) & 0x0F0F0F0Fu;  // bytes: codes 1, 3, 5, 7 (+8)
+  const f16x2 s2 = __builtin_bit_cast(f16x2, (s16 & 0xFFFFu) * 0x10001u);
+  const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // bytes (ev.j, 0, od.j, 0): selector j, 0x0C (zero), 4 + j, 0x0C
+    const uint32_t sel = (uint32_t)j | 0x0C00u | ((uint32_t)(4 + j) << 16) | 0x0C000000u;
+    const uint32_t h = __builtin_amdgcn_perm(od, ev, sel) | 0x64006400u;
+    const f16x2 q = __builtin_bit_cast(f16x2, h) + off;
+    r[j] = __builtin_bit_cast(uint32_t, q * s2);
+  }
+  return r;
 }
 
 // s_waitcnt immediate for vmcnt(vm) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] |
@@ -256,13 +274,15 @@ __device__ __forceinline__ void buf_load_lds16(const uint16_t* base, int extent,
 // no redundant waits.
 constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | 0x70 | ((vm >> 4) << 14); }
 
-// AF16: the weight tiles already hold fp16 (dequantised int4), no conversion.
-template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
+// WKW: weight kind (WF_*). Wt: weight tiles, or int4 code super-tiles with
+// Wsc their fp16 scales (unused otherwise).
+template <int NB, int MB, int WGN, int WGM, int EPI, int WKW>
 __global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
     GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
-k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
-            void* __restrict__ out, int M, int N, int K, int n_begin, int n_end) {
-  using C = GemmCfg<NB, MB, WGN, WGM>;
+k_gemm_wf16(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
+            const uint16_t* __restrict__ Act, void* __restrict__ out, int M, int N, int K,
+            int n_begin, int n_end) {
+  using C = GemmCfg<NB, MB, WGN, WGM, WKW>;
   extern __shared__ __align__(16) uint16_t lds[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -289,17 +309,39 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   // descriptor's extent would return zeros rather than fault (all reads
   // here are in range: row and token blocks are clamped below).
   //
-  // Weight chunk i of a thread: 16-row storage tile rb = W*i + wave of the
-  // tile (rows past N clamped), slot = lane; its LDS image sits at rb * 1 KB.
+  // Weight chunk i of a thread: 16-row band rb = W*i + wave of the tile
+  // (rows past N clamped), slot = lane. bf16 / fp16: its 1 KB storage tile,
+  // LDS image at rb * 1 KB. int4: word (kbeg + kt) % 4 of the lane's 16-byte
+  // slot of the band's super-tile (kbeg + kt) / 4, i.e. the codes of group
+  // kbeg + kt, LDS image at rb * 256 bytes in slot order; and one 4-byte
+  // load per wave of group scales: lane j takes the scale pair (groups
+  // 2 (g/2), +1) of row j % 16 of band wave * SC_BANDS + (j / 16) % SC_BANDS
+  // (lanes past 16 SC_BANDS repeat those loads into unused LDS words).
   const int rb0 = n0 >> 4;
-  const uint16_t* wbase = Wt + ((int64_t)rb0 * nkb + kbeg) * 512;
-  const int wext = buf_extent(((int64_t)nrb * nkb - ((int64_t)rb0 * nkb + kbeg)) * 1024);
+  const int nq = (K + 127) >> 7;  // int4 super-tiles per band
+  const void* wbase;
+  int wext;
+  if constexpr (C::Q4) {
+    wbase = static_cast<const uint8_t*>(Wt) + (int64_t)rb0 * nq * 1024;
+    wext = buf_extent(((int64_t)nrb - rb0) * nq * 1024);
+  } else {
+    wbase = static_cast<const uint16_t*>(Wt) + ((int64_t)rb0 * nkb + kbeg) * 512;
+    wext = buf_extent(((int64_t)nrb * nkb - ((int64_t)rb0 * nkb + kbeg)) * 1024);
+  }
   int woff[C::A_PER_T];
 #pragma unroll
   for (int i = 0; i < C::A_PER_T; ++i) {
     const int rb = C::W * i + wave;
     const int rbc = rb0 + rb < nrb ? rb : nrb - 1 - rb0;
-    woff[i] = rbc * nkb * 1024 + lane * 16;
+    woff[i] = C::Q4 ? rbc * nq * 1024 + lane * 16 : rbc * nkb * 1024 + lane * 16;
+  }
+  const uint16_t* sbase = Wsc + (int64_t)rb0 * nq * 64;
+  const int sext = C::Q4 ? buf_extent(((int64_t)nrb - rb0) * nq * 128) : 0;
+  int soff_lane = 0;
+  if constexpr (C::Q4) {
+    const int rb = wave * C::SC_BANDS + (lane >> 4) % C::SC_BANDS;
+    const int rbc = rb0 + rb < nrb ? rb : nrb - 1 - rb0;
+    soff_lane = rbc * nq * 128 + (lane & 15) * 8;
   }
   // Activation chunk i: fragment f = W*i + wave of the stage (token block
   // f/2 of the tile, half q = f%2), one contiguous 1 KB fragment of the tiled
@@ -329,28 +371,54 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   // the loads of step kt into stage st: weights, then activations
   auto load_a = [&](int kt, int st) __attribute__((always_inline)) {
     uint16_t* base = lds + st * C::STAGE_ELEMS;
+    if constexpr (C::Q4) {
+      const int g = kbeg + kt;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i)
-      buf_load_lds16(wbase, wext, (lptr_t)(base + (C::W * i + wave) * 512), woff[i], kt * 1024);
+      for (int i = 0; i < C::A_PER_T; ++i)
+        buf_load_lds<4>(wbase, wext, (lptr_t)(base + (C::W * i + wave) * 128), woff[i],
+                        (g >> 2) * 1024 + (g & 3) * 4);
+      buf_load_lds<4>(sbase, sext, (lptr_t)(base + C::A_CODE_ELEMS + wave * 128), soff_lane,
+                      (g >> 2) * 128 + (g & 2) * 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::A_PER_T; ++i)
+        buf_load_lds<16>(wbase, wext, (lptr_t)(base + (C::W * i + wave) * 512), woff[i],
+                         kt * 1024);
+    }
   };
   auto load_b = [&](int kt, int st) __attribute__((always_inline)) {
     uint16_t* base = lds + st * C::STAGE_ELEMS + C::A_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
-      buf_load_lds16(abase, aext, (lptr_t)(base + (C::W * i + wave) * 512), aoff[i], kt * 2048);
+      buf_load_lds<16>(abase, aext, (lptr_t)(base + (C::W * i + wave) * 512), aoff[i], kt * 2048);
   };
   auto load_step = [&](int kt, int st) __attribute__((always_inline)) {
     load_a(kt, st);
     load_b(kt, st);
   };
 
+  // int4: lane l of the fragment of 32-row block b, half q reads the code
+  // word of slot 32 q + 16 (l / 32) + l % 16 of band 2b + (l % 32) / 16, and
+  // that row's fp16 scale of the step's group (half g % 2 of its pair)
+  const int q4_band = (lane & 31) >> 4, q4_slot = (lane >> 5) * 16 + (lane & 15);
   u32x4 fa[2][C::WNB], fb[2][C::WMB];
-  auto frag_load_a = [&](int buf, int st, int q) __attribute__((always_inline)) {
+  auto frag_load_a = [&](int buf, int st, int q, int kt) __attribute__((always_inline)) {
     const uint16_t* base = lds + st * C::STAGE_ELEMS;
+    if constexpr (C::Q4) {
+      const uint32_t* codes = reinterpret_cast<const uint32_t*>(base);
 #pragma unroll
-    for (int i = 0; i < C::WNB; ++i)
-      fa[buf][i] = *reinterpret_cast<const u32x4*>(
-          &base[a_rd + (wn * C::WNB + i) * 1024 + q * 256]);
+      for (int i = 0; i < C::WNB; ++i) {
+        const int band = 2 * (wn * C::WNB + i) + q4_band;
+        const int sw = (band / C::SC_BANDS) * 64 + (band % C::SC_BANDS) * 16 + (lane & 15);
+        fa[buf][i][0] = codes[band * 64 + q * 32 + q4_slot];
+        fa[buf][i][1] = base[C::A_CODE_ELEMS + sw * 2 + ((kbeg + kt) & 1)];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::WNB; ++i)
+        fa[buf][i] = *reinterpret_cast<const u32x4*>(
+            &base[a_rd + (wn * C::WNB + i) * 1024 + q * 256]);
+    }
   };
   auto frag_load_b = [&](int buf, int st, int q) __attribute__((always_inline)) {
     const uint16_t* base = lds + st * C::STAGE_ELEMS;
@@ -359,22 +427,26 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
       fb[buf][j] = *reinterpret_cast<const u32x4*>(
           &base[b_rd + ((wm * C::WMB + j) * 2 + q) * 512]);
   };
-  auto frag_load = [&](int buf, int st, int q) __attribute__((always_inline)) {
-    frag_load_a(buf, st, q);
+  auto frag_load = [&](int buf, int st, int q, int kt) __attribute__((always_inline)) {
+    frag_load_a(buf, st, q, kt);
     frag_load_b(buf, st, q);
   };
   // the same reads, weights strictly first, all issued before what follows
-  auto frag_load_ordered = [&](int buf, int st, int q) __attribute__((always_inline)) {
-    frag_load_a(buf, st, q);
+  auto frag_load_ordered = [&](int buf, int st, int q, int kt) __attribute__((always_inline)) {
+    frag_load_a(buf, st, q, kt);
     __builtin_amdgcn_sched_barrier(0);
     frag_load_b(buf, st, q);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // weight fragments bf16 -> fp16 in place (after their LDS reads land)
+  // weight fragments to fp16 in place (after their LDS reads land): bf16
+  // converted, int4 dequantised, fp16 as they are
   auto convert = [&](int buf) __attribute__((always_inline)) {
-    if constexpr (!AF16) {
+    if constexpr (WKW == WF_BF16) {
 #pragma unroll
       for (int i = 0; i < C::WNB; ++i) fa[buf][i] = bf16x8_to_f16x8(fa[buf][i]);
+    } else if constexpr (C::Q4) {
+#pragma unroll
+      for (int i = 0; i < C::WNB; ++i) fa[buf][i] = int4x8_to_f16x8(fa[buf][i][0], fa[buf][i][1]);
     }
   };
   auto mma = [&](int buf) __attribute__((always_inline)) {
@@ -396,7 +468,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   constexpr bool kSpread = C::W == 8;
   auto interleave = [&](auto nl_c) __attribute__((always_inline)) {
     constexpr int NMF = C::WNB * C::WMB;
-    constexpr int NV = AF16 ? 0 : C::WNB * 12, HALF = NMF / 2;
+    constexpr int NV = WKW == WF_F16 ? 0 : C::WNB * (C::Q4 ? 20 : 12), HALF = NMF / 2;
     constexpr int NL = kSpread ? decltype(nl_c)::value : 0;
     constexpr int LS = NMF / (NL > 0 ? NL : 1) > 0 ? NMF / (NL > 0 ? NL : 1) : 1;  // MFMAs per load
 #pragma unroll
@@ -414,7 +486,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   for (int s = 0; s < npre; ++s) load_step(s, s);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
-  frag_load(0, 0, 0);
+  frag_load(0, 0, 0, 0);
   convert(0);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
 
@@ -427,17 +499,17 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   for (; kt + 4 < nkt; ++kt) {
     const int st1 = st == 4 ? 0 : st + 1, st4 = st == 0 ? 4 : st - 1;
     if (!kSpread) load_a(kt + 4, st4);
-    frag_load_ordered(1, st, 1);
+    frag_load_ordered(1, st, 1, kt);
     if (kSpread) load_a(kt + 4, st4);
     mma(0);
     convert(1);
-    interleave(std::integral_constant<int, C::A_PER_T>{});
+    interleave(std::integral_constant<int, C::A_LD>{});
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T + C::A_PER_T));
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * C::LD_PER_T + C::A_LD));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (!kSpread) load_b(kt + 4, st4);
-    frag_load_ordered(0, st1, 0);
+    frag_load_ordered(0, st1, 0, kt + 1);
     if (kSpread) load_b(kt + 4, st4);
     mma(1);
     convert(0);
@@ -452,7 +524,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
   for (; kt < nkt; ++kt) {
     const int st1 = st == 4 ? 0 : st + 1;
     const int behind = nkt - 2 - kt;  // steps after kt+1 whose loads may be in flight
-    frag_load(1, st, 1);
+    frag_load(1, st, 1, kt);
     mma(0);
     convert(1);
     if (behind >= 2)
@@ -465,7 +537,7 @@ k_gemm_wf16(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ Act,
     // (one copy of each MFMA group: accumulators that flow through
     // duplicated MFMAs in branches get split across register files)
     const bool more = kt + 1 < nkt;
-    if (more) frag_load(0, st1, 0);
+    if (more) frag_load(0, st1, 0, kt + 1);
     mma(1);
     if (more) convert(0);
     st = st1;
@@ -521,22 +593,28 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 // Launch one GEMM with a given block tile and wave grid (splits > 1 only
 // with the fp32 partial epilogue).
-template <int NB, int MB, int WGN, int WGM, int EPI, bool AF16>
-static hipError_t launch_gemm_t(const uint16_t* W, const uint16_t* Act, void* out, int M, int N,
-                                int K, int splits, hipStream_t stream, int n_begin, int n_end) {
-  using C = GemmCfg<NB, MB, WGN, WGM>;
+// The weights of one GEMM: tiles (bf16 or fp16), or int4 codes and scales.
+struct GemmW {
+  const void* w;
+  const uint16_t* s;
+};
+
+template <int NB, int MB, int WGN, int WGM, int EPI, int WKW>
+static hipError_t launch_gemm_t(GemmW W, const uint16_t* Act, void* out, int M, int N, int K,
+                                int splits, hipStream_t stream, int n_begin, int n_end) {
+  using C = GemmCfg<NB, MB, WGN, WGM, WKW>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [] {
     attr_err =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_wf16<NB, MB, WGN, WGM, EPI, WKW>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
   });
   if (attr_err != hipSuccess) return attr_err;
   const int tiles = ((n_end - n_begin + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
   launch_kernel(epi_gate(EPI) ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
-                k_gemm_wf16<NB, MB, WGN, WGM, EPI, AF16>, dim3(tiles, splits), dim3(C::THREADS),
-                (uint32_t)C::LDS_BYTES, stream, W, Act, out, M, N, K, n_begin, n_end);
+                k_gemm_wf16<NB, MB, WGN, WGM, EPI, WKW>, dim3(tiles, splits), dim3(C::THREADS),
+                (uint32_t)C::LDS_BYTES, stream, W.w, W.s, Act, out, M, N, K, n_begin, n_end);
   return hipGetLastError();
 }
 
@@ -589,9 +667,9 @@ static GemmPlan plan_gemm(int M, int N, int K, bool may_split) {
   return best;
 }
 
-template <int EPI, bool AF16>
-static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const uint16_t* Act,
-                                   void* out, int M, int N, int K, hipStream_t stream) {
+template <int EPI, int WKW>
+static hipError_t launch_gemm_plan(const GemmPlan& g, GemmW W, const uint16_t* Act, void* out,
+                                   int M, int N, int K, hipStream_t stream) {
   const int n_main = N - g.tail_rows;
   hipError_t e = hipSuccess;
   if (n_main > 0) {
@@ -600,16 +678,16 @@ static hipError_t launch_gemm_plan(const GemmPlan& g, const uint16_t* W, const u
     constexpr bool w4 = !epi_gate(EPI) && kDownW4;
     constexpr int s0n = w4 ? kDnWgn : kS0Wgn, s0m = w4 ? kDnWgm : kS0Wgm;
     if (g.shape == 0)
-      e = launch_gemm_t<8, 8, s0n, s0m, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
+      e = launch_gemm_t<8, 8, s0n, s0m, EPI, WKW>(W, Act, out, M, N, K, g.splits, stream, 0,
                                                   n_main);
     else if (g.shape == 1)
-      e = launch_gemm_t<8, 4, 4, kS1Wgm, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0,
+      e = launch_gemm_t<8, 4, 4, kS1Wgm, EPI, WKW>(W, Act, out, M, N, K, g.splits, stream, 0,
                                                         n_main);
     else
-      e = launch_gemm_t<4, 4, 2, 2, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
+      e = launch_gemm_t<4, 4, 2, 2, EPI, WKW>(W, Act, out, M, N, K, g.splits, stream, 0, n_main);
   }
   if (e != hipSuccess || g.tail_rows == 0) return e;
-  return launch_gemm_t<8, 4, 4, kS1Wgm, EPI, AF16>(W, Act, out, M, N, K, g.splits, stream,
+  return launch_gemm_t<8, 4, 4, kS1Wgm, EPI, WKW>(W, Act, out, M, N, K, g.splits, stream,
                                                       n_main, N);
 }
 
@@ -639,12 +717,11 @@ static GemmPlan plan_down(int64_t M, int64_t d, int64_t ff) {
 
 // Workspace regions, in order (each 256-byte aligned): n fp16 [pad32(M), d]
 // and a fp16 [pad32(M), ff], both fragment-tiled; r fp32 [M]; the down
-// projection's split-K partials fp32 [splits, M, d]; for int4 weights, the
-// dequantised fp16 W_gu [2ff, d] and W_down [d, ff], fragment-tiled.
+// projection's split-K partials fp32 [splits, M, d]. The same for every
+// weight type (int4 weights are dequantised inside the GEMMs).
 struct PrefillWs {
   uint16_t *n, *a;
   float *r, *part;
-  uint16_t *wgu16, *wd16;
 };
 
 static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, size_t part_bytes,
@@ -660,8 +737,6 @@ static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, size_t
   w.a = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * ff * 2));
   w.r = reinterpret_cast<float*>(take((size_t)M * 4));
   w.part = reinterpret_cast<float*>(take(part_bytes));
-  w.wgu16 = reinterpret_cast<uint16_t*>(take((size_t)2 * ff * d * 2));
-  w.wd16 = reinterpret_cast<uint16_t*>(take((size_t)d * ff * 2));
   *total = off;
   return w;
 }
@@ -671,10 +746,9 @@ static size_t split_partial_bytes(int64_t M, int64_t d, int splits) {
 }
 
 static size_t ws_total(int64_t M, int64_t d, int64_t ff, int wtype, size_t part_bytes) {
+  (void)wtype;  // the same regions for every weight type
   size_t total = 0;
   prefill_ws(nullptr, M, d, ff, part_bytes, &total);
-  // (the fp16 expansion of the weights: int4 only)
-  if (wtype != 1) total -= align256((size_t)2 * ff * d * 2) + align256((size_t)d * ff * 2);
   return total;
 }
 
@@ -697,36 +771,28 @@ size_t prefill_workspace_envelope(int64_t M, int64_t d, int64_t ff, int wtype) {
   return ws_total(M, d, ff, wtype, part);
 }
 
-template <bool AF16>
-static hipError_t prefill_gemms(const Problem& p, const PrefillWs& w, const uint16_t* wgu,
-                                const uint16_t* wd, const GemmPlan& g2, hipStream_t stream) {
+template <int WKW>
+static hipError_t prefill_gemms(const Problem& p, const PrefillWs& w, GemmW wgu, GemmW wd,
+                                const GemmPlan& g2, hipStream_t stream) {
   const GemmPlan g1 =
       with_tail(plan_gemm((int)p.M, (int)(2 * p.ff), (int)p.d, false), (int)p.M, (int)(2 * p.ff));
   const int N1 = (int)(2 * p.ff), M1 = (int)p.M, K1 = (int)p.d;
   hipError_t e =
-      p.act == 1   ? launch_gemm_plan<EPI_GELU_TANH_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1,
-                                                                  stream)
-      : p.act == 2 ? launch_gemm_plan<EPI_GELU_ERF_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1,
+      p.act == 1   ? launch_gemm_plan<EPI_GELU_TANH_MUL_F16, WKW>(g1, wgu, w.n, w.a, M1, N1, K1,
                                                                  stream)
-                   : launch_gemm_plan<EPI_SILU_MUL_F16, AF16>(g1, wgu, w.n, w.a, M1, N1, K1, stream);
+      : p.act == 2 ? launch_gemm_plan<EPI_GELU_ERF_MUL_F16, WKW>(g1, wgu, w.n, w.a, M1, N1, K1,
+                                                                stream)
+                   : launch_gemm_plan<EPI_SILU_MUL_F16, WKW>(g1, wgu, w.n, w.a, M1, N1, K1, stream);
   if (e != hipSuccess) return e;
   if (g2.splits == 1)
-    return launch_gemm_plan<EPI_STORE_BF16, AF16>(g2, wd, w.a, p.y, (int)p.M, (int)p.d, (int)p.ff,
-                                                  stream);
-  e = launch_gemm_plan<EPI_STORE_F32, AF16>(g2, wd, w.a, w.part, (int)p.M, (int)p.d, (int)p.ff,
-                                            stream);
+    return launch_gemm_plan<EPI_STORE_BF16, WKW>(g2, wd, w.a, p.y, (int)p.M, (int)p.d, (int)p.ff,
+                                                 stream);
+  e = launch_gemm_plan<EPI_STORE_F32, WKW>(g2, wd, w.a, w.part, (int)p.M, (int)p.d, (int)p.ff,
+                                           stream);
   if (e != hipSuccess) return e;
   const int64_t n4 = p.M * p.d / 4;
   launch_kernel(KK_SPLITK_REDUCE, k_splitk_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
                 stream, w.part, p.y, n4, g2.splits);
-  return hipGetLastError();
-}
-
-static hipError_t launch_dequant_f16(const uint8_t* q, const uint16_t* s, int64_t R, int64_t K,
-                                     uint16_t* out, hipStream_t stream) {
-  const int64_t chunks = (R >> 4) * (K >> 5) * 64;
-  launch_kernel(KK_DEQUANT, k_dequant_f16_tiled, dim3((unsigned)((chunks + 255) / 256)), dim3(256),
-                0, stream, reinterpret_cast<const uint32_t*>(q), s, R, K, out);
   return hipGetLastError();
 }
 
@@ -742,19 +808,10 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
                 stream, p.x, p.gamma, w.r, w.n, (int)p.M, (int)p.d, slots, p.res, p.hout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.wtype == 0)
-    return prefill_gemms<false>(p, w, reinterpret_cast<const uint16_t*>(p.w_gu),
-                                reinterpret_cast<const uint16_t*>(p.w_down), g2, stream);
-  if (p.wtype == 2)  // fp16 weights: the fp16 products read them as they are
-    return prefill_gemms<true>(p, w, reinterpret_cast<const uint16_t*>(p.w_gu),
-                               reinterpret_cast<const uint16_t*>(p.w_down), g2, stream);
-  if ((e = launch_dequant_f16(reinterpret_cast<const uint8_t*>(p.w_gu), p.s_gu, 2 * p.ff, p.d,
-                              w.wgu16, stream)) != hipSuccess)
-    return e;
-  if ((e = launch_dequant_f16(reinterpret_cast<const uint8_t*>(p.w_down), p.s_down, p.d, p.ff,
-                              w.wd16, stream)) != hipSuccess)
-    return e;
-  return prefill_gemms<true>(p, w, w.wgu16, w.wd16, g2, stream);
+  const GemmW wgu{p.w_gu, p.s_gu}, wd{p.w_down, p.s_down};
+  if (p.wtype == 0) return prefill_gemms<WF_BF16>(p, w, wgu, wd, g2, stream);
+  if (p.wtype == 2) return prefill_gemms<WF_F16>(p, w, wgu, wd, g2, stream);
+  return prefill_gemms<WF_INT4>(p, w, wgu, wd, g2, stream);
 }
 
 }  // namespace fmlp

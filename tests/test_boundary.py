@@ -180,7 +180,15 @@ def test_f16_weights_pass_the_host_checks():
     assert ws(2048, 4096, 14336, 2) == ws(2048, 4096, 14336, 0)
     for M in (9, 33):  # no single-pass partials (the bf16 size keeps them at every M)
         assert ws(M, 4096, 14336, 2) < ws(M, 4096, 14336, 0)
-    assert ws(2048, 4096, 14336, 2) < ws(2048, 4096, 14336, 1)
+    # int4 prefill dequantises inside the GEMMs: no weight expansion in the
+    # workspace, so int4 needs what fp16 needs on every path but the
+    # single pass (bf16 only)
+    for M in (1, 16, 32, 33, 512, 2048):
+        assert ws(M, 8192, 28672, 1) == ws(M, 8192, 28672, 2)
+    # the 70B decode configuration: well under 8 MB (was 1.41 GB with the
+    # fp16 expansion)
+    assert ws(16, 8192, 28672, 1) < 8 << 20
+    assert ws(1, 8192, 28672, 1) < 8 << 20
 
 
 def test_convert_f16_validation():

@@ -300,6 +300,32 @@ def test_prefill_int4_large_m(M):
     assert_parity(layer.forward(x, g, EPS), layer.oracle(x, g, EPS), f"int4 prefill M={M}")
 
 
+@pytest.mark.parametrize("d,ff,M", [(256, 704, 70), (1024, 3584, 512), (8192, 1024, 40),
+                                    (96, 160, 33)])
+def test_int4_prefill_equals_fp16_weights_of_s_times_q(d, ff, M):
+    # The int4 GEMMs expand each weight to fp16(s * q) (the exact product,
+    # rounded once to nearest even) inside their operand path. The same
+    # values stored as fp16 weights (dequantised exactly, rounded by torch,
+    # tiled) through the fp16-weight GEMMs must give y bit for bit.
+    layer = Int4Layer(d, ff, 70 + d)
+    q_il = torch.empty((2 * ff, d // 2), dtype=torch.uint8, device="cuda")
+    s_il = torch.empty((2 * ff, d // 32), dtype=torch.float16, device="cuda")
+    q_il[0::2], q_il[1::2] = layer.q_g, layer.q_u
+    s_il[0::2], s_il[1::2] = layer.s_g, layer.s_u
+
+    def tiled_f16(q, s):
+        w16 = F.fmlp_dequant_int4(q, s).half()
+        return F.fmlp_pack_matrix(w16.view(torch.bfloat16)).view(torch.float16)
+
+    wgu16, wd16 = tiled_f16(q_il, s_il), tiled_f16(layer.q_dn, layer.s_dn)
+    x, g = bf16_inputs(M, d, 870 + M)
+    for path in (F.FMLP_PATH_PREFILL, F.FMLP_PATH_AUTO):
+        y4 = layer.forward(x, g, EPS, path=path)
+        y16 = F.fmlp_forward_path(x, g, EPS, wgu16, wd16, path=F.FMLP_PATH_PREFILL)
+        if path == F.FMLP_PATH_PREFILL or M > 32:
+            assert torch.equal(y4.view(torch.int16), y16.view(torch.int16))
+
+
 def test_int4_end_to_end_from_bf16(tiny):
     # quantise gate, up and down with the library in the exchange format,
     # pack, run; the oracle quantises the same seeded bf16 weights itself
