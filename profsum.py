@@ -6,6 +6,9 @@
   pmc:    four --pmc runs (FETCH_SIZE and WRITE_SIZE of one kernel, the same
           two counters of a plain copy of known size) -> HBM bytes per launch
           of that kernel, each counter scaled by what it reads for the copy.
+  counters: several --pmc runs of shader counters plus a kernel trace ->
+          per-dispatch averages, MFMA busy share, shader clock, LDS / VALU
+          activity of one kernel.
 
 Reads CSV files only; runs nothing on the GPU.
 """
@@ -114,6 +117,96 @@ def pmc(args):
     print(text)
 
 
+def _dispatch_values(dirname, match):
+    """{counter: [per-dispatch value]} for kernels whose name matches (each
+    dispatch's value summed over the counter's dimensions), plus
+    "_DURATION_NS": the dispatches' own durations in that run."""
+    path = _one(os.path.join(dirname, "**", "*counter_collection.csv"))
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if not re.search(match, r["Kernel_Name"]):
+            continue
+        key = (r["Counter_Name"], r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        dk = ("_DURATION_NS", r["Dispatch_Id"])
+        per[dk] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for (c, _), v in sorted(per.items(), key=lambda kv: int(kv[0][1])):
+        out.setdefault(c, []).append(v)
+    if not out:
+        raise SystemExit(f"no dispatch of /{match}/ in {path}")
+    return out
+
+
+def _trace_avg_ns(dirname, match):
+    path = _one(os.path.join(dirname, "**", "*kernel_stats.csv"))
+    calls, total = 0, 0.0
+    for r in csv.DictReader(open(path)):
+        if re.search(match, r["Name"]):
+            calls += int(r["Calls"])
+            total += float(r["TotalDurationNs"])
+    if not calls:
+        raise SystemExit(f"no kernel /{match}/ in {path}")
+    return total / calls, calls
+
+
+def counters(args):
+    """Hardware counters of one kernel (several --pmc passes, one directory
+    each) with the kernel's average duration from a --kernel-trace run:
+    per-dispatch averages and the derived utilisations."""
+    vals = {}
+    for d in args.dirs:
+        for c, v in _dispatch_values(d, args.match).items():
+            vals[c] = v
+    avg = {c: statistics.mean(v) for c, v in vals.items()}
+    dur_ns, calls = _trace_avg_ns(args.trace, args.match)
+    simds, cus = args.cus * 4, args.cus
+    # GRBM counters arrive summed over the XCDs (one GRBM each): per-XCD
+    # cycles are the sum over args.xcds; SQ counters are sums over all CUs
+    gui_x = avg["GRBM_GUI_ACTIVE"] / args.xcds if "GRBM_GUI_ACTIVE" in avg else None
+    lines = [f"# hardware counters of {args.kernel} ({args.title})",
+             f"kernel_match: {args.match}",
+             f"avg_duration_us: {dur_ns / 1e3:.2f}  (kernel trace, {calls} dispatches)"]
+    gui = gui_x
+    if gui:
+        cdur = avg.get("_DURATION_NS", dur_ns)
+        lines.append(f"shader_clock_ghz: {gui / cdur:.3f}  (GRBM_GUI_ACTIVE / {args.xcds} XCDs"
+                     " / the dispatch's duration in the counter run)")
+    if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        lines.append(f"mfma_busy_pct: {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.1f}"
+                     f"  (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * {simds} SIMDs))")
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in avg:
+        fl = avg["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+        lines.append(f"mfma_f16_flop_per_dispatch: {fl:.4g}  (SQ_INSTS_VALU_MFMA_MOPS_F16 * 512)")
+        lines.append(f"mfma_tflop_per_s: {fl / dur_ns / 1e3:.1f}")
+        if gui:
+            peak_at_clock = 2500.0 * (gui / dur_ns) / 2.4
+            lines.append(f"mfma_peak_at_measured_clock_tflop_per_s: {peak_at_clock:.0f}"
+                         "  (2.5 PFLOP/s scaled from 2.4 GHz)")
+    if gui:
+        for c in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                  "SQ_ACTIVE_INST_MISC", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                  "SQ_ACTIVE_INST_ANY", "SQ_VALU_MFMA_COEXEC_CYCLES"):
+            if c in avg and "SQ_WAVE_CYCLES" in avg:
+                lines.append(f"{c.lower()}_per_wave_cycle: {avg[c] / avg['SQ_WAVE_CYCLES']:.3f}")
+        if "SQ_LDS_IDX_ACTIVE" in avg:
+            lines.append(f"lds_active_pct: {100 * avg['SQ_LDS_IDX_ACTIVE'] / (gui * cus):.1f}"
+                         f"  (SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE * {cus} CUs))")
+        if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
+            lines.append(f"lds_bank_conflict_ratio: "
+                         f"{avg['SQ_LDS_BANK_CONFLICT'] / max(avg['SQ_LDS_IDX_ACTIVE'], 1):.4f}")
+        if "TA_TA_BUSY_sum" in avg:
+            lines.append(f"ta_busy_pct: {100 * avg['TA_TA_BUSY_sum'] / (gui * cus):.1f}")
+    if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+        lines.append(f"valu_insts_per_mfma: {avg['SQ_INSTS_VALU'] / max(avg['SQ_INSTS_MFMA'], 1):.2f}")
+    lines += ["", "per-dispatch averages:"]
+    lines += [f"  {c}: {avg[c]:.6g}" for c in sorted(avg)]
+    lines += ["", "commands:"] + [f"  {c}" for c in args.cmds]
+    text = "\n".join(lines) + "\n"
+    open(args.out, "w").write(text)
+    print(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -131,8 +224,16 @@ def main():
     p.add_argument("--M", type=int, required=True)
     p.add_argument("--steps", type=int, required=True,
                    help="forward steps in the counted run (bench.py warmup + steps)")
+    c = sub.add_parser("counters")
+    c.add_argument("--dirs", nargs="+", required=True, help="one directory per --pmc pass")
+    c.add_argument("--trace", required=True, help="directory of a --kernel-trace --stats run")
+    for a in ("match", "kernel", "title", "out"):
+        c.add_argument("--" + a, required=True)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--cmds", nargs="+", default=[])
     args = ap.parse_args()
-    {"ktrace": ktrace, "pmc": pmc}[args.mode](args)
+    {"ktrace": ktrace, "pmc": pmc, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":

@@ -1,8 +1,8 @@
 // Prefill path (M > 32 tokens): the MLP is a dense contraction here, so it
 // runs as two LDS-tiled MFMA GEMMs.
 //
-//   0. RMS pre-pass: n = fp16(gamma * x * r), r = 1/sqrt(mean(x^2) + eps)
-//      (FastTPS review section 3, Figure 4 part1).
+//   0. RMSNorm: n = fp16(gamma * x * r), r = 1/sqrt(mean(x^2) + eps), one
+//      pass over x (FastTPS review section 3, Figure 4 part1).
 //   1. C = n W_gu^T on fp16 MFMA; the epilogue pairs interleaved columns
 //      (gate 2i, up 2i+1) inside each lane and writes a = SiLU(g) * u as
 //      fp16 (Figure 4 part2; the [M, 2ff] gate/up product never reaches HBM).
@@ -46,77 +46,83 @@ __device__ __forceinline__ int64_t act_tile_off(int t, int k, int K) {
 static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
 
 // ---------------------------------------------------------------- RMS pre-pass
-// (a) r_t = 1/sqrt(mean(x_t^2) + eps), one wave per token.
-__global__ __launch_bounds__(256) void k_rms_scale(const uint16_t* __restrict__ x, float eps,
-                                                   float* __restrict__ r, int M, int d,
-                                                   const uint16_t* __restrict__ res) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (t >= M) return;
-  const uint16_t* xr = x + (int64_t)t * d;
-  const uint16_t* rr = res ? res + (int64_t)t * d : nullptr;
+// n = fp16(gamma * x * r), r = 1/sqrt(mean(x^2) + eps), written in the
+// fragment-tiled activation layout; one wave per token slot of the padded
+// token range (slots past M repeat the last token: finite, never stored
+// into an output). Each lane holds chunks lane, lane + 64, ... of the row
+// (kRmsRegs of them in registers, the rest of a very long row re-read), sums
+// their squares in that order, and the wave combines the lane sums; then
+// every chunk is scaled and stored as one 16-byte slot of its fragment.
+// With res, the row is the residual stream h = bf16_rne(x + res), stored to
+// hout once per element.
+constexpr int kRmsRegs = 16;  // chunks of 8 per lane kept in registers (d <= 8192)
+
+__global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ gamma,
+                                                        float eps, uint16_t* __restrict__ n,
+                                                        int M, int d,
+                                                        const uint16_t* __restrict__ res,
+                                                        uint16_t* __restrict__ hout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 8 + (threadIdx.x >> 6);  // token slot (< pad32(M))
+  const int ts = t < M ? t : M - 1;
+  const uint16_t* xr = x + (int64_t)ts * d;
+  const uint16_t* rr = res ? res + (int64_t)ts * d : nullptr;
   const int nch = d >> 3;
-  // kU chunks per lane in flight at once (one load, then its wait, per
-  // chunk would serialise the row's memory latency)
-  constexpr int kU = 8;
+  auto row = [&](int c) {
+    const u32x4 v = ld16(xr + c * 8);
+    return rr ? add_bf16x8(v, ld16(rr + c * 8)) : v;
+  };
+  u32x4 v[kRmsRegs];
+#pragma unroll
+  for (int i = 0; i < kRmsRegs; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < nch ? row(c) : u32x4{0u, 0u, 0u, 0u};
+  }
   float ss = 0.f;
-  for (int c0 = lane; c0 < nch; c0 += 64 * kU) {
-    u32x4 v[kU], rv[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int c = c0 + u * 64;
-      v[u] = c < nch ? ld16(xr + c * 8) : u32x4{0u, 0u, 0u, 0u};
-      if (rr) rv[u] = c < nch ? ld16(rr + c * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < kRmsRegs; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_lo(v[i][j]), hi = bf16_hi(v[i][j]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
     }
+  for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) {  // only for very long rows
+    const u32x4 w = row(c);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const u32x4 w = rr ? add_bf16x8(v[u], rv[u]) : v[u];  // residual stream
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  if (lane == 0) r[t] = 1.0f / sqrtf(ss / (float)d + eps);
-}
-
-// (b) n = fp16(gamma * x * r) in the fragment-tiled layout, one 16-byte slot
-// per thread (consecutive threads write consecutive slots). Slots of padding
-// tokens get the last token's values (finite, never stored).
-__global__ __launch_bounds__(256) void k_rms_tile(const uint16_t* __restrict__ x,
-                                                  const uint16_t* __restrict__ gamma,
-                                                  const float* __restrict__ r,
-                                                  uint16_t* __restrict__ n, int M, int d,
-                                                  int64_t slots, const uint16_t* __restrict__ res,
-                                                  uint16_t* __restrict__ hout) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= slots) return;
-  const int slot = (int)(g & 63);
-  const int64_t frag = g >> 6;                       // = tb * (d/16) + f
-  const int fpb = d >> 4;                            // fragments per token block
-  const int tb = (int)(frag / fpb), f = (int)(frag - (int64_t)tb * fpb);
-  const int t0 = tb * 32 + (slot & 31);
-  const int t = t0 < M ? t0 : M - 1;  // padding tokens repeat the last one
-  const int k = (f >> 1) * 32 + (f & 1) * 16 + (slot >> 5) * 8;
-  u32x4 v = ld16(x + (int64_t)t * d + k);
-  if (res) {  // the residual stream h = bf16_rne(x + res), stored once per element
-    v = add_bf16x8(v, ld16(res + (int64_t)t * d + k));
-    if (t0 < M) st16(hout + (int64_t)t * d + k, v);
-  }
-  const u32x4 gm = ld16(gamma + k);
-  const float rt = r[t];
-  u32x4 o;
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  // chunk c (columns 8c .. 8c+7) of token slot t: fragment (t/32, c/4, (c/2)%2),
+  // slot (c%2)*32 + t%32
+  const int tb = t >> 5, tl = t & 31, nkb = d >> 5;
+  auto put = [&](int c, u32x4 w) {
+    if (hout && t < M) st16(hout + (int64_t)t * d + c * 8, w);
+    const u32x4 gm = ld16(gamma + c * 8);
+    u32x4 o;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const _Float16 lo = (_Float16)(bf16_lo(v[j]) * bf16_lo(gm[j]) * rt);
-    const _Float16 hi = (_Float16)(bf16_hi(v[j]) * bf16_hi(gm[j]) * rt);
-    o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)(bf16_lo(w[j]) * bf16_lo(gm[j]) * r);
+      const _Float16 hi = (_Float16)(bf16_hi(w[j]) * bf16_hi(gm[j]) * r);
+      o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    const int64_t frag = ((int64_t)tb * nkb + (c >> 2)) * 2 + ((c >> 1) & 1);
+    st16(n + frag * 512 + ((c & 1) * 32 + tl) * 8, o);
+  };
+#pragma unroll
+  for (int i = 0; i < kRmsRegs; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nch) put(c, v[i]);
   }
-  st16(n + g * 8, o);
+  for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) put(c, row(c));
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -716,12 +722,12 @@ static GemmPlan plan_down(int64_t M, int64_t d, int64_t ff) {
 }
 
 // Workspace regions, in order (each 256-byte aligned): n fp16 [pad32(M), d]
-// and a fp16 [pad32(M), ff], both fragment-tiled; r fp32 [M]; the down
-// projection's split-K partials fp32 [splits, M, d]. The same for every
+// and a fp16 [pad32(M), ff], both fragment-tiled; the down projection's
+// split-K partials fp32 [splits, M, d]. The same for every
 // weight type (int4 weights are dequantised inside the GEMMs).
 struct PrefillWs {
   uint16_t *n, *a;
-  float *r, *part;
+  float* part;
 };
 
 static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, size_t part_bytes,
@@ -735,7 +741,6 @@ static PrefillWs prefill_ws(char* base, int64_t M, int64_t d, int64_t ff, size_t
   };
   w.n = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * d * 2));
   w.a = reinterpret_cast<uint16_t*>(take((size_t)pad32(M) * ff * 2));
-  w.r = reinterpret_cast<float*>(take((size_t)M * 4));
   w.part = reinterpret_cast<float*>(take(part_bytes));
   *total = off;
   return w;
@@ -801,11 +806,8 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   size_t total = 0;
   const PrefillWs w =
       prefill_ws(p.ws, p.M, p.d, p.ff, split_partial_bytes(p.M, p.d, g2.splits), &total);
-  launch_kernel(KK_RMS_PREP, k_rms_scale, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, stream,
-                p.x, p.eps, w.r, (int)p.M, (int)p.d, p.res);
-  const int64_t slots = pad32(p.M) * p.d / 8;
-  launch_kernel(KK_RMS_TILE, k_rms_tile, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
-                stream, p.x, p.gamma, w.r, w.n, (int)p.M, (int)p.d, slots, p.res, p.hout);
+  launch_kernel(KK_RMS_NORM, k_rms_norm_tiled, dim3((unsigned)(pad32(p.M) / 8)), dim3(512), 0,
+                stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const GemmW wgu{p.w_gu, p.s_gu}, wd{p.w_down, p.s_down};

@@ -19,10 +19,9 @@ enum KernelKind {
   KK_DECODE_DOWN_BF16,
   KK_DECODE_GATEUP_INT4,
   KK_DECODE_DOWN_INT4,
-  KK_RMS_PREP,
   KK_GEMM_GATEUP,
   KK_GEMM_DOWN,
-  KK_RMS_TILE,
+  KK_RMS_NORM,
   KK_SPLITK_REDUCE,
   KK_DECODE_FUSED_BF16,
   KK_PARTIAL_REDUCE,
