@@ -99,16 +99,13 @@ def kernel_bytes(kernel, M, d, ff, wtype, f16=None):
     path at larger M (f16: a prep kernel ran): gate/up reads the prepared
     fp16 n, the product is fp16 (2 bytes per element).
     Single-pass decode: one kernel reads both matrices, x and gamma and
-    writes fp32 partial sums per 32-feature slice of ff, which the reduce
-    kernel reads back to write y."""
+    writes y (its fp32 partial sums per 32-feature slice of ff are scratch
+    traffic inside the launch, not counted, like the decode intermediate)."""
     gu, dn = weight_bytes(d, ff, wtype)
     f16 = wtype == "int4" if f16 is None else f16
     a_elem = 2 if f16 else 4
-    partials = (ff // 32) * M * d * 4  # single-pass decode: fp32 per 32-feature slice
     if kernel == "decode_fused_bf16":
-        return gu + dn + M * d * 2 + d * 2 + partials
-    if kernel == "partial_reduce":
-        return partials + M * d * 2
+        return gu + dn + M * d * 2 + d * 2 + M * d * 2
     if "gateup" in kernel:
         act_in = M * d * 2 + (0 if f16 else d * 2)
         return gu + act_in + M * ff * a_elem
@@ -144,7 +141,6 @@ def kernel_source_sha(kernel):
         "decode_gateup_int4": "decode.hip", "decode_down_int4": "decode.hip",
         "gemm_gateup_silu_f16": "prefill.hip", "gemm_down_f16": "prefill.hip",
         "act_prep": "decode.hip", "decode_fused_bf16": "decode.hip",
-        "partial_reduce": "decode.hip",
     }.get(kernel)
     if src is None:
         return None
@@ -407,7 +403,7 @@ def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True, live_profil
                     "traffic": None if w16 else measured_traffic(dom, wname, M)}
     for name, k in kernels.items():
         t = k["us_per_step"]
-        if name.startswith("decode") or name in ("act_prep", "partial_reduce"):
+        if name.startswith("decode") or name == "act_prep":
             k["gb_per_s"] = round(kernel_bytes(name, M, d, ff, w.wtype,
                                                w.wtype == "int4" or "act_prep" in kernels)
                                   / (t * 1e3), 1)

@@ -116,12 +116,6 @@ static int down_splits(int64_t blocks, int64_t ff, bool int4) {
   return best;
 }
 
-// Single-pass decode: fp32 partial sums [ff/32, M, d] from the start of the
-// workspace.
-size_t fused_partial_bytes(int64_t M, int64_t d, int64_t ff) {
-  return (size_t)(ff / 32) * M * d * 4;
-}
-
 size_t decode_workspace_bytes(int64_t M, int64_t d, int64_t ff) {
   // n fp16 [M, d] (int4 only); a: bf16 hi + lo [M, ff] (int4: fp16 in the
   // first half); split-K partials fp32 [kMaxSplit, M, d]; counters [d/16]
@@ -836,10 +830,9 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
 }
 
 // ------------------------------------------------------------ single pass
-// Gate/up, SiLU*mul and down in one pass over the weights (FastTPS review,
-// section 3: the Fusion MLP keeps the intermediate on chip and moves only
-// the input and the output). Workgroup w owns the 32 features
-// [32w, 32w + 32) of ff:
+// Gate/up, SiLU*mul and down in one launch (FastTPS review, section 3: the
+// Fusion MLP keeps the intermediate on chip and moves only the input and the
+// output). Workgroup w owns the 32 features [32w, 32w + 32) of ff:
 //   1. their 64 interleaved W_gu rows (row blocks 4w .. 4w+3) against
 //      gamma * x, S waves splitting K, the RMS factor folded into the
 //      epilogue exactly as in k_decode_gateup;
@@ -848,25 +841,118 @@ __global__ __launch_bounds__(64 * S) void k_decode_down(
 //   3. the matching 32 columns of W_down (K unit w of every 16-row block,
 //      one 1 KB tile each) against a, each wave taking every S-th row block,
 //      giving the fp32 partial  part[w][t][j] = sum_{i in slice w}
-//      W_down[j][i] a[t][i].
+//      W_down[j][i] a[t][i];
+//   4. the cross-workgroup sum of the nw = ff/32 partials, by arrival, in
+//      two levels: slices are grouped G = ceil(sqrt(nw)) at a time; the last
+//      workgroup of a group to arrive sums its group's partials in slice
+//      order into grp[g], and the last of those sums grp[0 .. ng-1] in group
+//      order into y. The result does not depend on arrival order, and no
+//      workgroup ever waits for another.
 // The down tiles do not depend on a, so each wave issues its first DQ of
 // them as soon as its gate/up loads have landed, before the cross-wave
-// reduction. No workgroup waits for another; k_partial_reduce sums the
-// ff/32 partials afterwards.
+// reduction.
+//
+// Ordering across workgroups (which may sit on different XCDs, whose L2
+// caches are not coherent with each other): partials and group sums are
+// written with agent-scope atomic stores, which the hardware writes through
+// to the device-coherent level and acknowledges only once they are there;
+// each thread then waits for its stores' acknowledgements (s_waitcnt
+// vmcnt(0): on gfx9 the vector memory counter covers stores), the workgroup
+// meets a barrier, and only then does one thread count it in with an
+// agent-scope atomic add, performed at that same level. A workgroup that
+// draws the last ticket therefore counts only after every other member's
+// data is in device-coherent memory, and it reads them with agent-scope
+// atomic loads, which are served from there rather than from a stale line
+// of its own L2. This is the release / acquire pair made explicit per
+// access: a fence instead would write back and invalidate the whole L2.
+//
+// The arrival counters need to start at zero: they live in a library-owned
+// device array (zero when the library loads), and the workgroup that draws a
+// counter's last ticket, the last to touch it in the launch, sets it back to
+// zero. Launches of this path that overlap in time on one GPU would share
+// the counters, so they must not overlap (the path's documented contract).
 // RES: on the residual stream h = bf16_rne(x + res), which workgroup 0 stores
 // to hout; act: the gate activation.
+constexpr int kSpMaxGroups = 128;  // ceil(sqrt(ff/32)) + 1 <= 92 for ff <= 262144
+__device__ unsigned int g_sp_count[kSpMaxGroups + 1];  // per group, then the final level
+
+__host__ __device__ inline int sp_group_size(int nw) {
+  int g = 1;
+  while (g * g < nw) ++g;
+  return g;
+}
+
+// dst[o] (or y[o] as bf16) = sum over k < n of src[k * stride + o], in k
+// order, for o < len; agent-scope loads and stores. A thread takes kSpE
+// outputs at a time (strided by the workgroup size) and keeps 8 loads of each
+// in flight, 8 * kSpE in all, before adding them in order.
+constexpr int kSpE = 4;
+__device__ __forceinline__ void sp_sum(const float* src, int64_t stride, int n, int64_t len,
+                                       float* dst, uint16_t* y) {
+  const int64_t nt = blockDim.x;
+  for (int64_t o0 = threadIdx.x; o0 < len; o0 += nt * kSpE) {
+    float acc[kSpE];
+#pragma unroll
+    for (int e = 0; e < kSpE; ++e) acc[e] = 0.f;
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      float v[kSpE][8];
+#pragma unroll
+      for (int e = 0; e < kSpE; ++e) {
+        const int64_t o = o0 + e * nt < len ? o0 + e * nt : o0;  // re-read, not stored
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int kk = k0 + k < n ? k0 + k : n - 1;  // re-read, not summed
+          v[e][k] = __hip_atomic_load(src + kk * stride + o, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kSpE; ++e)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k0 + k < n) acc[e] += v[e][k];
+    }
+#pragma unroll
+    for (int e = 0; e < kSpE; ++e) {
+      const int64_t o = o0 + e * nt;
+      if (o >= len) break;
+      if (y)
+        y[o] = bf16_rne(acc[e]);
+      else
+        __hip_atomic_store(dst + o, acc[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// This workgroup's arrival at counter c of `members`: true for the last one,
+// which also resets the counter. Call after the workgroup's stores have been
+// issued; all threads must call it.
+__device__ __forceinline__ bool sp_arrive(unsigned int* c, unsigned int members) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int prev =
+        __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == members - 1;
+    if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return last;
+}
+
 template <int S, int P, int DQ, bool RES>
 __global__ __launch_bounds__(64 * S) void k_decode_fused(
     const uint16_t* __restrict__ w_gu, const uint16_t* __restrict__ w_down,
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ gamma, float eps,
-    float* __restrict__ part, int M, int d, int ff, int act, const uint16_t* __restrict__ res,
-    uint16_t* __restrict__ hout) {
+    float* __restrict__ part, float* __restrict__ grp, uint16_t* __restrict__ y, int M, int d,
+    int ff, int act, const uint16_t* __restrict__ res, uint16_t* __restrict__ hout) {
   constexpr int RB = 4;  // 4 x 16 W_gu rows = 32 gate/up pairs
   __shared__ f32x4 red[S * RB * 64];
   __shared__ float ssred[S * 16];
   __shared__ uint32_t abuf[2][16][17];  // [hi, lo][token][feature pair], padded
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int col = lane & 15, grp_l = lane >> 4;
   const int sl = blockIdx.x;
   f32x4 acc[RB][1];
   float ss[1];
@@ -922,14 +1008,15 @@ __global__ __launch_bounds__(64 * S) void k_decode_fused(
     abuf[1][t][pp] = l;
   }
   __syncthreads();
-  // A operand: token col, features 8*grp .. 8*grp+7 of the slice
+  // A operand: token col, features 8*grp_l .. 8*grp_l+7 of the slice
   u32x4 ah, al;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ah[i] = abuf[0][col][grp * 4 + i];
-    al[i] = abuf[1][col][grp * 4 + i];
+    ah[i] = abuf[0][col][grp_l * 4 + i];
+    al[i] = abuf[1][col][grp_l * 4 + i];
   }
-  float* pw = part + (int64_t)sl * M * d;
+  const int64_t md = (int64_t)M * d;
+  float* pw = part + (int64_t)sl * md;
   for (int j0 = 0; j0 < nt; j0 += DQ) {
 #pragma unroll
     for (int q = 0; q < DQ; ++q) {
@@ -942,82 +1029,49 @@ __global__ __launch_bounds__(64 * S) void k_decode_fused(
         const int row = (wave + j * S) * 16 + col;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = grp * 4 + e;
-          if (t < M) pw[(int64_t)t * d + row] = c[e];
+          const int t = grp_l * 4 + e;
+          if (t < M)
+            __hip_atomic_store(pw + (int64_t)t * d + row, c[e], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
   }
+
+  // step 4: the two-level arrival-ordered, order-independent reduction
+  const int nw = (int)gridDim.x, G = sp_group_size(nw), ng = (nw + G - 1) / G;
+  const int g = sl / G, g0 = g * G, members = nw - g0 < G ? nw - g0 : G;
+  if (!sp_arrive(&g_sp_count[g], (unsigned)members)) return;
+  sp_sum(part + (int64_t)g0 * md, md, members, md, grp + (int64_t)g * md, nullptr);
+  if (!sp_arrive(&g_sp_count[kSpMaxGroups], (unsigned)ng)) return;
+  sp_sum(grp, md, ng, md, nullptr, y);
 }
 
-// y[t][j] = bf16( sum over w of part[w][t][j] ). Workgroup: 16 outputs of
-// one token; thread i sums partials w = i, i+256, ... in order, then a fixed
-// two-level combination through LDS (deterministic for a given shape).
-__global__ __launch_bounds__(256) void k_partial_reduce(const float* __restrict__ part,
-                                                        uint16_t* __restrict__ y, int nw, int M,
-                                                        int d) {
-  __shared__ float s1[256][17];
-  __shared__ float s2[16][17];
-  const int j0 = blockIdx.x * 16, t = blockIdx.y;
-  float acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int w = threadIdx.x; w < nw; w += 256) {
-    const float* p = part + ((int64_t)w * M + t) * d + j0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p + 4 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * c + e] += v[e];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s1[threadIdx.x][i] = acc[i];
-  __syncthreads();
-  {
-    const int i = threadIdx.x & 15, c = threadIdx.x >> 4;
-    float v = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) v += s1[c * 16 + k][i];
-    s2[c][i] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    float v = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) v += s2[c][threadIdx.x];
-    y[(int64_t)t * d + j0 + threadIdx.x] = bf16_rne(v);
-  }
-}
-
-// Measured on MI355X, the single pass loses to the two-kernel decode at
-// every workload shape (Phi-3 M=1: 28.1 us for the pass + 4.0 us for the
-// reduction against 30.5 us; Llama-8B M=1: 70.5 against 66.4 us): one
-// 150-350 MB stream runs no faster than the two separate ones, and the
-// partial-sum reduction costs more than the second launch saves. So the
-// automatic choice never takes it; FMLP_PATH_SINGLE_PASS forces it.
 bool single_pass_auto(int64_t M, int64_t d, int64_t ff, int wtype) {
   (void)M, (void)d, (void)ff, (void)wtype;
   return false;
 }
 
+// Single-pass workspace: fp32 partial sums [ff/32, M, d] and group sums
+// [ng, M, d] from the start of the workspace.
+size_t fused_partial_bytes(int64_t M, int64_t d, int64_t ff) {
+  const int nw = (int)(ff / 32), G = sp_group_size(nw), ng = (nw + G - 1) / G;
+  return align256((size_t)nw * M * d * 4) + (size_t)ng * M * d * 4;
+}
+
 hipError_t launch_decode_fused(const Problem& p, hipStream_t stream) {
-  float* part = reinterpret_cast<float*>(p.ws);
   const int nw = p.ff / 32;
+  float* part = reinterpret_cast<float*>(p.ws);
+  float* grp = reinterpret_cast<float*>(p.ws + align256((size_t)nw * p.M * p.d * 4));
   auto go = [&](auto kern) {
-    launch_kernel(KK_DECODE_FUSED_BF16, kern, dim3(nw), dim3(64 * kFuS), 0,
-                  stream, static_cast<const uint16_t*>(p.w_gu),
-                  static_cast<const uint16_t*>(p.w_down), p.x, p.gamma, p.eps, part, p.M, p.d,
-                  p.ff, p.act, p.res, p.hout);
+    launch_kernel(KK_DECODE_FUSED_BF16, kern, dim3(nw), dim3(64 * kFuS), 0, stream,
+                  static_cast<const uint16_t*>(p.w_gu), static_cast<const uint16_t*>(p.w_down),
+                  p.x, p.gamma, p.eps, part, grp, p.y, p.M, p.d, p.ff, p.act, p.res, p.hout);
   };
   if (p.res)
     go(k_decode_fused<kFuS, kFuP, kFuDq, true>);
   else
     go(k_decode_fused<kFuS, kFuP, kFuDq, false>);
-  hipError_t e;
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  launch_kernel(KK_PARTIAL_REDUCE, k_partial_reduce, dim3(p.d / 16, p.M), dim3(256), 0, stream,
-                static_cast<const float*>(part), p.y, nw, p.M, p.d);
   return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ static const char* const kKernelNames[fmlp::KK_COUNT] = {
     "pack_tile", "quantize_int4", "dequant_int4", "act_prep", "decode_gateup_bf16",
     "decode_down_bf16", "decode_gateup_int4", "decode_down_int4",
     "gemm_gateup_silu_f16", "gemm_down_f16", "rms_norm_f16", "splitk_reduce",
-    "decode_fused_bf16", "partial_reduce", "read_probe", "convert_f16"};
+    "decode_fused_bf16", "read_probe", "convert_f16"};
 
 int fmlp_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lock(fmlp::g_mu);

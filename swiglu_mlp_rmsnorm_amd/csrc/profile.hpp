@@ -24,7 +24,6 @@ enum KernelKind {
   KK_RMS_NORM,
   KK_SPLITK_REDUCE,
   KK_DECODE_FUSED_BF16,
-  KK_PARTIAL_REDUCE,
   KK_READ_PROBE,
   KK_CONVERT_F16,
   KK_COUNT
