@@ -66,11 +66,13 @@ enum fmlp_path {
   FMLP_PATH_AUTO = 0,    /* decode kernels for M <= 32, MFMA GEMMs above */
   FMLP_PATH_DECODE = 1,  /* force the decode (weight-streaming) kernels; M <= 32 */
   FMLP_PATH_PREFILL = 2, /* force the tiled MFMA GEMM path; any M */
-  FMLP_PATH_SINGLE_PASS = 3 /* force the single-pass decode (gate/up, SiLU*mul
-                               and down in one kernel over the weights, then a
-                               reduction of per-slice partial sums; FastTPS
-                               review, section 3, Fusion MLP); bf16 weights,
-                               M <= 8 */
+  FMLP_PATH_SINGLE_PASS = 3 /* force the single-pass decode: gate/up, SiLU*mul,
+                               down and the cross-workgroup sum of per-slice
+                               partials in one launch (FastTPS review,
+                               section 3, Fusion MLP); bf16 weights, M <= 8.
+                               Its arrival counters are library-owned device
+                               memory: single-pass calls must not overlap in
+                               time on one GPU */
 };
 
 enum fmlp_activation {
