@@ -49,6 +49,7 @@
 #include <cstdint>
 #include <cstring>
 #include <cfenv>
+#include <vector>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -407,41 +408,67 @@ struct WeightView {
 // h = bf16_rne(x + res) when res is given (then also written to h_out when
 // that is given). gate row i is (g_view, g_row0 + g_stride*i), up row i
 // likewise.
+//
+// Every output is one sum over k ascending. Tokens are taken kTokenChunk at a
+// time; within a chunk the loops run over weight rows outermost, so each row's
+// values are read once per chunk and used for each of its tokens. The sum of
+// each (token, output) pair is the same sequence of operations whatever the
+// loop order or the thread that runs it.
 static void forward_core(const uint16_t* x, const uint16_t* res, uint16_t* h_out,
                          const uint16_t* gamma, double eps, int act,
                          const WeightView& gv, int64_t g_row0, int64_t g_stride,
                          const WeightView& uv, int64_t u_row0, int64_t u_stride,
                          const WeightView& dv, int64_t M, int64_t d, int64_t ff,
                          double* y) {
-  double* n = new double[d];
-  double* a = new double[ff];
-  uint16_t* h = new uint16_t[d];
-  for (int64_t m = 0; m < M; ++m) {
-    const uint16_t* xm = x + m * d;
-    if (res) {
-      oracle_residual_add(xm, res + m * d, d, h);
-      if (h_out) std::memcpy(h_out + m * d, h, (size_t)d * sizeof(uint16_t));
-      xm = h;
+  constexpr int64_t kTokenChunk = 16;
+  std::vector<double> n((size_t)(kTokenChunk * d));
+  std::vector<double> a((size_t)(kTokenChunk * ff));
+  std::vector<uint16_t> h((size_t)d);
+  for (int64_t m0 = 0; m0 < M; m0 += kTokenChunk) {
+    const int64_t mc = M - m0 < kTokenChunk ? M - m0 : kTokenChunk;
+    for (int64_t m = 0; m < mc; ++m) {
+      const uint16_t* xm = x + (m0 + m) * d;
+      if (res) {
+        oracle_residual_add(xm, res + (m0 + m) * d, d, h.data());
+        if (h_out) std::memcpy(h_out + (m0 + m) * d, h.data(), (size_t)d * sizeof(uint16_t));
+        xm = h.data();
+      }
+      oracle_rmsnorm(xm, gamma, eps, 1, d, n.data() + m * d);
     }
-    oracle_rmsnorm(xm, gamma, eps, 1, d, n);
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < ff; ++i) {
-      double g = 0.0, u = 0.0;
-      const int64_t gr = g_row0 + g_stride * i, ur = u_row0 + u_stride * i;
-      for (int64_t k = 0; k < d; ++k) g += gv.at(gr, k) * n[k];
-      for (int64_t k = 0; k < d; ++k) u += uv.at(ur, k) * n[k];
-      a[i] = gate_act(act, g) * u;
+#pragma omp parallel
+    {
+      std::vector<double> wg((size_t)d), wu((size_t)d);
+#pragma omp for schedule(static)
+      for (int64_t i = 0; i < ff; ++i) {
+        const int64_t gr = g_row0 + g_stride * i, ur = u_row0 + u_stride * i;
+        for (int64_t k = 0; k < d; ++k) wg[k] = gv.at(gr, k);
+        for (int64_t k = 0; k < d; ++k) wu[k] = uv.at(ur, k);
+        for (int64_t m = 0; m < mc; ++m) {
+          const double* nm = n.data() + m * d;
+          double g = 0.0, u = 0.0;
+          for (int64_t k = 0; k < d; ++k) {
+            g += wg[k] * nm[k];
+            u += wu[k] * nm[k];
+          }
+          a[m * ff + i] = gate_act(act, g) * u;
+        }
+      }
     }
-#pragma omp parallel for schedule(static)
-    for (int64_t j = 0; j < d; ++j) {
-      double acc = 0.0;
-      for (int64_t i = 0; i < ff; ++i) acc += dv.at(j, i) * a[i];
-      y[m * d + j] = acc;
+#pragma omp parallel
+    {
+      std::vector<double> wd((size_t)ff);
+#pragma omp for schedule(static)
+      for (int64_t j = 0; j < d; ++j) {
+        for (int64_t i = 0; i < ff; ++i) wd[i] = dv.at(j, i);
+        for (int64_t m = 0; m < mc; ++m) {
+          const double* am = a.data() + m * ff;
+          double acc = 0.0;
+          for (int64_t i = 0; i < ff; ++i) acc += wd[i] * am[i];
+          y[(m0 + m) * d + j] = acc;
+        }
+      }
     }
   }
-  delete[] n;
-  delete[] a;
-  delete[] h;
 }
 
 // Eq(1) from separate gate and up matrices (the unfused ordering), with the

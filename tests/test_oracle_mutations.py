@@ -15,7 +15,7 @@ MUTATIONS = {
     "gamma_dropped": ("* r * bf16_value(gamma[k])", "* r"),
     "gate_up_rows_swapped": ("gu, 0, 2, gu, 1, 2", "gu, 1, 2, gu, 0, 2"),
     "silu_on_up_branch": ("gate_act(act, g) * u", "gate_act(act, u) * g"),
-    "w_down_transposed": ("acc += dv.at(j, i) * a[i]", "acc += dv.at(i % dv.K, j % ff) * a[i]"),
+    "w_down_transposed": ("wd[i] = dv.at(j, i);", "wd[i] = dv.at((i * d + j) / ff, (i * d + j) % ff);"),
     "round_half_away": ("float rq = std::nearbyint(ratio_k);", "float rq = std::round(ratio_k);"),
     "nibble_order_swapped": ("const uint8_t byte = qrow[k / 2];\n  const int nib = (k & 1) ? (byte >> 4) : (byte & 0xF);",
                              "const uint8_t byte = qrow[k / 2];\n  const int nib = (k & 1) ? (byte & 0xF) : (byte >> 4);"),
@@ -27,7 +27,7 @@ MUTATIONS = {
     "gelu_tanh_cubic_coefficient": ("0.044715 * t * t * t", "0.0447 * t * t * t"),
     "gelu_forms_swapped": ("if (act == 1) return oracle_gelu_tanh(t);", "if (act == 1) return oracle_gelu_erf(t);"),
     "bf16_round_toward_zero": ("std::nearbyint(std::ldexp(a, 8 - e2))", "std::trunc(std::ldexp(a, 8 - e2))"),
-    "residual_not_normalised": ("      xm = h;\n", "      (void)xm;\n"),
+    "residual_not_normalised": ("      xm = h.data();\n", "      (void)xm;\n"),
     "f16_subnormal_rounds_nearest": ("std::floor(std::ldexp(a, 24))", "std::nearbyint(std::ldexp(a, 24))"),
     "f16_sign_dropped": ("out[i] = (uint16_t)((w[i] & 0x8000u) | bits);", "out[i] = bits;"),
     "f16_exponent_bias": ("(((e2 - 1 + 15) << 10)", "(((e2 - 1 + 16) << 10)"),
