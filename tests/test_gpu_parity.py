@@ -154,6 +154,9 @@ def test_both_paths_at_the_crossover(tiny, M, path):
                                     # staged gate/up activations with more chunks than
                                     # the staging registers hold
                                     (4096, 1024, 3),
+                                    # a K split of the down projection whose equal
+                                    # slices would leave the last one empty
+                                    (32, 3104, 1),
                                     # 2ff/16 = 1032 row blocks: the eight-block gate/up
                                     # workgroups at two token blocks (M > 16)
                                     (64, 8256, 17), (64, 8256, 32), (64, 8256, 9),
@@ -266,7 +269,11 @@ def test_decode_int4_ragged(M):
                                     # than the staging registers hold: gate/up at d=8192,
                                     # and a 4-way K-split down projection at ff=20480
                                     (8192, 256, 3), (1024, 20480, 4), (1024, 20480, 2),
-                                    (4096, 1056, 1)])
+                                    (4096, 1056, 1),
+                                    # a K split of the down projection whose equal
+                                    # slices would leave the last one empty (25 K units
+                                    # over 6 slices): the split count is recomputed
+                                    (32, 3104, 1), (32, 3104, 3)])
 def test_decode_int4_shapes(d, ff, M):
     layer = Int4Layer(d, ff, 40 + d)
     x, g = bf16_inputs(M, d, 550 + M)
@@ -277,7 +284,7 @@ def test_decode_int4_shapes(d, ff, M):
                                     (200, F.FMLP_PATH_AUTO), (1, F.FMLP_PATH_PREFILL),
                                     (32, F.FMLP_PATH_PREFILL)])
 def test_prefill_int4(M, path):
-    # int4 on the MFMA path: weights expanded to fp16 tiles, then the GEMMs
+    # int4 on the MFMA path: the GEMMs dequantise the codes in their operand path
     layer = Int4Layer(TINY_D, TINY_FF, 31)
     x, g = bf16_inputs(M, TINY_D, 800 + M)
     assert_parity(layer.forward(x, g, EPS, path=path), layer.oracle(x, g, EPS),
