@@ -55,14 +55,24 @@ static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
 // every chunk is scaled and stored as one 16-byte slot of its fragment.
 // With res, the row is the residual stream h = bf16_rne(x + res), stored to
 // hout once per element.
+// STAGE (d <= 8192): the 8 token slots of a workgroup fill whole 128-byte
+// lines of each fragment (slots 8j .. 8j+7 of one column chunk), so the
+// scaled chunks go through LDS first and each store instruction then writes
+// 8 whole lines, rather than 64 scattered 16-byte pieces of 64 lines (one
+// per token row chunk). LDS position of chunk c of the workgroup's token w:
+// 8c + (w ^ c % 8), conflict-free for both the row-wise writes and the
+// line-wise reads.
 constexpr int kRmsRegs = 16;  // chunks of 8 per lane kept in registers (d <= 8192)
+constexpr int kRmsStageMaxD = 8192;
 
+template <bool STAGE>
 __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ gamma,
                                                         float eps, uint16_t* __restrict__ n,
                                                         int M, int d,
                                                         const uint16_t* __restrict__ res,
                                                         uint16_t* __restrict__ hout) {
+  extern __shared__ u32x4 rms_lds[];  // STAGE: 8 d / 8 chunks of 16 bytes
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 8 + (threadIdx.x >> 6);  // token slot (< pad32(M))
   const int ts = t < M ? t : M - 1;
@@ -114,15 +124,30 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
       o[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
              ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    const int64_t frag = ((int64_t)tb * nkb + (c >> 2)) * 2 + ((c >> 1) & 1);
-    st16(n + frag * 512 + ((c & 1) * 32 + tl) * 8, o);
+    if constexpr (STAGE) {
+      rms_lds[c * 8 + ((threadIdx.x >> 6) ^ (c & 7))] = o;
+    } else {
+      const int64_t frag = ((int64_t)tb * nkb + (c >> 2)) * 2 + ((c >> 1) & 1);
+      st16(n + frag * 512 + ((c & 1) * 32 + tl) * 8, o);
+    }
   };
 #pragma unroll
   for (int i = 0; i < kRmsRegs; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) put(c, v[i]);
   }
-  for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) put(c, row(c));
+  if constexpr (STAGE) {
+    __syncthreads();
+    // position p holds chunk c = p / 8 of token slot 8 blockIdx.x + (p % 8 ^ c % 8)
+    const int tl0 = (blockIdx.x * 8) & 31;
+    for (int p = threadIdx.x; p < nch * 8; p += 512) {
+      const int c = p >> 3, w = (p & 7) ^ (c & 7);
+      const int64_t frag = ((int64_t)tb * nkb + (c >> 2)) * 2 + ((c >> 1) & 1);
+      st16(n + frag * 512 + ((c & 1) * 32 + tl0 + w) * 8, rms_lds[p]);
+    }
+  } else {
+    for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) put(c, row(c));
+  }
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -806,8 +831,22 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
   size_t total = 0;
   const PrefillWs w =
       prefill_ws(p.ws, p.M, p.d, p.ff, split_partial_bytes(p.M, p.d, g2.splits), &total);
-  launch_kernel(KK_RMS_NORM, k_rms_norm_tiled, dim3((unsigned)(pad32(p.M) / 8)), dim3(512), 0,
-                stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
+  const dim3 rgrid((unsigned)(pad32(p.M) / 8));
+  if (p.d <= kRmsStageMaxD) {
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rms_norm_tiled<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     16 * kRmsStageMaxD);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<true>, rgrid, dim3(512), (uint32_t)(16 * p.d),
+                  stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
+  } else {
+    launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<false>, rgrid, dim3(512), 0, stream, p.x,
+                  p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const GemmW wgu{p.w_gu, p.s_gu}, wd{p.w_down, p.s_down};

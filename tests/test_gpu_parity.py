@@ -149,6 +149,9 @@ def test_both_paths_at_the_crossover(tiny, M, path):
 @pytest.mark.parametrize("d,ff,M", [(32, 32, 1), (64, 96, 3), (96, 160, 40), (512, 1376, 5),
                                     (512, 1376, 70), (160, 224, 17), (256, 4096, 100),
                                     (288, 2048, 33), (256, 38400, 33),
+                                    # d past 8192: the prefill RMSNorm stores each token
+                                    # row without staging the workgroup's rows in LDS
+                                    (8224, 512, 40),
                                     # >= 768 gate/up workgroups: the 4-wave gate/up launch
                                     (256, 6144, 1), (96, 6176, 3),
                                     # staged gate/up activations with more chunks than
