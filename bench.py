@@ -146,8 +146,17 @@ def kernel_source_sha(kernel):
         return None
     h = hashlib.sha256()
     for f in (src, "device_common.hpp"):
-        h.update(open(os.path.join(ROOT, "swiglu_mlp_rmsnorm_amd", "csrc", f), "rb").read())
+        text = open(os.path.join(ROOT, "swiglu_mlp_rmsnorm_amd", "csrc", f)).read()
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
+
+
+def code_only(text):
+    """A C++ source without its comments and blank lines, so that editing a
+    comment does not expire a measurement of the code."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
 
 
 def measured_traffic(kernel, workload, M):

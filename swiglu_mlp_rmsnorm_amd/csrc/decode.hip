@@ -33,8 +33,11 @@
 // fp16 normal range), and half the activation bytes per workgroup, which at
 // that M match the weight bytes.
 //
-// int4 weights: one fp16 MFMA per group. A word holds the 8 codes a lane
-// needs; with u = word ^ 0x88888888 each nibble is q+8, and
+// int4 weights: one fp16 MFMA per group. The conversion is the published
+// magic-number int4 -> fp16 method (Kim et al., "Who Says Elephants Can't
+// Run", arXiv 2211.10017): a 4-bit field placed under the fp16 exponent of
+// 1024 is an exact fp16 integer. A word holds the 8 codes a lane needs; with
+// u = word ^ 0x88888888 each nibble is q+8, and
 //   (u & 0x000F000F) | 0x64006400 -> fp16 (1032 + q0, 1032 + q4)
 //   (u & 0x00F000F0) | 0x64006400 -> fp16 (1152 + 16 q1, 1152 + 16 q5)
 // (and the same on u >> 8 for codes 2,6 / 3,7): six VALU operations per 8

@@ -276,7 +276,9 @@ __device__ __forceinline__ void buf_load_lds(const void* base, int extent, lptr_
 // Eight int4 codes (one 32-bit word, code m in bits 4m..4m+3, two's
 // complement) and their fp16 group scale -> the eight weights s*q as fp16 in
 // natural order, each the exact product rounded once to nearest even: the
-// same value as fp16(float(s) * q). With t = w ^ 0x88888888 every nibble is
+// same value as fp16(float(s) * q). The magic-number int4 -> fp16 method
+// (Kim et al., arXiv 2211.10017), with a byte permute to place the nibbles:
+// with t = w ^ 0x88888888 every nibble is
 // q + 8; v_perm places nibbles 2j and 2j+1 in the low bytes of the two halves
 // of word j, and with 0x6400 in the high bytes the halves are the fp16
 // values 1024 + q + 8 (exact); a packed fp16 add of -1032 leaves q exactly,
