@@ -230,9 +230,10 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  *                             fmlp_pack_int4_interleaved for W_gu and
  *                             fmlp_pack_int4_matrix for W_down). Decode
  *                             (M <= 32) dequantises in registers, exactly;
- *                             prefill first expands both matrices to fp16
- *                             tiles in the workspace (s*q rounded once to
- *                             fp16), so its workspace holds 6*ff*d bytes more
+ *                             prefill dequantises inside its GEMMs, each
+ *                             weight fp16(s*q) (the exact product rounded
+ *                             once to nearest even) right before its MFMAs,
+ *                             with no expanded copy and no extra workspace
  *                FMLP_W_F16: w_gu and w_down as for FMLP_W_BF16, converted
  *                             by fmlp_convert_f16; scales ignored. Decode
  *                             takes fp16 n and a at every M (one RMSNorm
@@ -246,8 +247,8 @@ size_t fmlp_workspace_size(int64_t M, int64_t d, int64_t ff, int32_t wtype);
  * Accumulation is fp32. The normalised input and the SiLU*mul intermediate
  * are kept as bf16 hi + lo pairs (about 2^-17 relative, the range of fp32)
  * on the bf16 decode path up to 16 tokens, and as fp16 on every other path
- * (the prefill path also converts bf16 weights, or s*q, to fp16 the way
- * fmlp_convert_f16 does). On those paths an intermediate beyond +-65504
+ * (the prefill path also converts bf16 weights to fp16 the way
+ * fmlp_convert_f16 does, and int4 weights to fp16(s*q) as above). On those paths an intermediate beyond +-65504
  * becomes +-inf, so that row of y comes out non-finite (inf or NaN), never
  * a finite wrong value; magnitudes below 2^-14 lose relative precision
  * gradually (fp16 subnormals).
