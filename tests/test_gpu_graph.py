@@ -1,6 +1,7 @@
-"""The forward under HIP graph capture: a captured fmlp_forward replays
-several times, with the program's own eager work and synchronisations in
-between, and every replay equals the eager result bit for bit (the library
+"""The forward under HIP graph capture: a captured fmlp_forward (or
+fmlp_forward_noalloc) replays several times, with the program's own eager
+work and synchronisations in between, and every replay equals the eager
+result bit for bit (the library
 clears its split-K counters with a kernel, not a memset, and allocates
 nothing, so a captured call is a fixed sequence of kernels)."""
 import pytest
@@ -70,3 +71,23 @@ def test_graph_replay_int4_with_residual(M):
         layer.forward_ex(x, g, EPS, y=y, workspace=ws, activation=F.FMLP_ACT_GELU_TANH,
                          residual=res, h_out=h, stream=torch.cuda.current_stream())
     _graph_matches_eager(run, [y, h])
+
+
+@pytest.mark.parametrize("d,ff,M", [(1024, 2048, 1),     # decode, split-K down (counters)
+                                    (256, 704, 70)])     # prefill
+def test_graph_replay_noalloc(d, ff, M):
+    # the entry point without a workspace is meant for captured code: every
+    # replay reuses the library's device scratch and equals the eager result
+    layer = Bf16Layer(d, ff, 86)
+    x, g = bf16_inputs(M, d, 87)
+    y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        F.fmlp_forward_noalloc(x, g, EPS, layer.wgu_t, layer.wd_t, y=y,
+                               stream=torch.cuda.current_stream())
+    _graph_matches_eager(run, [y])
+    ws = torch.empty(F.fmlp_workspace_size(M, d, ff, F.FMLP_W_BF16), dtype=torch.uint8,
+                     device="cuda")
+    y_ws = F.fmlp_forward(x, g, EPS, layer.wgu_t, layer.wd_t, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_ws.view(torch.int16))
