@@ -50,7 +50,7 @@ static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
 // fragment-tiled activation layout; one wave per token slot of the padded
 // token range (slots past M repeat the last token: finite, never stored
 // into an output). Each lane holds chunks lane, lane + 64, ... of the row
-// (kRmsRegs of them in registers, the rest of a very long row re-read), sums
+// (R of them in registers, the rest of a very long row re-read), sums
 // their squares in that order, and the wave combines the lane sums; then
 // every chunk is scaled and stored as one 16-byte slot of its fragment.
 // With res, the row is the residual stream h = bf16_rne(x + res), stored to
@@ -62,10 +62,12 @@ static inline int64_t pad32(int64_t m) { return (m + 31) & ~(int64_t)31; }
 // per token row chunk). LDS position of chunk c of the workgroup's token w:
 // 8c + (w ^ c % 8), conflict-free for both the row-wise writes and the
 // line-wise reads.
-constexpr int kRmsRegs = 16;  // chunks of 8 per lane kept in registers (d <= 8192)
+// R: chunks of 8 per lane kept in registers, 8 for rows up to d = 4096 and
+// 16 up to 8192 (sized to the row, so that short rows leave registers for
+// more waves per CU).
 constexpr int kRmsStageMaxD = 8192;
 
-template <bool STAGE>
+template <bool STAGE, int R>
 __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ gamma,
                                                         float eps, uint16_t* __restrict__ n,
@@ -83,22 +85,22 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
     const u32x4 v = ld16(xr + c * 8);
     return rr ? add_bf16x8(v, ld16(rr + c * 8)) : v;
   };
-  u32x4 v[kRmsRegs];
+  u32x4 v[R];
 #pragma unroll
-  for (int i = 0; i < kRmsRegs; ++i) {
+  for (int i = 0; i < R; ++i) {
     const int c = lane + 64 * i;
     v[i] = c < nch ? row(c) : u32x4{0u, 0u, 0u, 0u};
   }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kRmsRegs; ++i)
+  for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float lo = bf16_lo(v[i][j]), hi = bf16_hi(v[i][j]);
       ss = fmaf(lo, lo, ss);
       ss = fmaf(hi, hi, ss);
     }
-  for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) {  // only for very long rows
+  for (int c = lane + 64 * R; c < nch; c += 64) {  // only for very long rows
     const u32x4 w = row(c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
     }
   };
 #pragma unroll
-  for (int i = 0; i < kRmsRegs; ++i) {
+  for (int i = 0; i < R; ++i) {
     const int c = lane + 64 * i;
     if (c < nch) put(c, v[i]);
   }
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
       st16(n + frag * 512 + ((c & 1) * 32 + tl0 + w) * 8, rms_lds[p]);
     }
   } else {
-    for (int c = lane + 64 * kRmsRegs; c < nch; c += 64) put(c, row(c));
+    for (int c = lane + 64 * R; c < nch; c += 64) put(c, row(c));
   }
 }
 
@@ -838,15 +840,24 @@ hipError_t launch_prefill(const Problem& p, hipStream_t stream) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [] {
-      attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rms_norm_tiled<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     16 * kRmsStageMaxD);
+      for (const void* k : {reinterpret_cast<const void*>(&k_rms_norm_tiled<true, 8>),
+                            reinterpret_cast<const void*>(&k_rms_norm_tiled<true, 16>)}) {
+        const hipError_t e = hipFuncSetAttribute(
+            k, hipFuncAttributeMaxDynamicSharedMemorySize, 16 * kRmsStageMaxD);
+        if (e != hipSuccess) attr_err = e;
+      }
     });
     if (attr_err != hipSuccess) return attr_err;
-    launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<true>, rgrid, dim3(512), (uint32_t)(16 * p.d),
-                  stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
+    if (p.d <= 4096)
+      launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<true, 8>, rgrid, dim3(512),
+                    (uint32_t)(16 * p.d), stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d,
+                    p.res, p.hout);
+    else
+      launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<true, 16>, rgrid, dim3(512),
+                    (uint32_t)(16 * p.d), stream, p.x, p.gamma, p.eps, w.n, (int)p.M, (int)p.d,
+                    p.res, p.hout);
   } else {
-    launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<false>, rgrid, dim3(512), 0, stream, p.x,
+    launch_kernel(KK_RMS_NORM, k_rms_norm_tiled<false, 16>, rgrid, dim3(512), 0, stream, p.x,
                   p.gamma, p.eps, w.n, (int)p.M, (int)p.d, p.res, p.hout);
   }
   hipError_t e = hipGetLastError();
