@@ -309,14 +309,16 @@ __device__ __forceinline__ u32x4 int4x8_to_f16x8(uint32_t w, uint32_t s16) {
 // no redundant waits.
 constexpr int wait_vm_lgkm0(int vm) { return (vm & 15) | 0x70 | ((vm >> 4) << 14); }
 
-// WKW: weight kind (WF_*). Wt: weight tiles, or int4 code super-tiles with
-// Wsc their fp16 scales (unused otherwise).
+// One workgroup's tile: the pid-th of the tiles of feature rows n_begin ..
+// n_end-1 (and K slice blockIdx.y of gridDim.y). WKW: weight kind (WF_*).
+// Wt: weight tiles, or int4 code super-tiles with Wsc their fp16 scales
+// (unused otherwise).
 template <int NB, int MB, int WGN, int WGM, int EPI, int WKW>
-__global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
-    GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
-k_gemm_wf16(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
-            const uint16_t* __restrict__ Act, void* __restrict__ out, int M, int N, int K,
-            int n_begin, int n_end) {
+__device__ __forceinline__ void gemm_tile(const void* __restrict__ Wt,
+                                          const uint16_t* __restrict__ Wsc,
+                                          const uint16_t* __restrict__ Act,
+                                          void* __restrict__ out, int M, int N, int K,
+                                          int n_begin, int n_end, int pid) {
   using C = GemmCfg<NB, MB, WGN, WGM, WKW>;
   extern __shared__ __align__(16) uint16_t lds[];
 
@@ -327,7 +329,6 @@ k_gemm_wf16(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
   // this launch covers feature rows n_begin .. n_end-1 of the N
   const int nN = (n_end - n_begin + C::BN - 1) / C::BN, nM = (M + C::BM - 1) / C::BM;
   const int T = nN * nM;
-  const int pid = blockIdx.x;
   const int xcd = pid & 7, idx = pid >> 3;
   const int per = T >> 3, rem = T & 7;
   const int tile = xcd * per + (xcd < rem ? xcd : rem) + idx;
@@ -613,6 +614,38 @@ k_gemm_wf16(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
   }
 }
 
+template <int NB, int MB, int WGN, int WGM, int EPI, int WKW>
+__global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
+    GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
+k_gemm_wf16(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
+            const uint16_t* __restrict__ Act, void* __restrict__ out, int M, int N, int K,
+            int n_begin, int n_end) {
+  gemm_tile<NB, MB, WGN, WGM, EPI, WKW>(Wt, Wsc, Act, out, M, N, K, n_begin, n_end,
+                                        (int)blockIdx.x);
+}
+
+// One launch for a GEMM whose last feature rows run as lower tiles:
+// workgroups below n_main_wgs take the NB x MB tiles of rows 0 .. n_main-1,
+// the others the NB x MBT tiles of rows n_main .. N-1. Workgroups are
+// dispatched in index order as CUs free up, so the lower tiles start while
+// the last full ones drain, with no kernel boundary between them (a launch
+// each measured about 4 us apart on MI355X). n_main_wgs is a multiple of 8,
+// which keeps both parts' XCD-major tile order.
+template <int NB, int MB, int MBT, int WGN, int WGM, int WGMT, int EPI, int WKW>
+__global__ __launch_bounds__(64 * WGN * WGM) __attribute__((amdgpu_waves_per_eu(
+    GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU, GemmCfg<NB, MB, WGN, WGM>::WAVES_PER_EU))) void
+k_gemm_wf16_tail(const void* __restrict__ Wt, const uint16_t* __restrict__ Wsc,
+                 const uint16_t* __restrict__ Act, void* __restrict__ out, int M, int N, int K,
+                 int n_main, int n_main_wgs) {
+  static_assert(WGN * WGM == WGN * WGMT, "both parts run on the same workgroup size");
+  if ((int)blockIdx.x < n_main_wgs)
+    gemm_tile<NB, MB, WGN, WGM, EPI, WKW>(Wt, Wsc, Act, out, M, N, K, 0, n_main,
+                                          (int)blockIdx.x);
+  else
+    gemm_tile<NB, MBT, WGN, WGMT, EPI, WKW>(Wt, Wsc, Act, out, M, N, K, n_main, N,
+                                            (int)blockIdx.x - n_main_wgs);
+}
+
 // y = bf16(sum over the split-K partials, in slice order): deterministic.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part,
                                                        uint16_t* __restrict__ y, int64_t n4,
@@ -650,6 +683,31 @@ static hipError_t launch_gemm_t(GemmW W, const uint16_t* Act, void* out, int M, 
   launch_kernel(epi_gate(EPI) ? KK_GEMM_GATEUP : KK_GEMM_DOWN,
                 k_gemm_wf16<NB, MB, WGN, WGM, EPI, WKW>, dim3(tiles, splits), dim3(C::THREADS),
                 (uint32_t)C::LDS_BYTES, stream, W.w, W.s, Act, out, M, N, K, n_begin, n_end);
+  return hipGetLastError();
+}
+
+// The 256 x 256 tiles of rows 0 .. n_main-1 and the 256 x 128 tiles of the
+// rest in one launch (gate/up GEMMs: both on 8 waves, 4 x 2).
+template <int EPI, int WKW>
+static hipError_t launch_gemm_main_tail(GemmW W, const uint16_t* Act, void* out, int M, int N,
+                                        int K, int n_main, hipStream_t stream) {
+  using C0 = GemmCfg<8, 8, 4, 2, WKW>;
+  using C1 = GemmCfg<8, 4, 4, 2, WKW>;
+  static_assert(C0::LDS_BYTES >= C1::LDS_BYTES, "LDS");
+  auto kern = k_gemm_wf16_tail<8, 8, 4, 4, 2, 2, EPI, WKW>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [kern] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)C0::LDS_BYTES);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  const int nM0 = (M + 255) / 256, nM1 = (M + 127) / 128;
+  const int main_wgs = (n_main / 256) * nM0;
+  const int tail_wgs = ((N - n_main + 255) / 256) * nM1;
+  launch_kernel(KK_GEMM_GATEUP, kern, dim3(main_wgs + tail_wgs), dim3(C0::THREADS),
+                (uint32_t)C0::LDS_BYTES, stream, W.w, W.s, Act, out, M, N, K, n_main, main_wgs);
   return hipGetLastError();
 }
 
@@ -706,6 +764,11 @@ template <int EPI, int WKW>
 static hipError_t launch_gemm_plan(const GemmPlan& g, GemmW W, const uint16_t* Act, void* out,
                                    int M, int N, int K, hipStream_t stream) {
   const int n_main = N - g.tail_rows;
+  // gate/up: the 256 x 256 tiles and the 256 x 128 tail tiles share a launch
+  if constexpr (epi_gate(EPI) && kS0Wgn == 4 && kS0Wgm == 2 && kS1Wgm == 2) {
+    if (g.tail_rows > 0 && g.shape == 0 && g.splits == 1 && n_main > 0)
+      return launch_gemm_main_tail<EPI, WKW>(W, Act, out, M, N, K, n_main, stream);
+  }
   hipError_t e = hipSuccess;
   if (n_main > 0) {
     // the down GEMM runs the 256 x 256 tile on 4 waves, the gate/up GEMM on
