@@ -7,7 +7,8 @@ CPU oracle consume what it returns (the oracle through host copies), so the
 two sides see bit-identical inputs.
 
 Workloads (synthetic stand-ins for the models the pages measure: Phi-3-mini,
-Llama-3.1-8B and Llama-70B shaped layers; no checkpoint or dataset is used):
+Llama-3.1-8B and Llama-70B shaped layers, and one GPU's tensor-parallel share
+of the last two; no checkpoint or dataset is used):
   x ~ N(0,1), gamma = 1 + N(0,0.1), W_gate / W_up / W_down ~ N(0,0.02), all
   rounded to bf16 (RNE); eps = 1e-5. int4 layers, in the row-major exchange
   format (codes [rows, K/2], scales [rows, K/32]): every packed byte uniform
@@ -46,6 +47,13 @@ WORKLOADS = {
         Workload("llama8b_decode_d4096_ff14336", 2, 4096, 14336, (1, 4, 16, 32), 32, "bf16"),
         Workload("llama8b_prefill_d4096_ff14336", 3, 4096, 14336, (512, 2048), 1, "bf16"),
         Workload("llama70b_int4_decode_d8192_ff28672", 4, 8192, 28672, (1, 16), 20, "int4"),
+        # one GPU's share of the two decode layers under 8-way tensor
+        # parallelism over ff (each GPU holds ff/8 gate/up pairs and the
+        # matching W_down columns; the partial y of the eight would then be
+        # summed across GPUs): 44 MB and 50 MB of weights per set, 16 sets
+        Workload("llama8b_tp8_shard_decode_d4096_ff1792", 5, 4096, 1792, (1, 16), 16, "bf16"),
+        Workload("llama70b_int4_tp8_shard_decode_d8192_ff3584", 6, 8192, 3584, (1, 16), 16,
+                 "int4"),
     )
 }
 

@@ -80,7 +80,8 @@ def test_full_size_parity_all_rows(wname, M, layer):
 @pytest.mark.parametrize("wname,M", [("phi3mini_decode_d3072_ff8192", 1),
                                      ("phi3mini_decode_d3072_ff8192", 8),
                                      ("llama8b_decode_d4096_ff14336", 1),
-                                     ("llama8b_decode_d4096_ff14336", 4)])
+                                     ("llama8b_decode_d4096_ff14336", 4),
+                                     ("llama8b_tp8_shard_decode_d4096_ff1792", 1)])
 def test_full_size_single_pass_all_rows(wname, M):
     w = synth.WORKLOADS[wname]
     L = FullLayer(w, 0)
