@@ -392,3 +392,36 @@ def test_residual_stream_bit_exact_at_larger_d(d, ff, M):
     # d = 18432 makes the int4 prep take its second pass over the row
     _check_ex(Bf16Layer(d, ff, 62), M, d, F.FMLP_ACT_GELU_ERF, True, 960 + M)
     _check_ex(Int4Layer(d, ff, 63), M, d, F.FMLP_ACT_SILU, True, 970 + M)
+
+
+# 2 ff / 256 = 258 bands of gate/up rows at one token tile: one round of
+# 256 x 256 tiles and the last two bands as 256 x 128 tail tiles, both in
+# the gate/up GEMM's single launch, for every weight kind and gate epilogue
+TAIL_D, TAIL_FF, TAIL_M = 64, 33024, 40
+
+
+@pytest.fixture(scope="module")
+def tail_layers():
+    from parity_util import F16Layer
+    return {"bf16": Bf16Layer(TAIL_D, TAIL_FF, 91), "f16": F16Layer(TAIL_D, TAIL_FF, 91),
+            "int4": Int4Layer(TAIL_D, TAIL_FF, 92)}
+
+
+@pytest.mark.parametrize("wt", ["bf16", "f16", "int4"])
+@pytest.mark.parametrize("act", [F.FMLP_ACT_SILU, F.FMLP_ACT_GELU_ERF])
+def test_gateup_tail_tiles_in_one_launch(tail_layers, wt, act):
+    L = tail_layers[wt]
+    x, g = bf16_inputs(TAIL_M, TAIL_D, 930)
+    y, _ = L.forward_ex(x, g, EPS, activation=act)
+    ref, _ = L.oracle_ex(x, g, EPS, act, None)
+    assert_parity(y, ref, f"{wt} act={act} with tail tiles")
+
+
+def test_gateup_tail_tiles_f16_weights_equal_bf16(tail_layers):
+    # on the prefill path the fp16 store is the GEMM's own weight conversion,
+    # so both weight kinds give the same bits through the merged launch
+    L = tail_layers["f16"]
+    x, g = bf16_inputs(TAIL_M, TAIL_D, 931)
+    y16 = L.forward(x, g, EPS)
+    y = L.forward_bf16(x, g, EPS)
+    assert torch.equal(y16.view(torch.int16), y.view(torch.int16))
