@@ -36,6 +36,7 @@ MUTATIONS = {
                                  "if (kind == 2) return bf16_value(bf[row * K + k]);"),
     "int4_scale_of_next_group": ("f16[s[row * (K / 32) + k / 32]]", "f16[s[row * (K / 32) + (k + 1) / 32]]"),
     "rms_mean_over_d_minus_1": ("std::sqrt(ss / (double)d + eps)", "std::sqrt(ss / (double)(d - 1) + eps)"),
+    "token_chunk_offset_dropped": ("y[(m0 + m) * d + j] = acc;", "y[m * d + j] = acc;"),
 }
 
 

@@ -229,7 +229,10 @@ def test_scale_invariance_with_zero_eps():
                                atol=1e-15)
 
 
-@pytest.mark.parametrize("M,d,ff,seed", [(1, 32, 32, 1), (3, 64, 96, 2), (2, 256, 704, 3)])
+# (37 rows: the oracle takes tokens 16 at a time, so this crosses two chunk
+# boundaries and ends in a partial chunk)
+@pytest.mark.parametrize("M,d,ff,seed", [(1, 32, 32, 1), (3, 64, 96, 2), (2, 256, 704, 3),
+                                         (37, 64, 96, 4)])
 def test_matches_torch_fp64_composition(M, d, ff, seed):
     # An independent implementation from library routines: rms_norm, matmul, silu.
     x, g, wg, wu, wd = _rand_layer(M, d, ff, 600 + seed)
@@ -467,8 +470,9 @@ def test_forward_ex_defaults_are_eq1():
 @pytest.mark.parametrize("act,approx", [(oracle.ACT_SILU, None), (oracle.ACT_GELU_TANH, "tanh"),
                                         (oracle.ACT_GELU_ERF, "none")])
 @pytest.mark.parametrize("with_res", [False, True])
-def test_forward_ex_matches_torch_composition(act, approx, with_res):
-    M, d, ff = 3, 128, 160
+@pytest.mark.parametrize("M", [3, 37])
+def test_forward_ex_matches_torch_composition(act, approx, with_res, M):
+    d, ff = 128, 160
     x, g, wg, wu, wd = _rand_layer(M, d, ff, 810 + act)
     res = rand_bf16((M, d), 2.0, 820 + act) if with_res else None
     X = torch.from_numpy(bf16_values(x))
