@@ -11,7 +11,8 @@ d=4096, ff=14336, M=2048 tokens (the MFMA half of the metric), with the
 three decode M=1 workloads (Phi-3-mini-, Llama-3.1-8B- and 70B-int4-shaped;
 the HBM half) measured in the same run and reported inside the same line
 under "decode_m1". `--workload`/`--M` select one configuration alone;
-`--all` prints one line per (workload, M).
+`--all` prints one line per (workload, M), the 70B-shaped int4 layer also at
+512 and 2048 tokens (its int4 weights through the prefill GEMMs).
 """
 from __future__ import annotations
 
@@ -49,7 +50,8 @@ def parse():
                     help=f"one workload alone (default: {DEFAULT_WORKLOAD} M={DEFAULT_M} with the "
                          "decode M=1 lines)")
     ap.add_argument("--M", type=int, default=None)
-    ap.add_argument("--all", action="store_true", help="every (workload, M); one line each")
+    ap.add_argument("--all", action="store_true",
+                    help="every (workload, M), prefill sizes included; one line each")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-clock budget of the CPU-oracle baseline sample (all threads; the "
                          "one-thread figure takes a third of it)")
@@ -114,17 +116,19 @@ def kernel_bytes(kernel, M, d, ff, wtype, f16=None):
     return dn + M * ff * a_elem + M * d * 2
 
 
-def gemm_bytes(kernel, M, d, ff):
-    """Algorithmic bytes of one prefill GEMM launch: bf16 weights, fp16
-    activations in, its output (fp16 SiLU*mul product, or bf16 y)."""
+def gemm_bytes(kernel, M, d, ff, wtype="bf16"):
+    """Algorithmic bytes of one prefill GEMM launch: its weights (bf16, or
+    int4 codes and scales), fp16 activations in, its output (fp16 SiLU*mul
+    product, or bf16 y)."""
+    gu, dn = weight_bytes(d, ff, wtype)
     if kernel == "gemm_gateup_silu_f16":
-        return 2 * ff * d * 2 + M * d * 2 + M * ff * 2
-    return d * ff * 2 + M * ff * 2 + M * d * 2
+        return gu + M * d * 2 + M * ff * 2
+    return dn + M * ff * 2 + M * d * 2
 
 
 def algorithmic_bytes(kernel, M, d, ff, wtype):
     if kernel.startswith("gemm"):
-        return gemm_bytes(kernel, M, d, ff)
+        return gemm_bytes(kernel, M, d, ff, wtype)
     return kernel_bytes(kernel, M, d, ff, wtype)
 
 
@@ -604,6 +608,12 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
 
 
+def all_pairs(workloads):
+    """(workload, M) of every `--all` line: each workload's configured token
+    counts, then those it also runs through the prefill GEMMs."""
+    return [(name, M) for name, w in workloads.items() for M in w.Ms + w.prefill_Ms]
+
+
 def decode_summary(rec):
     """The fields of a decode M=1 record that the default line nests."""
     keep = ("value", "unit", "ms_per_step", "steps", "warmup", "dtype", "step_gb_per_s",
@@ -634,10 +644,9 @@ def main():
                 args.warmup if args.warmup is not None else wu)
 
     if args.all:
-        for wname, w in synth.WORKLOADS.items():
-            for M in w.Ms:
-                st, wu = steps_for(wname, M)
-                print(json.dumps(run_one(wname, M, st, wu, args)), flush=True)
+        for wname, M in all_pairs(synth.WORKLOADS):
+            st, wu = steps_for(wname, M)
+            print(json.dumps(run_one(wname, M, st, wu, args)), flush=True)
         return
     if args.workload is not None:
         w = synth.WORKLOADS[args.workload]

@@ -37,6 +37,7 @@ class Workload:
     Ms: tuple
     sets: int           # distinct layer weight sets rotated per step
     wtype: str          # "bf16" or "int4"
+    prefill_Ms: tuple = ()  # token counts also measured on the prefill path
 
 
 WORKLOADS = {
@@ -46,7 +47,10 @@ WORKLOADS = {
         Workload("phi3mini_decode_d3072_ff8192", 1, 3072, 8192, (1, 8), 32, "bf16"),
         Workload("llama8b_decode_d4096_ff14336", 2, 4096, 14336, (1, 4, 16, 32), 32, "bf16"),
         Workload("llama8b_prefill_d4096_ff14336", 3, 4096, 14336, (512, 2048), 1, "bf16"),
-        Workload("llama70b_int4_decode_d8192_ff28672", 4, 8192, 28672, (1, 16), 20, "int4"),
+        # (and its int4 weights through the prefill GEMMs, at the Llama-8B
+        # prefill token counts)
+        Workload("llama70b_int4_decode_d8192_ff28672", 4, 8192, 28672, (1, 16), 20, "int4",
+                 (512, 2048)),
         # one GPU's share of the two decode layers under 8-way tensor
         # parallelism over ff (each GPU holds ff/8 gate/up pairs and the
         # matching W_down columns; the partial y of the eight would then be

@@ -1,8 +1,8 @@
 """Host-side checks of bench.py (no GPU): the byte and flop counts behind
 its roofline figures against the figures worked out independently for the
 workloads (the per-step table of the measurement plan, in decimal MB and
-GFLOP), the refusal of more than one GPU, and the comment-blind source hash
-that expires a committed traffic summary."""
+GFLOP), the lines `--all` prints, the refusal of more than one GPU, and the
+comment-blind source hash that expires a committed traffic summary."""
 import os
 import subprocess
 import sys
@@ -44,6 +44,28 @@ def test_kernel_bytes_add_up_to_the_weights():
     # int4: half a byte per weight plus one fp16 scale per 32
     gu, dn = bench.weight_bytes(8192, 28672, "int4")
     assert dn == 8192 * 28672 // 2 + 8192 * (28672 // 32) * 2
+
+
+def test_gemm_bytes_follow_the_weight_type():
+    d, ff, M = 8192, 28672, 512
+    for wt in ("bf16", "int4"):
+        gu, dn = bench.weight_bytes(d, ff, wt)
+        assert bench.gemm_bytes("gemm_gateup_silu_f16", M, d, ff, wt) == gu + M * d * 2 + M * ff * 2
+        assert bench.gemm_bytes("gemm_down_f16", M, d, ff, wt) == dn + M * ff * 2 + M * d * 2
+    # int4 GEMMs read a quarter of the bf16 weight bytes plus one fp16 scale per 32
+    assert (bench.gemm_bytes("gemm_down_f16", 0, d, ff, "int4") ==
+            d * ff // 2 + d * (ff // 32) * 2)
+
+
+def test_all_lines_cover_every_configuration():
+    from swiglu_mlp_rmsnorm_amd import synth
+    pairs = bench.all_pairs(synth.WORKLOADS)
+    assert len(pairs) == len(set(pairs))
+    for name, w in synth.WORKLOADS.items():
+        assert all((name, M) in pairs for M in w.Ms)
+    # int4 weights through the prefill GEMMs, at the prefill token counts
+    assert ("llama70b_int4_decode_d8192_ff28672", 512) in pairs
+    assert ("llama70b_int4_decode_d8192_ff28672", 2048) in pairs
 
 
 def test_more_than_one_gpu_is_refused():
