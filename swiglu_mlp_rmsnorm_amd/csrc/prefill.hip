@@ -517,10 +517,16 @@ __device__ __forceinline__ void gemm_tile(const void* __restrict__ Wt,
     }
   };
 
-  // prologue: steps 0..3 -> stages 0..3; wait for step 0; its first fragments
+  // prologue: steps 0..3 -> stages 0..3; wait for step 0 only (the loop's
+  // waits cover steps 1..3, whose loads stay in flight: with every CU
+  // starting a tile at once, waiting for all four steps held the first
+  // MFMAs back by about 1 us per tile on MI355X); its first fragments
   const int npre = nkt < 4 ? nkt : 4;
   for (int s = 0; s < npre; ++s) load_step(s, s);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  if (npre == 4)
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * C::LD_PER_T));
+  else
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
   frag_load(0, 0, 0, 0);
   convert(0);
