@@ -587,6 +587,38 @@ __device__ __forceinline__ void gemm_tile(const void* __restrict__ Wt,
 
   // epilogue: lane holds token t = col of block (i, j) and rows 8r + 4 grp + e
   const int col = lane & 31, grp = lane >> 5;
+  if constexpr (epi_gate(EPI)) {
+    // Row pair (2p, 2p+1) of a 32-row block gives product p of its 16, so
+    // lane l holds products 4r + 2 grp and 4r + 2 grp + 1 (r = 0..3) of its
+    // token. Lanes l and l ^ 32 swap two of their four words, leaving
+    // products 0..7 in lane l < 32 and 8..15 in lane l + 32: each then
+    // stores one 16-byte slot, and the wave one whole 1 KB fragment.
+    // (Blocks lie wholly inside or outside n_end: both are multiples of 32.)
+#pragma unroll
+    for (int i = 0; i < C::WNB; ++i) {
+      const int fb = n0 + (wn * C::WNB + i) * 32;
+#pragma unroll
+      for (int j = 0; j < C::WMB; ++j) {
+        const int t = m0 + (wm * C::WMB + j) * 32 + col;
+        uint32_t pk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const _Float16 a0 =
+              (_Float16)act_mul(epi_act(EPI), acc[i][j][4 * r], acc[i][j][4 * r + 1]);
+          const _Float16 a1 =
+              (_Float16)act_mul(epi_act(EPI), acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]);
+          pk[r] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        }
+        const uint32_t s0 = __shfl_xor(grp ? pk[0] : pk[2], 32);
+        const uint32_t s1 = __shfl_xor(grp ? pk[1] : pk[3], 32);
+        const u32x4 o = grp ? u32x4{s0, pk[2], s1, pk[3]} : u32x4{pk[0], s0, pk[1], s1};
+        if (t < M && fb < n_end)
+          st16(static_cast<uint16_t*>(out) + act_tile_off(t, fb / 2 + 8 * grp, N / 2), o);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::WNB; ++i) {
 #pragma unroll
@@ -599,14 +631,7 @@ __device__ __forceinline__ void gemm_tile(const void* __restrict__ Wt,
         if (f0 >= n_end) continue;
         const float v0 = acc[i][j][4 * r], v1 = acc[i][j][4 * r + 1];
         const float v2 = acc[i][j][4 * r + 2], v3 = acc[i][j][4 * r + 3];
-        if (epi_gate(EPI)) {
-          const _Float16 a0 = (_Float16)act_mul(epi_act(EPI), v0, v1);
-          const _Float16 a1 = (_Float16)act_mul(epi_act(EPI), v2, v3);
-          const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) +
-                                       act_tile_off(t, f0 / 2, N / 2)) = packed;
-        } else if (EPI == EPI_STORE_BF16) {
+        if (EPI == EPI_STORE_BF16) {
           uint32_t* dst =
               reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (int64_t)t * N + f0);
           dst[0] = pack_bf16_rne(v0, v1);
