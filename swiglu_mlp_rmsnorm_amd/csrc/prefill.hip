@@ -85,11 +85,22 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
     const u32x4 v = ld16(xr + c * 8);
     return rr ? add_bf16x8(v, ld16(rr + c * 8)) : v;
   };
-  u32x4 v[R];
+  // the row's chunks, and for rows up to 8 chunks per lane gamma's too (in
+  // flight with them rather than loaded after the row's sum is known; longer
+  // rows would run out of registers)
+  constexpr bool kPreGamma = R <= 8;
+  u32x4 v[R], gv[kPreGamma ? R : 1];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int c = lane + 64 * i;
     v[i] = c < nch ? row(c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (kPreGamma) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int c = lane + 64 * i;
+      gv[i] = c < nch ? ld16(gamma + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
   }
   float ss = 0.f;
 #pragma unroll
@@ -115,9 +126,8 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
   // chunk c (columns 8c .. 8c+7) of token slot t: fragment (t/32, c/4, (c/2)%2),
   // slot (c%2)*32 + t%32
   const int tb = t >> 5, tl = t & 31, nkb = d >> 5;
-  auto put = [&](int c, u32x4 w) {
+  auto put = [&](int c, u32x4 w, u32x4 gm) {
     if (hout && t < M) st16(hout + (int64_t)t * d + c * 8, w);
-    const u32x4 gm = ld16(gamma + c * 8);
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int c = lane + 64 * i;
-    if (c < nch) put(c, v[i]);
+    if (c < nch) put(c, v[i], kPreGamma ? gv[kPreGamma ? i : 0] : ld16(gamma + c * 8));
   }
   if constexpr (STAGE) {
     __syncthreads();
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(512) void k_rms_norm_tiled(const uint16_t* __restri
       st16(n + frag * 512 + ((c & 1) * 32 + tl0 + w) * 8, rms_lds[p]);
     }
   } else {
-    for (int c = lane + 64 * R; c < nch; c += 64) put(c, row(c));
+    for (int c = lane + 64 * R; c < nch; c += 64) put(c, row(c), ld16(gamma + c * 8));
   }
 }
 
