@@ -275,7 +275,7 @@ def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True):
     steps again with the library's per-launch HIP events (dispatch start and
     end stamps on the launch stream), for the per-kernel durations. The
     events are kept out of the timed region: they add idle time between the
-    launches (about 24 us per Llama-8B prefill step), though not to the
+    launches (microseconds per launch), though not to the
     kernels' own durations, which agree with a rocprofv3 kernel trace."""
     import torch
     from swiglu_mlp_rmsnorm_amd import fmlp as F
