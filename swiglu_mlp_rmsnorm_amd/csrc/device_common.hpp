@@ -98,10 +98,10 @@ __device__ __forceinline__ float silu_mul(float t, float u) { return t * fast_si
 
 // erf(x) by the rational approximation of Abramowitz and Stegun, Handbook
 // of Mathematical Functions, formula 7.1.26: 1 - (a1 k + ... + a5 k^5)
-// e^(-x^2) with k = 1 / (1 + p x) for x >= 0 (absolute error below 1.5e-7,
-// about 5e-7 evaluated in fp32), odd in x. Branch-free, one hardware reciprocal and one exponential (the
-// sigmoid's cost); far below the fp16 rounding of the product it feeds.
-// Limits: +-1 for x -> +-inf, NaN for NaN.
+// e^(-x^2) with k = 1 / (1 + p x) for x >= 0, odd in x. Absolute error
+// below 1.5e-7 (about 5e-7 evaluated in fp32), far below the fp16 rounding
+// of the product it feeds. Branch-free: one hardware reciprocal and one
+// exponential, the sigmoid's cost. Limits: +-1 for x -> +-inf, NaN for NaN.
 __device__ __forceinline__ float erf_as7126(float x) {
   const float ax = fabsf(x);
   const float k = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
