@@ -186,11 +186,27 @@ def measured_traffic(kernel, workload, M):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
+# the accuracy bar of the forward (max |y - y_ref| over rms(y_ref), and the
+# mean relative error sum |y - y_ref| / sum |y_ref|)
+PARITY_BAR = {"max_over_rms": 2e-2, "l1_rel": 3e-3}
+
+
+def parity_rows(M, n=16):
+    """n token rows spread evenly over the M (all of them when M <= n)."""
+    if M <= n:
+        return list(range(M))
+    return sorted({round(k * (M - 1) / (n - 1)) for k in range(n)})
+
+
+def cpu_baseline(w, M, host_layer, host_inputs, budget_s, rows=None, y_rows=None):
     """Time the fp64 CPU oracle, as it stands, on a bounded sample of the same
     workload (weight set 0, the same seeded row-major weights and inputs):
     rows are independent, so it runs calls on consecutive row subsets until
-    the budget is spent, first with every OpenMP thread, then with one."""
+    the budget is spent, first with every OpenMP thread, then with one.
+    With `rows` and the GPU's y of those rows (`y_rows`, from the measured
+    launch on the full input), the oracle's y of the same rows also gives the
+    parity of the measured configuration on that sample: (record, parity)."""
+    import numpy as np
     from oracle import oracle
     x, g = host_inputs
     if w.wtype == "int4":
@@ -198,12 +214,22 @@ def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
         q_gu, s_gu = oracle.pack_interleaved_int4(qg, sg, qu, su)
 
         def call(xs):
-            oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, qd, sd)
+            return oracle.forward_int4(xs, g, w_eps(), q_gu, s_gu, qd, sd)
     else:
         wg, wu, wd = host_layer
 
         def call(xs):
-            oracle.forward_unfused(xs, g, w_eps(), wg, wu, wd)
+            return oracle.forward_unfused(xs, g, w_eps(), wg, wu, wd)
+
+    parity = None
+    if rows is not None:
+        y_ref = call(np.ascontiguousarray(x[rows]))
+        err = np.abs(y_rows - y_ref)
+        parity = {"rows": len(rows), "of_tokens": M,
+                  "max_over_rms": float(err.max() / np.sqrt(np.mean(y_ref ** 2))),
+                  "l1_rel": float(err.sum() / np.abs(y_ref).sum()), "bar": PARITY_BAR,
+                  "note": "oracle (fp64) against the GPU's y of the measured launch, "
+                          "weight set 0, rows spread evenly over the input"}
 
     def timed(rows_per_call, budget):
         done, calls = 0, 0
@@ -233,7 +259,7 @@ def cpu_baseline(w, M, host_layer, host_inputs, budget_s):
         "sample": (f"{calls} oracle forward call(s) of {rows_per_call} row(s) of the {M}-token "
                    f"input on weight set 0 of {w.name} (fp64, {threads} threads, {el:.1f} s); "
                    f"then {calls1} call(s) of 1 row on 1 thread ({el1:.1f} s)"),
-    }
+    }, parity
 
 
 def w_eps():
@@ -438,11 +464,16 @@ def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True):
             ceiling["dominant_kernel_frac_of_ceiling"] = round(
                 roofline["achieved"] / ceiling["gb_per_s"], 4)
 
-    cpu_rec = None
+    cpu_rec = parity = None
     if cpu:
         host_inputs = (synth.bits(xs[0][0]), synth.bits(xs[0][1]))
+        # the GPU's y of weight set 0 from the measured launch (full input)
+        step(0)
+        torch.cuda.synchronize()
+        rows = parity_rows(M)
+        y_rows = y[rows].double().cpu().numpy()
         log(f"[bench] CPU oracle baseline ({args.cpu_seconds:.0f} s budget)")
-        cpu_rec = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds)
+        cpu_rec, parity = cpu_baseline(w, M, host0, host_inputs, args.cpu_seconds, rows, y_rows)
 
     step_gbs = sb / (ms_per_step * 1e-3) / 1e9
     step_tflops = step_flops(M, d, ff) / (ms_per_step * 1e-3) / 1e12
@@ -473,6 +504,11 @@ def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True):
             "int4-f16": "fp16 from int4 codes and fp16 group scales"}[dtype]
             + "; fp32 accumulation; bf16 x, gamma and y"),
         "data": "synthetic",
+        "seeds": ("1_000_003 * workload + 1_009 * layer + tensor id (x 0, gamma 1, W_gate 2, "
+                  f"W_up 3, W_down 4; int4 codes and scales 5-10); workload {w.index}"),
+        "env": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                "gpu": torch.cuda.get_device_name(0),
+                "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)},
         "config": {"workload": wname, "M": M, "d": d, "ff": ff, "weight_sets": w.sets,
                    "wtype": "f16" if w16 else w.wtype, "path": path, "activation": args.activation,
                    "residual": bool(args.residual), "parallelism": "none (1 GPU)"},
@@ -485,6 +521,7 @@ def run_one(wname, M, steps, warmup, args, *, cpu=True, spread=True):
         "spread": spr,
         "kernels": kernels,
         "cpu_baseline": cpu_rec,
+        "parity_sample": parity,
     }
     del layers, xs
     torch.cuda.empty_cache()

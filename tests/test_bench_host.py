@@ -68,6 +68,15 @@ def test_all_lines_cover_every_configuration():
     assert ("llama70b_int4_decode_d8192_ff28672", 2048) in pairs
 
 
+def test_parity_rows_span_the_input():
+    assert bench.parity_rows(5) == [0, 1, 2, 3, 4]
+    rows = bench.parity_rows(2048)
+    assert len(rows) == 16 and rows[0] == 0 and rows[-1] == 2047
+    # one row in each of the eight 256-token tiles at least
+    assert {r // 256 for r in rows} == set(range(8))
+    assert rows == sorted(set(rows))
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
