@@ -386,6 +386,28 @@ def test_variants_int4(act, with_res, path, M):
     _check_ex(layer, M, 1024, act, with_res, 930 + M, path=path)
 
 
+@pytest.mark.parametrize("act", [F.FMLP_ACT_SILU, F.FMLP_ACT_GELU_TANH, F.FMLP_ACT_GELU_ERF])
+@pytest.mark.parametrize("path,M", [(F.FMLP_PATH_DECODE, 3), (F.FMLP_PATH_DECODE, 20),
+                                    (F.FMLP_PATH_PREFILL, 70)])
+def test_gate_activations_over_a_wide_range(act, path, M):
+    # W_gate ten times larger: the gate pre-activations span about +-10, the
+    # range where the kernels' sigmoid and erf approximations (hardware exp
+    # and reciprocal; the Abramowitz-Stegun erf) meet both tails, against
+    # the oracle's exact functions
+    layer = Bf16Layer(TINY_D, TINY_FF, 64)
+    layer.wg = (layer.wg.float() * 10.0).to(torch.bfloat16)
+    layer.wgu_t = F.fmlp_pack_interleaved(layer.wg, layer.wu)
+    layer.host = (synth.bits(layer.wg),) + layer.host[1:]
+    x, g = bf16_inputs(M, TINY_D, 990 + M)
+    xf, gf = x.float().cpu(), g.float().cpu()
+    n = xf * torch.rsqrt(xf.pow(2).mean(1, keepdim=True) + EPS) * gf
+    z = n @ layer.wg.float().cpu().T
+    assert float(z.abs().max()) > 8.0  # the test reaches the tails
+    y, _ = layer.forward_ex(x, g, EPS, activation=act, path=path)
+    ref, _ = layer.oracle_ex(x, g, EPS, act, None)
+    assert_parity(y, ref, f"wide gate act={act} path={path} M={M}")
+
+
 @pytest.mark.parametrize("d,ff,M", [(3072, 8192, 1), (4096, 1024, 16), (18432, 64, 2),
                                     (256, 6144, 2)])
 def test_residual_stream_bit_exact_at_larger_d(d, ff, M):
