@@ -77,6 +77,30 @@ def test_parity_rows_span_the_input():
     assert rows == sorted(set(rows))
 
 
+def test_cpu_leg_parity_of_the_oracle_own_rounded_output():
+    # the CPU leg's parity on the tiny layer, fed the oracle's own y rounded
+    # to bf16 for the sampled rows: only y's rounding remains (at most half a
+    # bf16 ulp: 2^-8 relative, 8 significand bits), and the record carries
+    # the bar
+    import numpy as np
+    import torch
+    from oracle import oracle
+    from swiglu_mlp_rmsnorm_amd import synth
+    w = synth.WORKLOADS["tiny_d256_ff704"]
+    M = 40
+    host = tuple(synth.bits(t) for t in synth.layer_bf16(w, 0))
+    x, g = (synth.bits(t) for t in synth.inputs(w, M))
+    rows = bench.parity_rows(M)
+    ref = oracle.forward_unfused(x[rows], g, synth.EPS, *host)
+    y_rows = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    rec, par = bench.cpu_baseline(w, M, host, (x, g), 0.2, rows, y_rows)
+    assert rec["kind"] == "oracle" and rec["value"] > 0 and rec["value_1core"] > 0
+    assert par["rows"] == 16 and par["of_tokens"] == M and par["bar"] == bench.PARITY_BAR
+    rel = np.abs(y_rows - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert rel.max() <= 2.0 ** -8
+    assert 0 < par["l1_rel"] < 2e-3 and 0 < par["max_over_rms"] < 2e-2
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
