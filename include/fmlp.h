@@ -75,6 +75,14 @@ enum fmlp_path {
                                time on one GPU */
 };
 
+/*
+ * Gate activations. The kernels evaluate the logistic function with the
+ * hardware exponential and reciprocal (about 1 ulp each; the tanh form
+ * through 0.5 (1 + tanh y) = sigma(2 y)) and erf by Abramowitz and Stegun's
+ * formula 7.1.26 (absolute error below 1.5e-7), in fp32; each product a is
+ * then rounded to fp16 (or kept as a bf16 hi + lo pair on the bf16 decode
+ * path at M <= 16).
+ */
 enum fmlp_activation {
   FMLP_ACT_SILU = 0,      /* SiLU(t) = t / (1 + e^-t): Eq(1), the default */
   FMLP_ACT_GELU_TANH = 1, /* 0.5 t (1 + tanh(sqrt(2/pi) (t + 0.044715 t^3))) */
