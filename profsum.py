@@ -170,8 +170,14 @@ def counters(args):
     gui = gui_x
     if gui:
         cdur = avg.get("_DURATION_NS", dur_ns)
-        lines.append(f"shader_clock_ghz: {gui / cdur:.3f}  (GRBM_GUI_ACTIVE / {args.xcds} XCDs"
-                     " / the dispatch's duration in the counter run)")
+        clk = gui / cdur
+        if clk <= 2.45:
+            lines.append(f"shader_clock_ghz: {clk:.3f}  (GRBM_GUI_ACTIVE / {args.xcds} XCDs"
+                         " / the dispatch's duration in the counter run)")
+        else:  # the GRBM window outlasts a short dispatch: no clock from it
+            lines.append(f"shader_clock_ghz: not derived (GRBM_GUI_ACTIVE / {args.xcds} XCDs"
+                         f" over the dispatch's duration gives {clk:.2f}, above the 2.4 GHz"
+                         " peak: the counting window is longer than the dispatch)")
     if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
         lines.append(f"mfma_busy_pct: {100 * avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.1f}"
                      f"  (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * {simds} SIMDs))")
